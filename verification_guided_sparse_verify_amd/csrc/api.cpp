@@ -1,0 +1,306 @@
+// Host side of the C ABI declared in include/vegas.h: argument validation,
+// launch planning (split sizes), workspace layout and dispatch.  Nothing here
+// synchronises with the device or allocates device memory.
+#include "vegas.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+vegas_status_t fail(vegas_status_t st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Workgroups the split kernel should expose: a few per CU on a 256-CU part.
+constexpr int kTargetWorkgroups = 1024;
+
+struct AttnPlan {
+    int mb = 0;          // 16-row query tiles per KV head
+    int chunk = 0;       // positions per split
+    int nsplit = 0;      // splits per (sequence, KV head)
+    size_t part_o = 0;   // bytes
+    size_t part_ml = 0;  // bytes
+    size_t total() const { return align_up(part_o) + align_up(part_ml); }
+};
+
+AttnPlan plan_attn(int batch, int hkv, int M, int head_dim, int max_n, bool gather) {
+    AttnPlan p;
+    p.mb = (M + 15) / 16;
+    const int unit = vegas::kAttnWaves * vegas::kAttnBlock;
+    const int n = max_n > 0 ? max_n : 1;
+    const int units = batch * hkv;
+    int want = (kTargetWorkgroups + units - 1) / units;
+    const int most = (n + unit - 1) / unit;
+    if (want > most) want = most;
+    if (want < 1) want = 1;
+    int chunk = (n + want - 1) / want;
+    chunk = (chunk + unit - 1) / unit * unit;
+    if (gather && chunk > vegas::kMaxGatherChunk) chunk = vegas::kMaxGatherChunk;
+    p.chunk = chunk;
+    p.nsplit = (n + chunk - 1) / chunk;
+    const size_t slots = (size_t)batch * hkv * p.nsplit;
+    p.part_o = slots * p.mb * 16 * head_dim * sizeof(float);
+    p.part_ml = slots * p.mb * 16 * 2 * sizeof(float);
+    return p;
+}
+
+vegas_status_t check_shape(const vegas_attn_shape_t* s) {
+    if (!s) return fail(VEGAS_ERR_INVALID_ARGUMENT, "shape is NULL");
+    if (s->dtype != VEGAS_DTYPE_F32 && s->dtype != VEGAS_DTYPE_BF16)
+        return fail(VEGAS_ERR_UNSUPPORTED, "dtype %d is not VEGAS_DTYPE_F32 or VEGAS_DTYPE_BF16", s->dtype);
+    if (s->batch < 1) return fail(VEGAS_ERR_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", s->batch);
+    if (s->num_q_heads < 1 || s->num_kv_heads < 1)
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "head counts must be >= 1 (Hq=%d, Hkv=%d)",
+                    s->num_q_heads, s->num_kv_heads);
+    if (s->num_q_heads % s->num_kv_heads != 0)
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                    s->num_q_heads, s->num_kv_heads);
+    if (s->head_dim != 64 && s->head_dim != 128)
+        return fail(VEGAS_ERR_UNSUPPORTED, "head_dim %d is not 64 or 128", s->head_dim);
+    if (!(s->softmax_scale > 0.f) || !std::isfinite(s->softmax_scale))
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
+    return VEGAS_OK;
+}
+
+vegas_status_t check_gamma(int32_t gamma, const vegas_attn_shape_t* s) {
+    if (gamma < 0 || gamma > 31) return fail(VEGAS_ERR_INVALID_ARGUMENT, "gamma %d outside 0..31", gamma);
+    const int G = s->num_q_heads / s->num_kv_heads;
+    if ((gamma + 1) * G > 64)
+        return fail(VEGAS_ERR_UNSUPPORTED, "(gamma+1)*(Hq/Hkv) = %d exceeds 64 query rows per KV head",
+                    (gamma + 1) * G);
+    return VEGAS_OK;
+}
+
+vegas_status_t hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(VEGAS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return VEGAS_OK;
+}
+
+struct SelectPlan {
+    int nchunks = 0;
+    size_t keys = 0, tpos = 0, tkey = 0, hist = 0;
+    size_t total() const { return align_up(keys) + align_up(tpos) + align_up(tkey) + align_up(hist); }
+};
+
+SelectPlan plan_select(int batch, int max_seqlen_k, int total_kv) {
+    SelectPlan p;
+    p.nchunks = (max_seqlen_k + vegas::kSelChunk - 1) / vegas::kSelChunk;
+    p.keys = (size_t)total_kv * sizeof(uint32_t);
+    p.tpos = (size_t)total_kv * sizeof(int32_t);
+    p.tkey = (size_t)total_kv * sizeof(uint32_t);
+    p.hist = (size_t)batch * vegas::kSelBins * sizeof(uint32_t);
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t vegas_abi_version(void) { return VEGAS_ABI_VERSION; }
+
+const char* vegas_status_string(vegas_status_t s) {
+    switch (s) {
+        case VEGAS_OK: return "VEGAS_OK";
+        case VEGAS_ERR_INVALID_ARGUMENT: return "VEGAS_ERR_INVALID_ARGUMENT";
+        case VEGAS_ERR_UNSUPPORTED: return "VEGAS_ERR_UNSUPPORTED";
+        case VEGAS_ERR_WORKSPACE_TOO_SMALL: return "VEGAS_ERR_WORKSPACE_TOO_SMALL";
+        case VEGAS_ERR_HIP: return "VEGAS_ERR_HIP";
+    }
+    return "VEGAS_ERR_UNKNOWN";
+}
+
+const char* vegas_last_error_message(void) { return g_last_error.c_str(); }
+
+vegas_status_t vegas_verify_workspace_size(const vegas_attn_shape_t* shape, int32_t gamma,
+                                           int32_t max_seqlen_k, size_t* bytes) {
+    vegas_status_t st = check_shape(shape);
+    if (st != VEGAS_OK) return st;
+    if ((st = check_gamma(gamma, shape)) != VEGAS_OK) return st;
+    if (!bytes) return fail(VEGAS_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    if (max_seqlen_k < gamma + 1)
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "max_seqlen_k %d < gamma+1", max_seqlen_k);
+    const int G = shape->num_q_heads / shape->num_kv_heads;
+    *bytes = plan_attn(shape->batch, shape->num_kv_heads, (gamma + 1) * G, shape->head_dim,
+                       max_seqlen_k, false).total();
+    return VEGAS_OK;
+}
+
+vegas_status_t vegas_verify_attn(const vegas_attn_shape_t* shape, int32_t gamma, const void* q,
+                                 const void* k, const void* v, const int32_t* cu_seqlens_k,
+                                 int32_t max_seqlen_k, int32_t total_kv, uint32_t collect_mask,
+                                 float* scores, void* out, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    vegas_status_t st = check_shape(shape);
+    if (st != VEGAS_OK) return st;
+    if ((st = check_gamma(gamma, shape)) != VEGAS_OK) return st;
+    const int W = gamma + 1;
+    if (!q || !k || !v || !cu_seqlens_k || !out)
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "q, k, v, cu_seqlens_k and out must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "q, k, v and out must be 16-byte aligned");
+    if (W < 32 && (collect_mask >> W) != 0u)
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "collect_mask 0x%x has bits at rows >= gamma+1 = %d",
+                    collect_mask, W);
+    if (collect_mask != 0u && !scores)
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "scores is NULL but collect_mask is non-zero");
+    if (max_seqlen_k < W)
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "max_seqlen_k %d < gamma+1 = %d", max_seqlen_k, W);
+    if (total_kv < shape->batch * W)
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "total_kv %d < batch*(gamma+1)", total_kv);
+    const int G = shape->num_q_heads / shape->num_kv_heads;
+    const AttnPlan plan = plan_attn(shape->batch, shape->num_kv_heads, W * G, shape->head_dim,
+                                    max_seqlen_k, false);
+    if (workspace_bytes < plan.total())
+        return fail(VEGAS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.total(),
+                    workspace_bytes);
+    if (!workspace) return fail(VEGAS_ERR_INVALID_ARGUMENT, "workspace is NULL");
+
+    vegas::AttnArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.cu_seqlens_k = cu_seqlens_k;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(plan.part_o));
+    a.scores = scores;
+    a.out = out;
+    a.batch = shape->batch;
+    a.hq = shape->num_q_heads;
+    a.hkv = shape->num_kv_heads;
+    a.G = G;
+    a.W = W;
+    a.M = W * G;
+    a.total_kv = total_kv;
+    a.chunk = plan.chunk;
+    a.nsplit = plan.nsplit;
+    a.scale = shape->softmax_scale;
+    a.scale_log2 = shape->softmax_scale * 1.4426950408889634f;
+    a.collect_mask = collect_mask;
+    return hip_status(vegas::launch_attn(a, shape->dtype == VEGAS_DTYPE_BF16, shape->head_dim, plan.mb,
+                                         false, collect_mask != 0u, static_cast<hipStream_t>(stream)),
+                      "verify launch");
+}
+
+vegas_status_t vegas_select_workspace_size(int32_t batch, int32_t num_kv_heads, int32_t gamma,
+                                           int32_t max_seqlen_k, int32_t total_kv, size_t* bytes) {
+    if (batch < 1 || num_kv_heads < 1) return fail(VEGAS_ERR_INVALID_ARGUMENT, "batch and num_kv_heads must be >= 1");
+    if (gamma < 0 || gamma > 31) return fail(VEGAS_ERR_INVALID_ARGUMENT, "gamma %d outside 0..31", gamma);
+    if (max_seqlen_k < gamma + 1 || total_kv < 1)
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "max_seqlen_k must be >= gamma+1 and total_kv >= 1");
+    if (!bytes) return fail(VEGAS_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    *bytes = plan_select(batch, max_seqlen_k, total_kv).total();
+    return VEGAS_OK;
+}
+
+vegas_status_t vegas_select_topk(int32_t batch, int32_t num_kv_heads, int32_t gamma,
+                                 const float* scores, const int32_t* cu_seqlens_k,
+                                 int32_t max_seqlen_k, int32_t total_kv, const int32_t* cu_k,
+                                 int32_t* indices, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    size_t need = 0;
+    vegas_status_t st = vegas_select_workspace_size(batch, num_kv_heads, gamma, max_seqlen_k, total_kv, &need);
+    if (st != VEGAS_OK) return st;
+    if (!scores || !cu_seqlens_k || !cu_k || !indices)
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "scores, cu_seqlens_k, cu_k and indices must be non-NULL");
+    if (workspace_bytes < need)
+        return fail(VEGAS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+    if (!workspace) return fail(VEGAS_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    const SelectPlan plan = plan_select(batch, max_seqlen_k, total_kv);
+    char* ws = static_cast<char*>(workspace);
+    vegas::SelectArgs a{};
+    a.scores = scores;
+    a.cu_seqlens_k = cu_seqlens_k;
+    a.cu_k = cu_k;
+    a.indices = indices;
+    a.keys = reinterpret_cast<uint32_t*>(ws);
+    ws += align_up(plan.keys);
+    a.tmp_pos = reinterpret_cast<int32_t*>(ws);
+    ws += align_up(plan.tpos);
+    a.tmp_key = reinterpret_cast<uint32_t*>(ws);
+    ws += align_up(plan.tkey);
+    a.hist = reinterpret_cast<uint32_t*>(ws);
+    a.batch = batch;
+    a.hkv = num_kv_heads;
+    a.W = gamma + 1;
+    a.total_kv = total_kv;
+    a.nchunks = plan.nchunks;
+    return hip_status(vegas::launch_select(a, static_cast<hipStream_t>(stream)), "select launch");
+}
+
+vegas_status_t vegas_sparse_decode_workspace_size(const vegas_attn_shape_t* shape, int32_t max_idx,
+                                                  size_t* bytes) {
+    vegas_status_t st = check_shape(shape);
+    if (st != VEGAS_OK) return st;
+    if (!bytes) return fail(VEGAS_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    if (max_idx < 0) return fail(VEGAS_ERR_INVALID_ARGUMENT, "max_idx %d < 0", max_idx);
+    const int G = shape->num_q_heads / shape->num_kv_heads;
+    if (G > 64) return fail(VEGAS_ERR_UNSUPPORTED, "Hq/Hkv = %d exceeds 64", G);
+    *bytes = plan_attn(shape->batch, shape->num_kv_heads, G, shape->head_dim, max_idx, true).total();
+    return VEGAS_OK;
+}
+
+vegas_status_t vegas_sparse_decode_attn(const vegas_attn_shape_t* shape, const void* q, const void* k,
+                                        const void* v, const int32_t* cu_seqlens_k, int32_t total_kv,
+                                        const int32_t* indices, const int32_t* cu_idx, int32_t max_idx,
+                                        void* out, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+    size_t need = 0;
+    vegas_status_t st = vegas_sparse_decode_workspace_size(shape, max_idx, &need);
+    if (st != VEGAS_OK) return st;
+    if (!q || !k || !v || !cu_seqlens_k || !cu_idx || !out)
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "q, k, v, cu_seqlens_k, cu_idx and out must be non-NULL");
+    if (max_idx > 0 && !indices) return fail(VEGAS_ERR_INVALID_ARGUMENT, "indices is NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "q, k, v and out must be 16-byte aligned");
+    if (total_kv < 1) return fail(VEGAS_ERR_INVALID_ARGUMENT, "total_kv must be >= 1");
+    if (workspace_bytes < need)
+        return fail(VEGAS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+    if (!workspace) return fail(VEGAS_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    const int G = shape->num_q_heads / shape->num_kv_heads;
+    const AttnPlan plan = plan_attn(shape->batch, shape->num_kv_heads, G, shape->head_dim, max_idx, true);
+    vegas::AttnArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.cu_seqlens_k = cu_seqlens_k;
+    a.indices = indices;
+    a.cu_idx = cu_idx;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(plan.part_o));
+    a.scores = nullptr;
+    a.out = out;
+    a.batch = shape->batch;
+    a.hq = shape->num_q_heads;
+    a.hkv = shape->num_kv_heads;
+    a.G = G;
+    a.W = 1;
+    a.M = G;
+    a.total_kv = total_kv;
+    a.chunk = plan.chunk;
+    a.nsplit = plan.nsplit;
+    a.scale = shape->softmax_scale;
+    a.scale_log2 = shape->softmax_scale * 1.4426950408889634f;
+    a.collect_mask = 0u;
+    return hip_status(vegas::launch_attn(a, shape->dtype == VEGAS_DTYPE_BF16, shape->head_dim, plan.mb,
+                                         true, false, static_cast<hipStream_t>(stream)),
+                      "sparse decode launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Internal interface between the host API (api.cpp) and the kernel launchers
+// (attn.hip, select.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vegas {
+
+// Waves per attention workgroup and positions per wave iteration.
+constexpr int kAttnWaves = 4;
+constexpr int kAttnBlock = 32;
+// Longest position range one workgroup takes in gather mode: its index list
+// is staged in LDS.
+constexpr int kMaxGatherChunk = 2048;
+
+// Arguments of the split attention kernel and of its combine kernel.
+// One kernel serves both the verification pass (contiguous positions, causal
+// tail, optional collection) and the drafting pass (gathered positions).
+struct AttnArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const int32_t* cu_seqlens_k;   // [batch+1]
+    const int32_t* indices;        // gather: per-sequence lists
+    const int32_t* cu_idx;         // gather: [batch+1]
+    float* part_o;                 // [batch*hkv*nsplit][MB*16*D] (fragment order)
+    float* part_ml;                // [batch*hkv*nsplit][MB*16][2] (max in log2 units, sum)
+    float* scores;                 // collect: [hkv, total_kv]
+    void* out;                     // [batch*W, hq, D]
+    int32_t batch, hq, hkv, G, W, M;   // M = W*G query rows per KV head
+    int32_t total_kv;
+    int32_t chunk;                 // positions per split, multiple of kAttnWaves*kAttnBlock
+    int32_t nsplit;                // splits per (sequence, KV head)
+    float scale;                   // softmax scale s
+    float scale_log2;              // s * log2(e)
+    uint32_t collect_mask;
+};
+
+hipError_t launch_attn(const AttnArgs& a, bool bf16, int head_dim, int mblocks, bool gather,
+                       bool collect, hipStream_t stream);
+
+struct SelectArgs {
+    const float* scores;           // [hkv, total_kv]
+    const int32_t* cu_seqlens_k;   // [batch+1]
+    const int32_t* cu_k;           // [batch+1]
+    int32_t* indices;              // [cu_k[batch]]
+    uint32_t* keys;                // [total_kv]
+    uint32_t* hist;                // [batch][kSelBins]
+    int32_t* tmp_pos;              // [total_kv]
+    uint32_t* tmp_key;             // [total_kv]
+    int32_t batch, hkv, W, total_kv;
+    int32_t nchunks;               // pass-1 workgroups per sequence
+};
+
+constexpr int kSelDigitBits = 12;
+constexpr int kSelBins = 1 << kSelDigitBits;
+constexpr int kSelChunk = 8192;    // positions per pass-1 workgroup
+
+hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+
+}  // namespace vegas

@@ -1,0 +1,162 @@
+"""Thin ctypes binding of libvegas.so (include/vegas.h).
+
+Argument marshalling only: every step of the hot path runs in the HIP
+kernels of the library.  Tensor arguments are torch tensors that already live
+on the GPU (torch supplies device memory and streams); they are passed as raw
+device pointers.  If the library has not been built, every call raises -- there
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libvegas.so")
+
+VEGAS_OK = 0
+VEGAS_ERR_INVALID_ARGUMENT = 1
+VEGAS_ERR_UNSUPPORTED = 2
+VEGAS_ERR_WORKSPACE_TOO_SMALL = 3
+VEGAS_ERR_HIP = 4
+
+VEGAS_DTYPE_F32 = 0
+VEGAS_DTYPE_BF16 = 1
+
+EXPORTED = (
+    "vegas_abi_version", "vegas_status_string", "vegas_last_error_message",
+    "vegas_verify_workspace_size", "vegas_verify_attn",
+    "vegas_select_workspace_size", "vegas_select_topk",
+    "vegas_sparse_decode_workspace_size", "vegas_sparse_decode_attn",
+)
+
+
+class VegasError(RuntimeError):
+    def __init__(self, status: int, fn: str, detail: str):
+        self.status = status
+        super().__init__(f"{fn} -> {status_string(status)}: {detail}")
+
+
+class AttnShape(ctypes.Structure):
+    """vegas_attn_shape_t."""
+    _fields_ = [("dtype", ctypes.c_int32), ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, U32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+        SP = ctypes.POINTER(AttnShape)
+        PSZ = ctypes.POINTER(ctypes.c_size_t)
+        sig = {
+            "vegas_abi_version": ([], I32),
+            "vegas_status_string": ([ctypes.c_int], ctypes.c_char_p),
+            "vegas_last_error_message": ([], ctypes.c_char_p),
+            "vegas_verify_workspace_size": ([SP, I32, I32, PSZ], ctypes.c_int),
+            "vegas_verify_attn": ([SP, I32, P, P, P, P, I32, I32, U32, P, P, P, SZ, P], ctypes.c_int),
+            "vegas_select_workspace_size": ([I32, I32, I32, I32, I32, PSZ], ctypes.c_int),
+            "vegas_select_topk": ([I32, I32, I32, P, P, I32, I32, P, P, P, SZ, P], ctypes.c_int),
+            "vegas_sparse_decode_workspace_size": ([SP, I32, PSZ], ctypes.c_int),
+            "vegas_sparse_decode_attn": ([SP, P, P, P, P, I32, P, P, I32, P, P, SZ, P], ctypes.c_int),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().vegas_status_string(status).decode()
+
+
+def _check(status: int, fn: str):
+    if status != VEGAS_OK:
+        raise VegasError(status, fn, lib().vegas_last_error_message().decode())
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def attn_shape(dtype: int, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+               softmax_scale: float) -> AttnShape:
+    return AttnShape(dtype, batch, num_q_heads, num_kv_heads, head_dim, softmax_scale)
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def vegas_abi_version() -> int:
+    return lib().vegas_abi_version()
+
+
+def vegas_verify_workspace_size(shape: AttnShape, gamma: int, max_seqlen_k: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().vegas_verify_workspace_size(ctypes.byref(shape), gamma, max_seqlen_k, ctypes.byref(n)),
+           "vegas_verify_workspace_size")
+    return n.value
+
+
+def vegas_verify_attn(shape: AttnShape, gamma: int, q, k, v, cu_seqlens_k, max_seqlen_k: int,
+                      total_kv: int, collect_mask: int, scores, out, workspace, stream=None) -> None:
+    _check(lib().vegas_verify_attn(ctypes.byref(shape), gamma, _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(cu_seqlens_k), max_seqlen_k, total_kv, collect_mask & 0xFFFFFFFF,
+                                   _ptr(scores), _ptr(out), _ptr(workspace), _nbytes(workspace),
+                                   _stream(stream)),
+           "vegas_verify_attn")
+
+
+def vegas_select_workspace_size(batch: int, num_kv_heads: int, gamma: int, max_seqlen_k: int,
+                                total_kv: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().vegas_select_workspace_size(batch, num_kv_heads, gamma, max_seqlen_k, total_kv,
+                                             ctypes.byref(n)),
+           "vegas_select_workspace_size")
+    return n.value
+
+
+def vegas_select_topk(batch: int, num_kv_heads: int, gamma: int, scores, cu_seqlens_k, max_seqlen_k: int,
+                      total_kv: int, cu_k, indices, workspace, stream=None) -> None:
+    _check(lib().vegas_select_topk(batch, num_kv_heads, gamma, _ptr(scores), _ptr(cu_seqlens_k), max_seqlen_k,
+                                   total_kv, _ptr(cu_k), _ptr(indices), _ptr(workspace), _nbytes(workspace),
+                                   _stream(stream)),
+           "vegas_select_topk")
+
+
+def vegas_sparse_decode_workspace_size(shape: AttnShape, max_idx: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().vegas_sparse_decode_workspace_size(ctypes.byref(shape), max_idx, ctypes.byref(n)),
+           "vegas_sparse_decode_workspace_size")
+    return n.value
+
+
+def vegas_sparse_decode_attn(shape: AttnShape, q, k, v, cu_seqlens_k, total_kv: int, indices, cu_idx,
+                             max_idx: int, out, workspace, stream=None) -> None:
+    _check(lib().vegas_sparse_decode_attn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k),
+                                          total_kv, _ptr(indices), _ptr(cu_idx), max_idx, _ptr(out),
+                                          _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "vegas_sparse_decode_attn")
