@@ -1,0 +1,265 @@
+"""Benchmark of the Vegas attention hot path on one MI355X.
+
+One step is one speculative decode iteration of the 128K Qwen3-8B-shaped
+workload (batch 4, 36 layers each with its own KV cache, 32 query / 8 KV
+heads, head_dim 128, prefix 131072, gamma 5, k = 5% = 6553 per sequence and
+layer, bf16): the verification pass runs verify (with Collect-2-Query) and
+select on every layer, then gamma drafting passes run the sparse decode on
+every layer.  The reported value is microseconds per layer-step
+(verify + select + gamma drafts of one layer) = step time / layers.
+
+Inputs are seeded synthetic tensors resident in HBM before timing starts.
+Per-call HIP events on the launch stream give each kernel's time inside the
+timed region; the HBM roofline uses algorithmic bytes (each KV byte of the
+verified cache read once, the selected rows gathered once per draft).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E, AMD's published figure
+METRIC = "µs per layer-step (verify+select+gamma drafts) and achieved HBM GB/s vs peak"
+
+
+def algorithmic_bytes(wl):
+    """Bytes the method must move, per call type, for one layer."""
+    es = 2 if wl.dtype == "bf16" else 4
+    B, Hq, Hkv, D, Wr = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.gamma + 1
+    total_kv = wl.total_kv
+    sumL = sum(wl.prefix_lens)
+    sumk = sum(wl.k_per_seq)
+    kv = total_kv * Hkv * D * es * 2
+    qo = B * Wr * Hq * D * es * 2
+    scores = Hkv * sumL * 4
+    verify = kv + qo + scores
+    select = scores + sumk * 4
+    draft = sumk * Hkv * D * es * 2 + sumk * 4 + B * Hq * D * es * 2
+    return {"verify": verify, "select": select, "draft": draft,
+            "layer_step": verify + select + wl.n_drafts * draft}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("attn.hip", "internal.h"):
+        with open(os.path.join(ROOT, "verification_guided_sparse_verify_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(profile_name, launches_key):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", profile_name)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for ln in open(path):
+        if "=" in ln and not ln.startswith("#"):
+            k, _, v = ln.partition("=")
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(kv[launches_key])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, layer_inputs, layer_steps, nseq):
+    """Time the CPU oracle on the first `nseq` sequences of layer 0 (verify, select over the
+    oracle's own scores, gamma drafts over the oracle's own selection)."""
+    import numpy as np
+    import oracle
+    from verification_guided_sparse_verify_amd import workloads as W
+
+    inp = layer_inputs[0]
+    cu = wl.cu_seqlens()
+    Wr = wl.gamma + 1
+    s1 = cu[nseq]
+    q = W.host_bits(inp["q"][: nseq * Wr])
+    k = W.host_bits(inp["k"][:s1])
+    v = W.host_bits(inp["v"][:s1])
+    dq = W.host_bits(inp["draft_q"][:, :nseq])
+    cus = np.array(cu[: nseq + 1], np.int32)
+    cuk = np.array(wl.cu_k()[: nseq + 1], np.int32)
+    oracle._lib()
+    t0 = time.perf_counter()
+    _, sc = oracle.verify_attn(q, k, v, cus, wl.gamma, wl.scale)
+    idx, _, _ = oracle.select_topk(sc, cus, wl.gamma, cuk)
+    for j in range(wl.n_drafts):
+        oracle.sparse_decode_attn(dq[j], k, v, cus, idx, cuk, wl.scale)
+    dt = time.perf_counter() - t0
+    omp = os.environ.get("OMP_NUM_THREADS")
+    threads = int(omp) if omp and omp.isdigit() else len(os.sched_getaffinity(0))
+    tasks = nseq * wl.num_kv_heads
+    return {
+        "value": round(dt * 1e6 * wl.batch / nseq, 1),
+        "unit": "us/layer-step",
+        "cores": min(threads, tasks),
+        "kind": "oracle",
+        "sample": (f"sequences 0..{nseq - 1} of {wl.batch} of layer 0 (verify + select + {wl.n_drafts} drafts), "
+                   f"{dt:.2f} s, scaled x{wl.batch / nseq:g} to one layer-step"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2, help="0-based workload index (default: 128K Qwen3-8B step)")
+    ap.add_argument("--layers", type=int, default=None, help="override the layer count (profiling runs only)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=2)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from verification_guided_sparse_verify_amd import workloads as W
+    from verification_guided_sparse_verify_amd import vegas as V
+    from verification_guided_sparse_verify_amd.step import LayerStep
+
+    if not os.path.exists(V.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    wl = W.named_workload(args.workload)
+    layers = args.layers if args.layers is not None else wl.layers
+    dev = "cuda:0"
+    t_gen = time.perf_counter()
+    layer_inputs, steps = [], []
+    for layer in range(layers):
+        inp = W.make_inputs(wl, seed=0, device=dev, layer=layer)
+        layer_inputs.append(inp)
+        steps.append(LayerStep(inp, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.gamma,
+                               wl.seqlens, wl.k_per_seq, wl.scale, n_drafts=wl.n_drafts))
+        if layer % 6 == 5:
+            torch.cuda.synchronize()
+            print(f"# generated layer {layer + 1}/{layers}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    print(f"# generated {layers} layers in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    ev_sets = []
+
+    def one_step(record):
+        evs = {"verify": [], "select": [], "draft": []} if record else None
+
+        def timed(kind, fn):
+            if record:
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                evs[kind].append((a, b))
+            else:
+                fn()
+
+        for st in steps:
+            timed("verify", lambda: st.verify(True))
+            timed("select", st.select)
+        for j in range(wl.n_drafts):
+            for st in steps:
+                timed("draft", lambda: st.draft(j))
+        if record:
+            ev_sets.append(evs)
+
+    for _ in range(args.warmup):
+        one_step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    per = {"verify": [], "select": [], "draft": []}
+    for evs in ev_sets:
+        for kind, pairs in evs.items():
+            per[kind].extend(a.elapsed_time(b) * 1e3 for a, b in pairs)   # microseconds
+    mean = {k: statistics.fmean(v) for k, v in per.items()}
+    med = {k: statistics.median(v) for k, v in per.items()}
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    us_layer_step = ms_per_step * 1e3 / layers
+    ab = algorithmic_bytes(wl)
+    step_gbps = ab["layer_step"] / (us_layer_step * 1e-6) / 1e9
+    verify_gbps = ab["verify"] / (mean["verify"] * 1e-6) / 1e9
+    traffic = read_traffic("attn_split_verify_qwen3_8b_128k_pmc.txt", "hbm_bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(us_layer_step, 2),
+        "unit": "us/layer-step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) K/V with planted heavy hitters, sinks and recency band)",
+        "config": {
+            "workload": wl.name if layers == wl.layers else f"{wl.name} (layers={layers})",
+            "batch": wl.batch, "layers": layers, "num_q_heads": wl.num_q_heads,
+            "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+            "prefix_lens": sorted(set(wl.prefix_lens)) if len(set(wl.prefix_lens)) <= 2 else "ragged",
+            "gamma": wl.gamma, "k_per_seq": wl.k_per_seq if len(set(wl.k_per_seq)) > 1 else wl.k_per_seq[0],
+            "kv_cache_bytes": wl.total_kv * wl.num_kv_heads * wl.head_dim * (2 if wl.dtype == "bf16" else 4) * 2 * layers,
+            "order": "verify+select over all layers, then gamma drafting passes over all layers",
+        },
+        "layer_step_gbps": round(step_gbps, 1),
+        "layer_step_frac_of_peak": round(step_gbps / PEAK_HBM_GBPS, 4),
+        "per_call_us": {k: {"mean": round(mean[k], 2), "median": round(med[k], 2)} for k in mean},
+        "collect_select_overhead_vs_plain_verify": None,
+        "roofline": {
+            "kernel": "verify: attn_split_kernel (+ attn_combine) per layer",
+            "bound": "hbm",
+            "achieved": round(verify_gbps, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(verify_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": ab["verify"],
+            "avg_launch_us": round(mean["verify"], 2),
+        },
+    }
+
+    # Plain verification (collection off) on the same layers, for the collection + select overhead.
+    plain = []
+    for _ in range(3):
+        for st in steps:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            st.verify(False)
+            b.record(stream)
+            plain.append((a, b))
+    torch.cuda.synchronize()
+    plain_us = statistics.fmean(a.elapsed_time(b) * 1e3 for a, b in plain)
+    result["plain_verify_us"] = round(plain_us, 2)
+    result["collect_select_overhead_vs_plain_verify"] = round((mean["verify"] + mean["select"]) / plain_us - 1, 4)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, layer_inputs, steps, min(args.cpu_seqs, wl.batch))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

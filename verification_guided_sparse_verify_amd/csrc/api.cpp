@@ -79,13 +79,24 @@ vegas_status_t check_shape(const vegas_attn_shape_t* s) {
     return VEGAS_OK;
 }
 
+// Query rows per KV head one workgroup can hold: 64, or 32 for fp32 at D = 128.
+int max_rows(const vegas_attn_shape_t* s) {
+    return (s->dtype == VEGAS_DTYPE_F32 && s->head_dim == 128) ? 32 : 64;
+}
+
 vegas_status_t check_gamma(int32_t gamma, const vegas_attn_shape_t* s) {
     if (gamma < 0 || gamma > 31) return fail(VEGAS_ERR_INVALID_ARGUMENT, "gamma %d outside 0..31", gamma);
     const int G = s->num_q_heads / s->num_kv_heads;
-    if ((gamma + 1) * G > 64)
-        return fail(VEGAS_ERR_UNSUPPORTED, "(gamma+1)*(Hq/Hkv) = %d exceeds 64 query rows per KV head",
-                    (gamma + 1) * G);
+    if ((gamma + 1) * G > max_rows(s))
+        return fail(VEGAS_ERR_UNSUPPORTED, "(gamma+1)*(Hq/Hkv) = %d exceeds %d query rows per KV head",
+                    (gamma + 1) * G, max_rows(s));
     return VEGAS_OK;
+}
+
+// Kernels address K/V with 32-bit byte offsets from a sequence's first row.
+bool rows_fit_32bit(const vegas_attn_shape_t* s, int64_t rows) {
+    const int64_t es = s->dtype == VEGAS_DTYPE_BF16 ? 2 : 4;
+    return rows * s->num_kv_heads * s->head_dim * es < (int64_t(1) << 32);
 }
 
 vegas_status_t hip_status(hipError_t e, const char* what) {
@@ -164,6 +175,8 @@ vegas_status_t vegas_verify_attn(const vegas_attn_shape_t* shape, int32_t gamma,
         return fail(VEGAS_ERR_INVALID_ARGUMENT, "max_seqlen_k %d < gamma+1 = %d", max_seqlen_k, W);
     if (total_kv < shape->batch * W)
         return fail(VEGAS_ERR_INVALID_ARGUMENT, "total_kv %d < batch*(gamma+1)", total_kv);
+    if (!rows_fit_32bit(shape, max_seqlen_k))
+        return fail(VEGAS_ERR_UNSUPPORTED, "one sequence's K/V rows span 4 GiB or more");
     const int G = shape->num_q_heads / shape->num_kv_heads;
     const AttnPlan plan = plan_attn(shape->batch, shape->num_kv_heads, W * G, shape->head_dim,
                                     max_seqlen_k, false);
@@ -251,7 +264,8 @@ vegas_status_t vegas_sparse_decode_workspace_size(const vegas_attn_shape_t* shap
     if (!bytes) return fail(VEGAS_ERR_INVALID_ARGUMENT, "bytes is NULL");
     if (max_idx < 0) return fail(VEGAS_ERR_INVALID_ARGUMENT, "max_idx %d < 0", max_idx);
     const int G = shape->num_q_heads / shape->num_kv_heads;
-    if (G > 64) return fail(VEGAS_ERR_UNSUPPORTED, "Hq/Hkv = %d exceeds 64", G);
+    if (G > max_rows(shape))
+        return fail(VEGAS_ERR_UNSUPPORTED, "Hq/Hkv = %d exceeds %d", G, max_rows(shape));
     *bytes = plan_attn(shape->batch, shape->num_kv_heads, G, shape->head_dim, max_idx, true).total();
     return VEGAS_OK;
 }

@@ -13,15 +13,16 @@
 // split).  Its four waves take 32-position blocks in turn.  All W*G query rows
 // that share KV head g (at most 64) are processed together, so every K/V byte
 // is read from HBM exactly once for all rows.  Per block and wave:
-//   S^T[pos, row] = K[pos, :] . Q[row, :]         16x16x32 bf16 MFMA, K from
-//                                                  registers (direct loads)
+//   S^T[pos, row] = K[pos, :] . Q[row, :]         16x16x32 bf16 MFMA; K straight
+//                                                  into registers, Q from LDS
 //   online softmax over positions (exp2 domain)    rows are MFMA columns, so a
 //                                                  row max is in-lane + 2 shuffles
-//   O^T[d, row] += V^T[d, pos] . P^T[pos, row]     V staged in LDS (swizzled),
-//                                                  read transposed
-// The P^T operand is the S^T accumulator itself: the k order of the MFMA is a
-// free permutation, so the four S^T values a lane owns for each of two 16-row
-// position tiles are exactly its eight k slots, and V^T is read in that order.
+//   O^T[d, row] += V^T[d, pos] . P^T[pos, row]     V copied HBM -> LDS by the
+//                                                  load-to-LDS path, read transposed
+// The P^T operand is the S^T accumulator itself: the k order of an MFMA is a
+// free permutation, so the four S^T values a lane owns for each of two
+// 16-position tiles are exactly its eight k slots, and V^T is read in that
+// order.  The next block's K and V are in flight while a block is computed.
 // Partials (m, l, O) of the four waves are merged in LDS and one partial per
 // workgroup goes to the workspace; attn_combine merges the splits.
 #include "internal.h"
@@ -31,14 +32,14 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr float kNegInf = -__builtin_inff();
-constexpr float kLog2e = 1.4426950408889634f;
 
 // Eight operand elements owned by one lane.
 template <bool BF16> struct Frag;
 template <> struct Frag<true> { uint4 u; };
-template <> struct Frag<false> { float f[8]; };
+template <> struct Frag<false> { uint4 u[2]; };
 
 template <bool BF16>
 __device__ __forceinline__ Frag<BF16> zero_frag() {
@@ -46,8 +47,8 @@ __device__ __forceinline__ Frag<BF16> zero_frag() {
     if constexpr (BF16) {
         r.u = make_uint4(0, 0, 0, 0);
     } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) r.f[i] = 0.f;
+        r.u[0] = make_uint4(0, 0, 0, 0);
+        r.u[1] = make_uint4(0, 0, 0, 0);
     }
     return r;
 }
@@ -59,10 +60,8 @@ __device__ __forceinline__ Frag<BF16> load_frag(const void* p) {
     if constexpr (BF16) {
         r.u = *reinterpret_cast<const uint4*>(p);
     } else {
-        const float4 a = reinterpret_cast<const float4*>(p)[0];
-        const float4 b = reinterpret_cast<const float4*>(p)[1];
-        r.f[0] = a.x; r.f[1] = a.y; r.f[2] = a.z; r.f[3] = a.w;
-        r.f[4] = b.x; r.f[5] = b.y; r.f[6] = b.z; r.f[7] = b.w;
+        r.u[0] = reinterpret_cast<const uint4*>(p)[0];
+        r.u[1] = reinterpret_cast<const uint4*>(p)[1];
     }
     return r;
 }
@@ -75,8 +74,11 @@ __device__ __forceinline__ f32x4_t mfma16(const Frag<true>& a, const Frag<true>&
                                                    __builtin_bit_cast(bf16x8_t, b.u), c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4_t mfma16(const Frag<false>& a, const Frag<false>& b, f32x4_t c) {
+    const uint32_t xs[8] = {a.u[0].x, a.u[0].y, a.u[0].z, a.u[0].w, a.u[1].x, a.u[1].y, a.u[1].z, a.u[1].w};
+    const uint32_t ys[8] = {b.u[0].x, b.u[0].y, b.u[0].z, b.u[0].w, b.u[1].x, b.u[1].y, b.u[1].z, b.u[1].w};
 #pragma unroll
-    for (int m = 0; m < 8; ++m) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.f[m], b.f[m], c, 0, 0, 0);
+    for (int m = 0; m < 8; ++m)
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(xs[m]), __uint_as_float(ys[m]), c, 0, 0, 0);
     return c;
 }
 
@@ -89,8 +91,10 @@ __device__ __forceinline__ Frag<BF16> pack_probs(const float (&p)[8]) {
         for (int i = 0; i < 8; ++i) v[i] = static_cast<__bf16>(p[i]);
         r.u = __builtin_bit_cast(uint4, v);
     } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) r.f[i] = p[i];
+        r.u[0] = make_uint4(__float_as_uint(p[0]), __float_as_uint(p[1]), __float_as_uint(p[2]),
+                            __float_as_uint(p[3]));
+        r.u[1] = make_uint4(__float_as_uint(p[4]), __float_as_uint(p[5]), __float_as_uint(p[6]),
+                            __float_as_uint(p[7]));
     }
     return r;
 }
@@ -114,6 +118,37 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Compiler barrier that also drains outstanding LDS operations of this wave.
 __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// One wave-wide 16-byte-per-lane copy HBM -> LDS: lane l's 16 bytes land at
+// lds + 16*l.  Issued as inline assembly on purpose: the compiler's wait
+// analysis would otherwise make every later LDS read wait for all copies in
+// flight, including the next block's.  Completion is ordered by vmcnt like
+// any load, and the block loop waits for it explicitly (wait_vmem).
+__device__ __forceinline__ void copy16_to_lds(const void* src, unsigned char* lds) {
+    const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds_addr) : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (they retire in issue order); also a compiler memory barrier.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Make the compiler treat a fragment as consumed here (it then waits for the
+// load that produced it at this point).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void keep_live(uint4& u) {
+    u32x4_t t = __builtin_bit_cast(u32x4_t, u);
+    asm volatile("" : "+v"(t));
+    u = __builtin_bit_cast(uint4, t);
+}
+__device__ __forceinline__ void keep_live(Frag<true>& f) { keep_live(f.u); }
+__device__ __forceinline__ void keep_live(Frag<false>& f) {
+    keep_live(f.u[0]);
+    keep_live(f.u[1]);
+}
+
 template <bool BF16, int D, int MB>
 struct Geo {
     static constexpr int ES = BF16 ? 2 : 4;       // element bytes
@@ -122,24 +157,206 @@ struct Geo {
     static constexpr int ROWB = D * ES;           // bytes of one K/V row of one head
     static constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
     static constexpr int EPC = 16 / ES;           // elements per chunk
-    static constexpr int RPI = 64 / CPR;          // V rows covered by one wave-wide 16-B load
-    static constexpr int VLD = kAttnBlock / RPI;  // V loads per lane per block
+    static constexpr int RPI = 64 / CPR;          // rows covered by one wave-wide 16-B copy
+    static constexpr int TLD = kAttnBlock / RPI;  // copies per lane per K (or V) tile
+    static constexpr int TILE = kAttnBlock * ROWB;
+    static constexpr int STAGE = 2 * TILE;        // K tile then V tile
+    static constexpr int NST = (kAttnWaves * 4 * STAGE <= 128 * 1024) ? 4 : 2;   // ring depth
+    static constexpr int RING = kAttnWaves * NST * STAGE;
+    static constexpr int BLOCK_OPS = 2 * TLD;     // copies one block issues
     static constexpr int SWZU = 16 / EPC;         // chunks per 16-element d tile
-    static constexpr int VBUF = kAttnBlock * ROWB;
+    static constexpr int KSWZ = CPR - 1 < 15 ? CPR - 1 : 15;
     static constexpr int NREG = DB * MB;          // O^T fragments per lane
     static constexpr int MSLOT = (NREG * 4 + 2 * MB) * 64 * 4;
-    static constexpr int MAIN = (kAttnWaves * VBUF > (kAttnWaves / 2) * MSLOT)
-                                    ? kAttnWaves * VBUF
-                                    : (kAttnWaves / 2) * MSLOT;
+    static constexpr int MAIN = RING > (kAttnWaves / 2) * MSLOT ? RING : (kAttnWaves / 2) * MSLOT;
 };
 
-// Byte offset of chunk cc of V row `row` inside a wave's tile.  The chunk
-// index is XOR-swizzled with the row's 4-row group so that the transposed
-// reads of the PV operand (four lane groups reading rows 4 apart, same d)
-// hit distinct LDS banks.
-template <class GEO>
-__device__ __forceinline__ int vtile_offset(int row, int cc) {
-    return row * GEO::ROWB + ((cc ^ (GEO::SWZU * ((row >> 2) & 3))) << 4);
+// Per-workgroup constants of the split kernel.  Offsets are 32-bit byte
+// offsets from the first token row of the sequence (the host bounds them).
+struct SplitCtx {
+    const unsigned char* kseq;
+    const unsigned char* vseq;
+    const int* idx_s;     // gather: staged index list of this split
+    int row_stride;       // bytes per token row: Hkv * D * element size
+    int head_off;         // g * D * element size
+    int start, end;       // position range of this split
+};
+
+// Byte offset of the row of position p (clamped into the split).
+template <bool GATHER>
+__device__ __forceinline__ uint32_t row_offset(const SplitCtx& c, int p) {
+    const int pc = min(p, c.end - 1);
+    const int t = GATHER ? c.idx_s[pc - c.start] : pc;
+    return (uint32_t)t * (uint32_t)c.row_stride + (uint32_t)c.head_off;
+}
+
+// Copy the K and V rows of the 16 positions from p0 into one ring stage.
+// Copy i of a tile fills LDS bytes [1024*i, 1024*i+1024): lane l lands on
+// row RPI*i + l/CPR at chunk position l%CPR, and fetches the global chunk the
+// tile's swizzle puts there.  K chunks are XORed with the row (so the 16
+// lanes reading one chunk column of 16 rows hit distinct banks); V chunks are
+// XORed with the row's 4-row group (so the transposed reads, four lane groups
+// on rows 4 apart, hit distinct banks).
+template <class GEO, bool GATHER>
+__device__ __forceinline__ void issue_block(const SplitCtx& c, int p0, int lane, unsigned char* stage) {
+#pragma unroll
+    for (int i = 0; i < GEO::TLD; ++i) {
+        const int row = i * GEO::RPI + lane / GEO::CPR;
+        const int cc = (lane % GEO::CPR) ^ (row & GEO::KSWZ);
+        copy16_to_lds(c.kseq + row_offset<GATHER>(c, p0 + row) + cc * 16, stage + i * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < GEO::TLD; ++i) {
+        const int row = i * GEO::RPI + lane / GEO::CPR;
+        const int cc = (lane % GEO::CPR) ^ (GEO::SWZU * ((row >> 2) & 3));
+        copy16_to_lds(c.vseq + row_offset<GATHER>(c, p0 + row) + cc * 16, stage + GEO::TILE + i * 1024);
+    }
+}
+
+// Per-wave running state of the online softmax.
+template <bool BF16, int D, int MB>
+struct WaveState {
+    Frag<BF16> qf[MB][D / 32];
+    float cmask[MB];
+    int rrow[MB];
+    float m_run[MB], l_run[MB];
+    f32x4_t o[D / 16][MB];
+};
+
+// PV step: acc += V^T(16 d x 16 pos) . P^T(16 pos x 16 rows).  Lane (lr, lg)
+// supplies d (resp. row) lr and the k slots = positions 4*lg .. 4*lg+3, which
+// is where the S^T accumulator left its probabilities.
+__device__ __forceinline__ f32x4_t mfma_pv(const uint32_t (&vt)[4], const float (&p)[4], f32x4_t acc,
+                                           std::true_type) {
+    typedef short s16x4_t __attribute__((ext_vector_type(4)));
+    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+    bf16x4_t pb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pb[i] = static_cast<__bf16>(p[i]);
+    s16x4_t va;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) va[i] = (short)vt[i];
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, __builtin_bit_cast(s16x4_t, pb), acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_pv(const uint32_t (&vt)[4], const float (&p)[4], f32x4_t acc,
+                                           std::false_type) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vt[m]), p[m], acc, 0, 0, 0);
+    return acc;
+}
+
+// One 16-position block: S^T, collection, mask, online softmax, O^T += V^T P^T.
+template <class GEO, bool BF16, int D, int MB, bool GATHER, bool COLLECT>
+__device__ __forceinline__ void compute_block(const AttnArgs& a, WaveState<BF16, D, MB>& ws, int p0, int L,
+                                              int end, int seq0, int g, int lane, const unsigned char* stage) {
+    constexpr int DC = D / 32, DB = D / 16, EPC = GEO::EPC;
+    const int lr = lane & 15, lg = lane >> 4;
+    const unsigned char* kt = stage;
+    const unsigned char* vtile = stage + GEO::TILE;
+
+    // S^T tile: 16 positions (MFMA rows) x 16 query rows per qb (MFMA columns).
+    f32x4_t s[MB];
+#pragma unroll
+    for (int qb = 0; qb < MB; ++qb) s[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ch = 0; ch < DC; ++ch) {
+        Frag<BF16> kf;
+        if constexpr (BF16) {
+            const int cc = 4 * ch + lg;
+            kf.u = *reinterpret_cast<const uint4*>(kt + lr * GEO::ROWB + ((cc ^ (lr & GEO::KSWZ)) << 4));
+        } else {
+            const int cc = 8 * ch + 2 * lg;
+            kf.u[0] = *reinterpret_cast<const uint4*>(kt + lr * GEO::ROWB + ((cc ^ (lr & GEO::KSWZ)) << 4));
+            kf.u[1] = *reinterpret_cast<const uint4*>(kt + lr * GEO::ROWB + (((cc + 1) ^ (lr & GEO::KSWZ)) << 4));
+        }
+#pragma unroll
+        for (int qb = 0; qb < MB; ++qb) s[qb] = mfma16(kf, ws.qf[qb][ch], s[qb]);
+    }
+
+    // Collect-2-Query: per prefix position, the collected rows' logits summed
+    // over the query heads of this KV head (a reduction over the 16 lanes
+    // holding the query rows), times s.
+    if constexpr (COLLECT) {
+        if (p0 < L) {
+            float red[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                float x = 0.f;
+#pragma unroll
+                for (int qb = 0; qb < MB; ++qb) x += ws.cmask[qb] * s[qb][v];
+                red[v] = row16_sum(x);
+            }
+            if (lr < 4) {
+                float val = red[0];
+                val = (lr == 1) ? red[1] : val;
+                val = (lr == 2) ? red[2] : val;
+                val = (lr == 3) ? red[3] : val;
+                const int pos = p0 + 4 * lg + lr;
+                if (pos < L && pos < end) a.scores[(size_t)g * a.total_kv + seq0 + pos] = a.scale * val;
+            }
+        }
+    }
+
+    const bool need_mask = GATHER ? (p0 + kAttnBlock > end) : (p0 + kAttnBlock > min(end, L + 1));
+    if (need_mask) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int pos = p0 + 4 * lg + v;
+#pragma unroll
+            for (int qb = 0; qb < MB; ++qb) {
+                const bool vis = pos < end && (GATHER || pos <= L + ws.rrow[qb]);
+                if (!vis) s[qb][v] = kNegInf;
+            }
+        }
+    }
+
+    float pr[MB][4];
+    bool rescale = false;
+    float alpha[MB];
+#pragma unroll
+    for (int qb = 0; qb < MB; ++qb) {
+        float mx = fmaxf(fmaxf(s[qb][0], s[qb][1]), fmaxf(s[qb][2], s[qb][3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx *= a.scale_log2;
+        const float m_new = fmaxf(ws.m_run[qb], mx);
+        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+        alpha[qb] = fast_exp2(ws.m_run[qb] - m_use);
+        rescale |= (alpha[qb] != 1.f);
+        ws.m_run[qb] = m_new;
+        float ls = 0.f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float p = fast_exp2(fmaf(s[qb][v], a.scale_log2, -m_use));
+            pr[qb][v] = p;
+            ls += p;
+        }
+        ws.l_run[qb] = fmaf(ws.l_run[qb], alpha[qb], ls);
+    }
+    if (__any(rescale)) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int qb = 0; qb < MB; ++qb) ws.o[db][qb] *= alpha[qb];
+    }
+
+    // O^T += V^T P^T over the 16 positions of the block.
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        const int d = 16 * db + lr;
+        const unsigned char* base = vtile + (4 * lg) * GEO::ROWB +
+                                    (((d / EPC) ^ (GEO::SWZU * lg)) << 4) + (d % EPC) * GEO::ES;
+        uint32_t vt[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            if constexpr (BF16) vt[m] = *reinterpret_cast<const uint16_t*>(base + m * GEO::ROWB);
+            else vt[m] = *reinterpret_cast<const uint32_t*>(base + m * GEO::ROWB);
+        }
+#pragma unroll
+        for (int qb = 0; qb < MB; ++qb)
+            ws.o[db][qb] = mfma_pv(vt, pr[qb], ws.o[db][qb], std::integral_constant<bool, BF16>());
+    }
+    lds_fence();   // this stage's reads are done before it is refilled
 }
 
 template <bool BF16, int D, int MB, bool GATHER, bool COLLECT>
@@ -147,14 +364,14 @@ __global__ void __launch_bounds__(kAttnWaves * 64)
 attn_split_kernel(const AttnArgs a) {
     using GEO = Geo<BF16, D, MB>;
     using T = typename std::conditional<BF16, uint16_t, float>::type;
-    constexpr int DC = GEO::DC, DB = GEO::DB, CPR = GEO::CPR, EPC = GEO::EPC;
-    constexpr int RPI = GEO::RPI, VLD = GEO::VLD, NREG = GEO::NREG;
+    constexpr int DC = GEO::DC, DB = GEO::DB, NREG = GEO::NREG, NST = GEO::NST;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[GEO::MAIN];
     __shared__ int idx_s[GATHER ? kMaxGatherChunk : 1];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // wave index as a scalar: every branch on it is uniform
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lr = lane & 15;
     const int lg = lane >> 4;
 
@@ -165,7 +382,7 @@ attn_split_kernel(const AttnArgs a) {
     const int b = wg / a.nsplit;
 
     const int seq0 = a.cu_seqlens_k[b];
-    const int n_b = a.cu_seqlens_k[b + 1] - seq0;
+    const int n_b = min(a.cu_seqlens_k[b + 1], a.total_kv) - seq0;
     int count, L, ib0 = 0;
     if constexpr (GATHER) {
         ib0 = a.cu_idx[b];
@@ -176,7 +393,7 @@ attn_split_kernel(const AttnArgs a) {
         L = n_b - a.W;
     }
     const int start = split * a.chunk;
-    if (n_b <= 0 || start >= count) return;          // uniform per workgroup
+    if (seq0 < 0 || n_b <= 0 || start >= count) return;          // uniform per workgroup
     const int end = min(start + a.chunk, count);
 
     if constexpr (GATHER) {
@@ -187,227 +404,66 @@ attn_split_kernel(const AttnArgs a) {
         __syncthreads();
     }
 
-    const T* __restrict__ kbase = static_cast<const T*>(a.k);
-    const T* __restrict__ vbase = static_cast<const T*>(a.v);
-    const int last_tok = a.total_kv - 1;
-    auto token = [&](int p) -> int {
-        const int pc = min(p, end - 1);
-        int t;
-        if constexpr (GATHER) t = seq0 + idx_s[pc - start];
-        else t = seq0 + pc;
-        return min(max(t, 0), last_tok);
-    };
-
-    // Q fragments (B operand of S^T): lane holds query row 16*qb + lr.
-    Frag<BF16> qf[MB][DC];
-    float cmask[MB];
-    int rrow[MB];
+    WaveState<BF16, D, MB> ws;
 #pragma unroll
     for (int qb = 0; qb < MB; ++qb) {
+        // B operand of S^T: query row 16*qb + lane%16, elements 32*ch + 8*(lane/16) .. +7
         const int j = 16 * qb + lr;
         const bool valid = j < a.M;
         const int r = valid ? j / a.G : a.W - 1;
         const int hl = valid ? j % a.G : 0;
-        rrow[qb] = r;
-        cmask[qb] = (COLLECT && valid && ((a.collect_mask >> r) & 1u)) ? 1.f : 0.f;
+        ws.rrow[qb] = r;
+        ws.cmask[qb] = (COLLECT && valid && ((a.collect_mask >> r) & 1u)) ? 1.f : 0.f;
         const T* qp = static_cast<const T*>(a.q) +
                       ((size_t)(b * a.W + r) * a.hq + (size_t)g * a.G + hl) * D + 8 * lg;
 #pragma unroll
-        for (int c = 0; c < DC; ++c) qf[qb][c] = valid ? load_frag<BF16>(qp + 32 * c) : zero_frag<BF16>();
-    }
-
-    float m_run[MB], l_run[MB];
-    f32x4_t o[DB][MB];
+        for (int ch = 0; ch < DC; ++ch) ws.qf[qb][ch] = valid ? load_frag<BF16>(qp + 32 * ch) : zero_frag<BF16>();
+        ws.m_run[qb] = kNegInf;
+        ws.l_run[qb] = 0.f;
 #pragma unroll
-    for (int qb = 0; qb < MB; ++qb) {
-        m_run[qb] = kNegInf;
-        l_run[qb] = 0.f;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[db][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int db = 0; db < DB; ++db) ws.o[db][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+    // Retire the Q loads here, where the compiler can see it, so that its own
+    // wait for them is not placed inside the block loop.
+#pragma unroll
+    for (int qb = 0; qb < MB; ++qb)
+#pragma unroll
+        for (int ch = 0; ch < DC; ++ch) keep_live(ws.qf[qb][ch]);
 
-    unsigned char* vtile = smem + wave * GEO::VBUF;
+    SplitCtx c;
+    c.row_stride = a.hkv * D * GEO::ES;
+    c.head_off = g * D * GEO::ES;
+    c.kseq = static_cast<const unsigned char*>(a.k) + (size_t)seq0 * c.row_stride;
+    c.vseq = static_cast<const unsigned char*>(a.v) + (size_t)seq0 * c.row_stride;
+    c.idx_s = idx_s;
+    c.start = start;
+    c.end = end;
+
+    // This wave's blocks are wave, wave+NW, ...; a ring of NST stages keeps
+    // NST-1 of them in flight.  A block past the last one is replaced by the
+    // last one (re-fetched, served by the caches) so that every iteration
+    // issues the same number of copies and the wait count stays exact.
     const int nblk = (end - start + kAttnBlock - 1) / kAttnBlock;
-
-    Frag<BF16> kc[2][DC];
-    uint4 vc[VLD];
-    auto load_block = [&](int p0, Frag<BF16> (&kf)[2][DC], uint4 (&vr)[VLD]) {
+    const int nmine = wave < nblk ? (nblk - wave + kAttnWaves - 1) / kAttnWaves : 0;
+    unsigned char* ring = smem + wave * (NST * GEO::STAGE);
+    auto block_pos = [&](int jj) { return start + (wave + kAttnWaves * min(jj, nmine - 1)) * kAttnBlock; };
+    if (nmine > 0) {
 #pragma unroll
-        for (int pb = 0; pb < 2; ++pb) {
-            const int tok = token(p0 + 16 * pb + lr);
-            const T* kp = kbase + ((size_t)tok * a.hkv + g) * D + 8 * lg;
-#pragma unroll
-            for (int c = 0; c < DC; ++c) kf[pb][c] = load_frag<BF16>(kp + 32 * c);
+        for (int st = 0; st < NST - 1; ++st) issue_block<GEO, GATHER>(c, block_pos(st), lane, ring + st * GEO::STAGE);
+        for (int jj = 0; jj < nmine; ++jj) {
+            wait_vmem<(NST - 2) * GEO::BLOCK_OPS>();      // block jj has landed
+            issue_block<GEO, GATHER>(c, block_pos(jj + NST - 1), lane, ring + ((jj + NST - 1) % NST) * GEO::STAGE);
+            compute_block<GEO, BF16, D, MB, GATHER, COLLECT>(a, ws, block_pos(jj), L, end, seq0, g, lane,
+                                                              ring + (jj % NST) * GEO::STAGE);
         }
-#pragma unroll
-        for (int i = 0; i < VLD; ++i) {
-            const int row = lane / CPR + i * RPI;
-            const int tok = token(p0 + row);
-            vr[i] = *reinterpret_cast<const uint4*>(vbase + ((size_t)tok * a.hkv + g) * D +
-                                                     (lane % CPR) * EPC);
-        }
-    };
-
-    int bi = wave;
-    if (bi < nblk) load_block(start + bi * kAttnBlock, kc, vc);
-    for (; bi < nblk; bi += kAttnWaves) {
-        const int p0 = start + bi * kAttnBlock;
-        const bool more = bi + kAttnWaves < nblk;
-        Frag<BF16> kn[2][DC];
-        uint4 vn[VLD];
-        if (more) load_block(p0 + kAttnWaves * kAttnBlock, kn, vn);
-
-        // Stage this block's V tile in the wave's LDS buffer.
-#pragma unroll
-        for (int i = 0; i < VLD; ++i) {
-            const int row = lane / CPR + i * RPI;
-            *reinterpret_cast<uint4*>(vtile + vtile_offset<GEO>(row, lane % CPR)) = vc[i];
-        }
-
-        // S^T tile: positions (MFMA rows) x query rows (MFMA columns), raw dot products.
-        f32x4_t s[2][MB];
-#pragma unroll
-        for (int pb = 0; pb < 2; ++pb)
-#pragma unroll
-            for (int qb = 0; qb < MB; ++qb) {
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int c = 0; c < DC; ++c) acc = mfma16(kc[pb][c], qf[qb][c], acc);
-                s[pb][qb] = acc;
-            }
-
-        // Collect-2-Query: per prefix position, sum the logits of the collected
-        // rows over the query heads of this KV head (a row reduction across the
-        // 16 lanes that hold the query rows), scaled by s.
-        if constexpr (COLLECT) {
-            if (p0 < L) {
-                float red[2][4];
-#pragma unroll
-                for (int pb = 0; pb < 2; ++pb)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        float x = 0.f;
-#pragma unroll
-                        for (int qb = 0; qb < MB; ++qb) x += cmask[qb] * s[pb][qb][v];
-                        red[pb][v] = row16_sum(x);
-                    }
-                if (lr < 8) {
-                    const int pb = lr >> 2, v = lr & 3;
-                    float val = red[0][0];
-                    val = (lr == 1) ? red[0][1] : val;
-                    val = (lr == 2) ? red[0][2] : val;
-                    val = (lr == 3) ? red[0][3] : val;
-                    val = (lr == 4) ? red[1][0] : val;
-                    val = (lr == 5) ? red[1][1] : val;
-                    val = (lr == 6) ? red[1][2] : val;
-                    val = (lr == 7) ? red[1][3] : val;
-                    const int pos = p0 + 16 * pb + 4 * lg + v;
-                    if (pos < L && pos < end) a.scores[(size_t)g * a.total_kv + seq0 + pos] = a.scale * val;
-                }
-            }
-        }
-
-        // Mask positions past the range and, for verification, past L + r.
-        const bool need_mask = GATHER ? (p0 + kAttnBlock > end) : (p0 + kAttnBlock > min(end, L + 1));
-        if (need_mask) {
-#pragma unroll
-            for (int pb = 0; pb < 2; ++pb)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int pos = p0 + 16 * pb + 4 * lg + v;
-#pragma unroll
-                    for (int qb = 0; qb < MB; ++qb) {
-                        const bool vis = pos < end && (GATHER || pos <= L + rrow[qb]);
-                        if (!vis) s[pb][qb][v] = kNegInf;
-                    }
-                }
-        }
-
-        // Online softmax in the exp2 domain.
-        float pr[MB][8];
-        bool rescale = false;
-        float alpha[MB];
-#pragma unroll
-        for (int qb = 0; qb < MB; ++qb) {
-            float mx = kNegInf;
-#pragma unroll
-            for (int pb = 0; pb < 2; ++pb)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[pb][qb][v]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            mx *= a.scale_log2;
-            const float m_new = fmaxf(m_run[qb], mx);
-            const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-            alpha[qb] = fast_exp2(m_run[qb] - m_use);
-            rescale |= (alpha[qb] != 1.f);
-            m_run[qb] = m_new;
-            float ls = 0.f;
-#pragma unroll
-            for (int pb = 0; pb < 2; ++pb)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float p = fast_exp2(fmaf(s[pb][qb][v], a.scale_log2, -m_use));
-                    pr[qb][4 * pb + v] = p;
-                    ls += p;
-                }
-            l_run[qb] = fmaf(l_run[qb], alpha[qb], ls);
-        }
-        if (__any(rescale)) {
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int qb = 0; qb < MB; ++qb) o[db][qb] *= alpha[qb];
-        }
-
-        // O^T += V^T P^T.  k slot m of lane group lg is position 4*lg+m (m<4)
-        // or 16+4*lg+(m-4) (m>=4): the S^T layout.
-        Frag<BF16> pf[MB];
-#pragma unroll
-        for (int qb = 0; qb < MB; ++qb) pf[qb] = pack_probs<BF16>(pr[qb]);
-        lds_fence();
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const int d = 16 * db + lr;
-            const unsigned char* base = vtile + (4 * lg) * GEO::ROWB +
-                                        (((d / EPC) ^ (GEO::SWZU * lg)) << 4) + (d % EPC) * GEO::ES;
-            Frag<BF16> vt;
-            if constexpr (BF16) {
-                uint32_t e[8];
-#pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    const int row = (m < 4) ? m : 12 + m;
-                    e[m] = *reinterpret_cast<const uint16_t*>(base + row * GEO::ROWB);
-                }
-                vt.u = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
-                                  e[6] | (e[7] << 16));
-            } else {
-#pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    const int row = (m < 4) ? m : 12 + m;
-                    vt.f[m] = *reinterpret_cast<const float*>(base + row * GEO::ROWB);
-                }
-            }
-#pragma unroll
-            for (int qb = 0; qb < MB; ++qb) o[db][qb] = mfma16(vt, pf[qb], o[db][qb]);
-        }
-        lds_fence();
-
-        if (more) {
-#pragma unroll
-            for (int pb = 0; pb < 2; ++pb)
-#pragma unroll
-                for (int c = 0; c < DC; ++c) kc[pb][c] = kn[pb][c];
-#pragma unroll
-            for (int i = 0; i < VLD; ++i) vc[i] = vn[i];
-        }
+        wait_vmem<0>();
     }
 
     // Row sums: each lane summed its own positions.
 #pragma unroll
     for (int qb = 0; qb < MB; ++qb) {
-        l_run[qb] += __shfl_xor(l_run[qb], 16);
-        l_run[qb] += __shfl_xor(l_run[qb], 32);
+        ws.l_run[qb] += __shfl_xor(ws.l_run[qb], 16);
+        ws.l_run[qb] += __shfl_xor(ws.l_run[qb], 32);
     }
 
     // Tree merge of the waves' (m, l, O) through LDS, in fragment order.
@@ -422,11 +478,11 @@ attn_split_kernel(const AttnArgs a) {
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int qb = 0; qb < MB; ++qb)
-                    *reinterpret_cast<f32x4_t*>(slot + ((db * MB + qb) * 64 + lane) * 4) = o[db][qb];
+                    *reinterpret_cast<f32x4_t*>(slot + ((db * MB + qb) * 64 + lane) * 4) = ws.o[db][qb];
 #pragma unroll
             for (int qb = 0; qb < MB; ++qb) {
-                slot[NREG * 256 + qb * 64 + lane] = m_run[qb];
-                slot[NREG * 256 + (MB + qb) * 64 + lane] = l_run[qb];
+                slot[NREG * 256 + qb * 64 + lane] = ws.m_run[qb];
+                slot[NREG * 256 + (MB + qb) * 64 + lane] = ws.l_run[qb];
             }
         }
         __syncthreads();
@@ -436,17 +492,17 @@ attn_split_kernel(const AttnArgs a) {
             for (int qb = 0; qb < MB; ++qb) {
                 const float mb = slot[NREG * 256 + qb * 64 + lane];
                 const float lb = slot[NREG * 256 + (MB + qb) * 64 + lane];
-                const float mm = fmaxf(m_run[qb], mb);
+                const float mm = fmaxf(ws.m_run[qb], mb);
                 if (mm != kNegInf) {
-                    const float ca = fast_exp2(m_run[qb] - mm);
+                    const float ca = fast_exp2(ws.m_run[qb] - mm);
                     const float cb = fast_exp2(mb - mm);
-                    m_run[qb] = mm;
-                    l_run[qb] = ca * l_run[qb] + cb * lb;
+                    ws.m_run[qb] = mm;
+                    ws.l_run[qb] = ca * ws.l_run[qb] + cb * lb;
 #pragma unroll
                     for (int db = 0; db < DB; ++db) {
                         const f32x4_t ob =
                             *reinterpret_cast<const f32x4_t*>(slot + ((db * MB + qb) * 64 + lane) * 4);
-                        o[db][qb] = ca * o[db][qb] + cb * ob;
+                        ws.o[db][qb] = ca * ws.o[db][qb] + cb * ob;
                     }
                 }
             }
@@ -460,60 +516,73 @@ attn_split_kernel(const AttnArgs a) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int qb = 0; qb < MB; ++qb) po[(db * MB + qb) * 64 + lane] = o[db][qb];
+            for (int qb = 0; qb < MB; ++qb) po[(db * MB + qb) * 64 + lane] = ws.o[db][qb];
         if (lg == 0) {
 #pragma unroll
             for (int qb = 0; qb < MB; ++qb) {
                 float2* pml = reinterpret_cast<float2*>(a.part_ml) + slot * (MB * 16) + qb * 16 + lr;
-                *pml = make_float2(m_run[qb], l_run[qb]);
+                *pml = make_float2(ws.m_run[qb], ws.l_run[qb]);
             }
         }
     }
 }
 
-// Merge the split partials of one (sequence, KV head, 16-row tile) and write
-// the normalised output rows in the storage dtype.
+// Merge the split partials of one (sequence, KV head, 16-row tile, 16-wide d
+// tile) and write the normalised output in the storage dtype.  One wave; each
+// lane owns one float4 of the fragment layout; eight splits' loads are in
+// flight at a time.
 template <bool BF16, int D, int MB, bool GATHER>
-__global__ void __launch_bounds__(64 * (D / 16))
-attn_combine_kernel(const AttnArgs a) {
+__global__ void __launch_bounds__(64) attn_combine_kernel(const AttnArgs a) {
     constexpr int DB = D / 16;
     constexpr int NREG = DB * MB;
+    constexpr int U = 8;
     int wg = blockIdx.x;
+    const int db = wg % DB;
+    wg /= DB;
     const int qb = wg % MB;
     wg /= MB;
     const int g = wg % a.hkv;
     const int b = wg / a.hkv;
-    const int db = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
+    const int lane = threadIdx.x;
     const int lr = lane & 15;
     const int lg = lane >> 4;
     const int j = 16 * qb + lr;
-    if (j >= a.M) return;
 
-    const int n_b = a.cu_seqlens_k[b + 1] - a.cu_seqlens_k[b];
+    const int seq0 = a.cu_seqlens_k[b];
+    const int n_b = min(a.cu_seqlens_k[b + 1], a.total_kv) - seq0;
     const int count = GATHER ? (a.cu_idx[b + 1] - a.cu_idx[b]) : n_b;
-    int nsv = (n_b > 0 && count > 0) ? (count + a.chunk - 1) / a.chunk : 0;
+    int nsv = (seq0 >= 0 && n_b > 0 && count > 0) ? (count + a.chunk - 1) / a.chunk : 0;
     nsv = min(nsv, a.nsplit);
 
     float mr = kNegInf, den = 0.f;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     const size_t slot0 = ((size_t)b * a.hkv + g) * a.nsplit;
-    for (int s = 0; s < nsv; ++s) {
-        const size_t slot = slot0 + s;
-        const float2 ml = reinterpret_cast<const float2*>(a.part_ml)[slot * (MB * 16) + j];
-        if (ml.x == kNegInf) continue;
-        const f32x4_t ov =
-            reinterpret_cast<const f32x4_t*>(a.part_o)[slot * (NREG * 64) + (db * MB + qb) * 64 + lane];
-        if (ml.x > mr) {
-            const float c = fast_exp2(mr - ml.x);
-            acc *= c;
-            den *= c;
-            mr = ml.x;
+    const float2* pml = reinterpret_cast<const float2*>(a.part_ml);
+    const f32x4_t* po = reinterpret_cast<const f32x4_t*>(a.part_o);
+    for (int s0 = 0; s0 < nsv; s0 += U) {
+        float2 ml[U];
+        f32x4_t ov[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = min(s0 + u, nsv - 1);
+            ml[u] = pml[(slot0 + s) * (MB * 16) + j];
+            ov[u] = po[(slot0 + s) * (NREG * 64) + (db * MB + qb) * 64 + lane];
         }
-        const float w = fast_exp2(ml.x - mr);
-        acc += w * ov;
-        den += w * ml.y;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (s0 + u >= nsv || ml[u].x == kNegInf) continue;
+            if (ml[u].x > mr) {
+                const float cf = fast_exp2(mr - ml[u].x);
+                acc *= cf;
+                den *= cf;
+                mr = ml[u].x;
+            }
+            const float w = fast_exp2(ml[u].x - mr);
+            acc += w * ov[u];
+            den += w * ml[u].y;
+        }
     }
+    if (j >= a.M) return;
     const float inv = den > 0.f ? 1.f / den : 0.f;
     acc *= inv;
 
@@ -536,25 +605,25 @@ attn_combine_kernel(const AttnArgs a) {
 template <bool BF16, int D, int MB, bool GATHER, bool COLLECT>
 hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
     const unsigned split_grid = (unsigned)(a.batch * a.hkv * a.nsplit);
-    const unsigned comb_grid = (unsigned)(a.batch * a.hkv * MB);
+    const unsigned comb_grid = (unsigned)(a.batch * a.hkv * MB * (D / 16));
     if (split_grid > 0)
         hipLaunchKernelGGL((attn_split_kernel<BF16, D, MB, GATHER, COLLECT>), dim3(split_grid),
                            dim3(kAttnWaves * 64), 0, stream, a);
     if (comb_grid > 0)
-        hipLaunchKernelGGL((attn_combine_kernel<BF16, D, MB, GATHER>), dim3(comb_grid),
-                           dim3(64 * (D / 16)), 0, stream, a);
+        hipLaunchKernelGGL((attn_combine_kernel<BF16, D, MB, GATHER>), dim3(comb_grid), dim3(64), 0, stream, a);
     return hipGetLastError();
 }
 
 template <bool BF16, int D, bool GATHER, bool COLLECT>
 hipError_t launch_mb(const AttnArgs& a, int mb, hipStream_t s) {
-    switch (mb) {
-        case 1: return launch_t<BF16, D, 1, GATHER, COLLECT>(a, s);
-        case 2: return launch_t<BF16, D, 2, GATHER, COLLECT>(a, s);
-        case 3: return launch_t<BF16, D, 3, GATHER, COLLECT>(a, s);
-        case 4: return launch_t<BF16, D, 4, GATHER, COLLECT>(a, s);
-        default: return hipErrorInvalidValue;
+    if (mb == 1) return launch_t<BF16, D, 1, GATHER, COLLECT>(a, s);
+    if (mb == 2) return launch_t<BF16, D, 2, GATHER, COLLECT>(a, s);
+    // fp32 at D = 128 stops at 32 rows per KV head (LDS budget)
+    if constexpr (BF16 || D == 64) {
+        if (mb == 3) return launch_t<BF16, D, 3, GATHER, COLLECT>(a, s);
+        if (mb == 4) return launch_t<BF16, D, 4, GATHER, COLLECT>(a, s);
     }
+    return hipErrorInvalidValue;
 }
 
 template <bool BF16, bool GATHER, bool COLLECT>

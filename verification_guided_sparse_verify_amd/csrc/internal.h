@@ -10,7 +10,7 @@ namespace vegas {
 
 // Waves per attention workgroup and positions per wave iteration.
 constexpr int kAttnWaves = 4;
-constexpr int kAttnBlock = 32;
+constexpr int kAttnBlock = 16;
 // Longest position range one workgroup takes in gather mode: its index list
 // is staged in LDS.
 constexpr int kMaxGatherChunk = 2048;
