@@ -74,41 +74,57 @@ def read_traffic(profile_name, launches_key):
         return None
 
 
-def cpu_baseline(wl, layer_inputs, layer_steps, nseq):
-    """Time the CPU oracle on the first `nseq` sequences of layer 0 (verify, select over the
-    oracle's own scores, gamma drafts over the oracle's own selection)."""
+def cpu_baseline(wl, layer_inputs, min_seconds=10.0):
+    """Time the CPU oracle on whole layers of the same workload (verify, select over the
+    oracle's own scores, gamma drafts over the oracle's own selection), one layer after
+    another until at least `min_seconds` of CPU work, and scale to one layer-step."""
     import numpy as np
     import oracle
     from verification_guided_sparse_verify_amd import workloads as W
 
-    inp = layer_inputs[0]
-    cu = wl.cu_seqlens()
-    Wr = wl.gamma + 1
-    s1 = cu[nseq]
-    q = W.host_bits(inp["q"][: nseq * Wr])
-    k = W.host_bits(inp["k"][:s1])
-    v = W.host_bits(inp["v"][:s1])
-    dq = W.host_bits(inp["draft_q"][:, :nseq])
-    cus = np.array(cu[: nseq + 1], np.int32)
-    cuk = np.array(wl.cu_k()[: nseq + 1], np.int32)
+    cus = np.array(wl.cu_seqlens(), np.int32)
+    cuk = np.array(wl.cu_k(), np.int32)
     oracle._lib()
-    t0 = time.perf_counter()
-    _, sc = oracle.verify_attn(q, k, v, cus, wl.gamma, wl.scale)
-    idx, _, _ = oracle.select_topk(sc, cus, wl.gamma, cuk)
-    for j in range(wl.n_drafts):
-        oracle.sparse_decode_attn(dq[j], k, v, cus, idx, cuk, wl.scale)
-    dt = time.perf_counter() - t0
+    spent, done = 0.0, 0
+    for inp in layer_inputs:
+        q = W.host_bits(inp["q"])
+        k = W.host_bits(inp["k"])
+        v = W.host_bits(inp["v"])
+        dq = W.host_bits(inp["draft_q"])
+        t0 = time.perf_counter()
+        _, sc = oracle.verify_attn(q, k, v, cus, wl.gamma, wl.scale)
+        idx, _, _ = oracle.select_topk(sc, cus, wl.gamma, cuk)
+        for j in range(wl.n_drafts):
+            oracle.sparse_decode_attn(dq[j], k, v, cus, idx, cuk, wl.scale)
+        spent += time.perf_counter() - t0
+        done += 1
+        del q, k, v, dq, sc
+        if spent >= min_seconds:
+            break
     omp = os.environ.get("OMP_NUM_THREADS")
     threads = int(omp) if omp and omp.isdigit() else len(os.sched_getaffinity(0))
-    tasks = nseq * wl.num_kv_heads
+    tasks = wl.batch * wl.num_kv_heads
     return {
-        "value": round(dt * 1e6 * wl.batch / nseq, 1),
+        "value": round(spent * 1e6 / done, 1),
         "unit": "us/layer-step",
         "cores": min(threads, tasks),
         "kind": "oracle",
-        "sample": (f"sequences 0..{nseq - 1} of {wl.batch} of layer 0 (verify + select + {wl.n_drafts} drafts), "
-                   f"{dt:.2f} s, scaled x{wl.batch / nseq:g} to one layer-step"),
+        "sample": (f"layers 0..{done - 1} of {len(layer_inputs)}, all {wl.batch} sequences "
+                   f"(verify + select + {wl.n_drafts} drafts each), {spent:.2f} s in total, "
+                   f"divided by {done} layer-steps"),
     }
+
+
+def copy_calibration(nbytes):
+    """A plain device-to-device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": nbytes, "copy_calibration_bytes_written": nbytes,
+                      "launches": 3}), flush=True)
 
 
 def main():
@@ -119,13 +135,19 @@ def main():
     ap.add_argument("--workload", type=int, default=2, help="0-based workload index (default: 128K Qwen3-8B step)")
     ap.add_argument("--layers", type=int, default=None, help="override the layer count (profiling runs only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seqs", type=int, default=2)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a device copy of BYTES bytes three times (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import torch
     from verification_guided_sparse_verify_amd import workloads as W
@@ -257,7 +279,7 @@ def main():
     result["collect_select_overhead_vs_plain_verify"] = round((mean["verify"] + mean["select"]) / plain_us - 1, 4)
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, layer_inputs, steps, min(args.cpu_seqs, wl.batch))
+        result["cpu_baseline"] = cpu_baseline(wl, layer_inputs, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
