@@ -9,9 +9,12 @@ every layer.  The reported value is microseconds per layer-step
 (verify + select + gamma drafts of one layer) = step time / layers.
 
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
-Per-call HIP events on the launch stream give each kernel's time inside the
-timed region; the HBM roofline uses algorithmic bytes (each KV byte of the
-verified cache read once, the selected rows gathered once per draft).
+Inside the timed region HIP events on the launch stream bracket every
+verification call (the dominant kernel); its average duration and the
+algorithmic bytes of one call (each KV byte of the verified cache read once,
+Q and O, the collected scores written once) give the HBM roofline figure.
+The per-call breakdown of select and drafting comes from two further steps
+with events around every call, after the timed region.
 """
 from __future__ import annotations
 
@@ -176,52 +179,68 @@ def main():
     print(f"# generated {layers} layers in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
-    ev_sets = []
+    bound = [st.bind(stream) for st in steps]     # ctypes arguments converted once
 
-    def one_step(record):
-        evs = {"verify": [], "select": [], "draft": []} if record else None
+    def one_step(verify_events=None, call_events=None):
+        """One speculative iteration: verify + select on every layer, then gamma drafting
+        passes over every layer.  verify_events: list receiving an event pair around every
+        verify call; call_events: dict receiving event pairs around every call."""
+        def timed(kind, fn, sink):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            sink[kind].append((a, b))
 
-        def timed(kind, fn):
-            if record:
+        for verify, _, select, _ in bound:
+            if call_events is not None:
+                timed("verify", verify, call_events)
+                timed("select", select, call_events)
+                continue
+            if verify_events is not None:
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
                 a.record(stream)
-                fn()
+                verify()
                 b.record(stream)
-                evs[kind].append((a, b))
+                verify_events.append((a, b))
             else:
-                fn()
-
-        for st in steps:
-            timed("verify", lambda: st.verify(True))
-            timed("select", st.select)
+                verify()
+            select()
         for j in range(wl.n_drafts):
-            for st in steps:
-                timed("draft", lambda: st.draft(j))
-        if record:
-            ev_sets.append(evs)
+            for _, _, _, drafts in bound:
+                if call_events is not None:
+                    timed("draft", drafts[j], call_events)
+                else:
+                    drafts[j]()
 
     for _ in range(args.warmup):
-        one_step(False)
+        one_step()
     torch.cuda.synchronize()
+    verify_pairs = []
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        one_step(True)
+        one_step(verify_events=verify_pairs)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    per = {"verify": [], "select": [], "draft": []}
-    for evs in ev_sets:
-        for kind, pairs in evs.items():
-            per[kind].extend(a.elapsed_time(b) * 1e3 for a, b in pairs)   # microseconds
+    # Per-call breakdown, outside the timed region: two more steps with events around every call.
+    call_pairs = {"verify": [], "select": [], "draft": []}
+    for _ in range(2):
+        one_step(call_events=call_pairs)
+    torch.cuda.synchronize()
+    per = {k: [a.elapsed_time(b) * 1e3 for a, b in v] for k, v in call_pairs.items()}   # microseconds
     mean = {k: statistics.fmean(v) for k, v in per.items()}
     med = {k: statistics.median(v) for k, v in per.items()}
+    verify_us = [a.elapsed_time(b) * 1e3 for a, b in verify_pairs]
+    verify_mean = statistics.fmean(verify_us)
 
     ms_per_step = elapsed * 1e3 / args.steps
     us_layer_step = ms_per_step * 1e3 / layers
     ab = algorithmic_bytes(wl)
     step_gbps = ab["layer_step"] / (us_layer_step * 1e-6) / 1e9
-    verify_gbps = ab["verify"] / (mean["verify"] * 1e-6) / 1e9
+    verify_gbps = ab["verify"] / (verify_mean * 1e-6) / 1e9
     traffic = read_traffic("attn_split_verify_qwen3_8b_128k_pmc.txt", "hbm_bytes_per_launch")
 
     result = {
@@ -259,24 +278,25 @@ def main():
             "frac": round(verify_gbps / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": ab["verify"],
-            "avg_launch_us": round(mean["verify"], 2),
+            "avg_launch_us": round(verify_mean, 2),
+            "launches_timed": len(verify_us),
         },
     }
 
     # Plain verification (collection off) on the same layers, for the collection + select overhead.
     plain = []
     for _ in range(3):
-        for st in steps:
+        for _, verify_plain, _, _ in bound:
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            st.verify(False)
+            verify_plain()
             b.record(stream)
             plain.append((a, b))
     torch.cuda.synchronize()
     plain_us = statistics.fmean(a.elapsed_time(b) * 1e3 for a, b in plain)
     result["plain_verify_us"] = round(plain_us, 2)
-    result["collect_select_overhead_vs_plain_verify"] = round((mean["verify"] + mean["select"]) / plain_us - 1, 4)
+    result["collect_select_overhead_vs_plain_verify"] = round((verify_mean + mean["select"]) / plain_us - 1, 4)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, layer_inputs, args.cpu_seconds)

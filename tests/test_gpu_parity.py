@@ -165,3 +165,41 @@ def test_qwen3_8b_128k_layer_sampled():
     inp, st = run_layer(wl, seed=0, layer=7)
     worst = check_layer(wl, inp, st, seqs=[2])
     log(f"  worst {worst}")
+
+
+SELECT_CASES = [
+    # KV heads, gamma, prefix lengths, k per sequence, integer score range (ties)
+    (2, 3, [5000, 70000, 1], [250, 3500, 1], 3),
+    (8, 5, [131072, 40000], [6553, 40000], 2),
+    (1, 0, [2049, 2047, 4096], [1, 2047, 0], 1),
+    (4, 1, [300000], [15000], 0),
+]
+
+
+@pytest.mark.parametrize("case", SELECT_CASES, ids=lambda c: f"H{c[0]}-g{c[1]}-L{c[2]}-k{c[3]}-r{c[4]}")
+def test_select_exact_on_tied_integer_scores(case):
+    """Integer-valued scores sum exactly in fp32 and fp64, so the selected lists must
+    equal the oracle's bit for bit, ties going to the lower position."""
+    hkv, gamma, prefixes, ks, rng_r = case
+    log(f"case: select hkv={hkv} gamma={gamma} L={prefixes} k={ks} range={rng_r}")
+    W_ = gamma + 1
+    lens = [L + W_ for L in prefixes]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cuk = np.concatenate([[0], np.cumsum(ks)]).astype(np.int32)
+    total = int(cu[-1])
+    g = torch.Generator(device="cpu")
+    g.manual_seed(7)
+    if rng_r == 0:
+        sc = torch.zeros(hkv, total, dtype=torch.float32)
+    else:
+        sc = torch.randint(-rng_r, rng_r + 1, (hkv, total), generator=g).to(torch.float32)
+    idx_ref, _, _ = oracle.select_topk(sc.numpy().astype(np.float64), cu, gamma, cuk)
+    dev = sc.cuda()
+    out = torch.full((max(int(cuk[-1]), 1),), -1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(V.vegas_select_workspace_size(len(prefixes), hkv, gamma, max(lens), total),
+                     dtype=torch.uint8, device="cuda")
+    V.vegas_select_topk(len(prefixes), hkv, gamma, dev, torch.from_numpy(cu).cuda(), max(lens), total,
+                        torch.from_numpy(cuk).cuda(), out, ws)
+    torch.cuda.synchronize()
+    got = out[: int(cuk[-1])].cpu().numpy()
+    assert np.array_equal(got, idx_ref)

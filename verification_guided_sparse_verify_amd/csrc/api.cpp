@@ -28,8 +28,11 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Workgroups the split kernel should expose: a few per CU on a 256-CU part.
-constexpr int kTargetWorkgroups = 1024;
+// Workgroups the split kernel should expose on a 256-CU part (the kernel
+// holds one workgroup per CU): a few rounds for verification, whose splits
+// are long, and a single round for the short gathered lists of drafting.
+constexpr int kVerifyWorkgroups = 1024;
+constexpr int kGatherWorkgroups = 256;
 
 struct AttnPlan {
     int mb = 0;          // 16-row query tiles per KV head
@@ -46,13 +49,17 @@ AttnPlan plan_attn(int batch, int hkv, int M, int head_dim, int max_n, bool gath
     const int unit = vegas::kAttnWaves * vegas::kAttnBlock;
     const int n = max_n > 0 ? max_n : 1;
     const int units = batch * hkv;
-    int want = (kTargetWorkgroups + units - 1) / units;
+    const int target = gather ? kGatherWorkgroups : kVerifyWorkgroups;
+    int want = (target + units - 1) / units;
     const int most = (n + unit - 1) / unit;
     if (want > most) want = most;
     if (want < 1) want = 1;
     int chunk = (n + want - 1) / want;
     chunk = (chunk + unit - 1) / unit * unit;
-    if (gather && chunk > vegas::kMaxGatherChunk) chunk = vegas::kMaxGatherChunk;
+    // Both caps are multiples of `unit`.  Verification uses the same plan with
+    // and without collection, so the two give bit-identical outputs.
+    const int cap = gather ? vegas::kMaxGatherChunk : vegas::kMaxCollectChunk;
+    if (chunk > cap) chunk = cap;
     p.chunk = chunk;
     p.nsplit = (n + chunk - 1) / chunk;
     const size_t slots = (size_t)batch * hkv * p.nsplit;
@@ -106,17 +113,22 @@ vegas_status_t hip_status(hipError_t e, const char* what) {
 
 struct SelectPlan {
     int nchunks = 0;
-    size_t keys = 0, tpos = 0, tkey = 0, hist = 0;
-    size_t total() const { return align_up(keys) + align_up(tpos) + align_up(tkey) + align_up(hist); }
+    size_t keys = 0, cand_key = 0, cand_pos = 0, zeroed = 0, seq_info = 0, chunk = 0;
+    size_t total() const {
+        return align_up(keys) + align_up(cand_key) + align_up(cand_pos) + align_up(zeroed) +
+               align_up(seq_info) + 3 * align_up(chunk);
+    }
 };
 
 SelectPlan plan_select(int batch, int max_seqlen_k, int total_kv) {
     SelectPlan p;
     p.nchunks = (max_seqlen_k + vegas::kSelChunk - 1) / vegas::kSelChunk;
     p.keys = (size_t)total_kv * sizeof(uint32_t);
-    p.tpos = (size_t)total_kv * sizeof(int32_t);
-    p.tkey = (size_t)total_kv * sizeof(uint32_t);
-    p.hist = (size_t)batch * vegas::kSelBins * sizeof(uint32_t);
+    p.cand_key = (size_t)total_kv * sizeof(uint32_t);
+    p.cand_pos = (size_t)total_kv * sizeof(int32_t);
+    p.zeroed = ((size_t)batch * vegas::kSelBins + batch) * sizeof(uint32_t);
+    p.seq_info = (size_t)batch * 4 * sizeof(uint32_t);
+    p.chunk = (size_t)batch * p.nchunks * sizeof(uint32_t);
     return p;
 }
 
@@ -217,6 +229,9 @@ vegas_status_t vegas_select_workspace_size(int32_t batch, int32_t num_kv_heads, 
     if (gamma < 0 || gamma > 31) return fail(VEGAS_ERR_INVALID_ARGUMENT, "gamma %d outside 0..31", gamma);
     if (max_seqlen_k < gamma + 1 || total_kv < 1)
         return fail(VEGAS_ERR_INVALID_ARGUMENT, "max_seqlen_k must be >= gamma+1 and total_kv >= 1");
+    if ((int64_t)max_seqlen_k > (int64_t)vegas::kSelMaxChunks * vegas::kSelChunk)
+        return fail(VEGAS_ERR_UNSUPPORTED, "max_seqlen_k %d exceeds %d", max_seqlen_k,
+                    vegas::kSelMaxChunks * vegas::kSelChunk);
     if (!bytes) return fail(VEGAS_ERR_INVALID_ARGUMENT, "bytes is NULL");
     *bytes = plan_select(batch, max_seqlen_k, total_kv).total();
     return VEGAS_OK;
@@ -237,18 +252,24 @@ vegas_status_t vegas_select_topk(int32_t batch, int32_t num_kv_heads, int32_t ga
     if (!workspace) return fail(VEGAS_ERR_INVALID_ARGUMENT, "workspace is NULL");
     const SelectPlan plan = plan_select(batch, max_seqlen_k, total_kv);
     char* ws = static_cast<char*>(workspace);
+    auto take = [&ws](size_t n) {
+        char* p = ws;
+        ws += align_up(n);
+        return p;
+    };
     vegas::SelectArgs a{};
     a.scores = scores;
     a.cu_seqlens_k = cu_seqlens_k;
     a.cu_k = cu_k;
     a.indices = indices;
-    a.keys = reinterpret_cast<uint32_t*>(ws);
-    ws += align_up(plan.keys);
-    a.tmp_pos = reinterpret_cast<int32_t*>(ws);
-    ws += align_up(plan.tpos);
-    a.tmp_key = reinterpret_cast<uint32_t*>(ws);
-    ws += align_up(plan.tkey);
-    a.hist = reinterpret_cast<uint32_t*>(ws);
+    a.keys = reinterpret_cast<uint32_t*>(take(plan.keys));
+    a.cand_key = reinterpret_cast<uint32_t*>(take(plan.cand_key));
+    a.cand_pos = reinterpret_cast<int32_t*>(take(plan.cand_pos));
+    a.zeroed = reinterpret_cast<uint32_t*>(take(plan.zeroed));
+    a.seq_info = reinterpret_cast<uint32_t*>(take(plan.seq_info));
+    a.chunk_above = reinterpret_cast<uint32_t*>(take(plan.chunk));
+    a.chunk_off = reinterpret_cast<uint32_t*>(take(plan.chunk));
+    a.chunk_ties = reinterpret_cast<uint32_t*>(take(plan.chunk));
     a.batch = batch;
     a.hkv = num_kv_heads;
     a.W = gamma + 1;

@@ -248,7 +248,8 @@ __device__ __forceinline__ f32x4_t mfma_pv(const uint32_t (&vt)[4], const float 
 // One 16-position block: S^T, collection, mask, online softmax, O^T += V^T P^T.
 template <class GEO, bool BF16, int D, int MB, bool GATHER, bool COLLECT>
 __device__ __forceinline__ void compute_block(const AttnArgs& a, WaveState<BF16, D, MB>& ws, int p0, int L,
-                                              int end, int seq0, int g, int lane, const unsigned char* stage) {
+                                              int end, int start, int lane, const unsigned char* stage,
+                                              float* score_s) {
     constexpr int DC = D / 32, DB = D / 16, EPC = GEO::EPC;
     const int lr = lane & 15, lg = lane >> 4;
     const unsigned char* kt = stage;
@@ -291,8 +292,7 @@ __device__ __forceinline__ void compute_block(const AttnArgs& a, WaveState<BF16,
                 val = (lr == 1) ? red[1] : val;
                 val = (lr == 2) ? red[2] : val;
                 val = (lr == 3) ? red[3] : val;
-                const int pos = p0 + 4 * lg + lr;
-                if (pos < L && pos < end) a.scores[(size_t)g * a.total_kv + seq0 + pos] = a.scale * val;
+                score_s[p0 - start + 4 * lg + lr] = a.scale * val;
             }
         }
     }
@@ -368,6 +368,8 @@ attn_split_kernel(const AttnArgs a) {
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[GEO::MAIN];
     __shared__ int idx_s[GATHER ? kMaxGatherChunk : 1];
+    // Collected scores of this split, written to HBM once the split is done.
+    __shared__ float score_s[COLLECT ? kMaxCollectChunk : 1];
 
     const int lane = threadIdx.x & 63;
     // wave index as a scalar: every branch on it is uniform
@@ -453,8 +455,8 @@ attn_split_kernel(const AttnArgs a) {
         for (int jj = 0; jj < nmine; ++jj) {
             wait_vmem<(NST - 2) * GEO::BLOCK_OPS>();      // block jj has landed
             issue_block<GEO, GATHER>(c, block_pos(jj + NST - 1), lane, ring + ((jj + NST - 1) % NST) * GEO::STAGE);
-            compute_block<GEO, BF16, D, MB, GATHER, COLLECT>(a, ws, block_pos(jj), L, end, seq0, g, lane,
-                                                              ring + (jj % NST) * GEO::STAGE);
+            compute_block<GEO, BF16, D, MB, GATHER, COLLECT>(a, ws, block_pos(jj), L, end, start, lane,
+                                                              ring + (jj % NST) * GEO::STAGE, score_s);
         }
         wait_vmem<0>();
     }
@@ -468,6 +470,12 @@ attn_split_kernel(const AttnArgs a) {
 
     // Tree merge of the waves' (m, l, O) through LDS, in fragment order.
     __syncthreads();
+    if constexpr (COLLECT) {
+        // Coalesced write of the split's collected scores (prefix positions only).
+        float* dst = a.scores + (size_t)g * a.total_kv + seq0 + start;
+        const int nsc = min(end, L) - start;
+        for (int i = threadIdx.x; i < nsc; i += blockDim.x) dst[i] = score_s[i];
+    }
     float* fs = reinterpret_cast<float*>(smem);
     constexpr int SLOTF = GEO::MSLOT / 4;
 #pragma unroll
@@ -528,14 +536,19 @@ attn_split_kernel(const AttnArgs a) {
 }
 
 // Merge the split partials of one (sequence, KV head, 16-row tile, 16-wide d
-// tile) and write the normalised output in the storage dtype.  One wave; each
-// lane owns one float4 of the fragment layout; eight splits' loads are in
-// flight at a time.
+// tile) and write the normalised output in the storage dtype.  Each lane of
+// a wave owns one float4 of the fragment layout; the four waves take the
+// splits in turn (four loads in flight each) and their partial merges are
+// combined through LDS in a fixed order.
+constexpr int kCombineWaves = 4;
+
 template <bool BF16, int D, int MB, bool GATHER>
-__global__ void __launch_bounds__(64) attn_combine_kernel(const AttnArgs a) {
+__global__ void __launch_bounds__(kCombineWaves * 64) attn_combine_kernel(const AttnArgs a) {
     constexpr int DB = D / 16;
     constexpr int NREG = DB * MB;
-    constexpr int U = 8;
+    constexpr int U = 4;
+    __shared__ f32x4_t acc_s[kCombineWaves - 1][64];
+    __shared__ float2 md_s[kCombineWaves - 1][64];
     int wg = blockIdx.x;
     const int db = wg % DB;
     wg /= DB;
@@ -543,7 +556,8 @@ __global__ void __launch_bounds__(64) attn_combine_kernel(const AttnArgs a) {
     wg /= MB;
     const int g = wg % a.hkv;
     const int b = wg / a.hkv;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
     const int lr = lane & 15;
     const int lg = lane >> 4;
     const int j = 16 * qb + lr;
@@ -559,18 +573,18 @@ __global__ void __launch_bounds__(64) attn_combine_kernel(const AttnArgs a) {
     const size_t slot0 = ((size_t)b * a.hkv + g) * a.nsplit;
     const float2* pml = reinterpret_cast<const float2*>(a.part_ml);
     const f32x4_t* po = reinterpret_cast<const f32x4_t*>(a.part_o);
-    for (int s0 = 0; s0 < nsv; s0 += U) {
+    for (int s0 = wave; s0 < nsv; s0 += U * kCombineWaves) {
         float2 ml[U];
         f32x4_t ov[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int s = min(s0 + u, nsv - 1);
+            const int s = min(s0 + u * kCombineWaves, nsv - 1);
             ml[u] = pml[(slot0 + s) * (MB * 16) + j];
             ov[u] = po[(slot0 + s) * (NREG * 64) + (db * MB + qb) * 64 + lane];
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (s0 + u >= nsv || ml[u].x == kNegInf) continue;
+            if (s0 + u * kCombineWaves >= nsv || ml[u].x == kNegInf) continue;
             if (ml[u].x > mr) {
                 const float cf = fast_exp2(mr - ml[u].x);
                 acc *= cf;
@@ -581,6 +595,24 @@ __global__ void __launch_bounds__(64) attn_combine_kernel(const AttnArgs a) {
             acc += w * ov[u];
             den += w * ml[u].y;
         }
+    }
+    if (wave > 0) {
+        acc_s[wave - 1][lane] = acc;
+        md_s[wave - 1][lane] = make_float2(mr, den);
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < kCombineWaves - 1; ++w) {
+        const float2 md = md_s[w][lane];
+        if (md.x == kNegInf) continue;
+        const f32x4_t ob = acc_s[w][lane];
+        const float mm = fmaxf(mr, md.x);
+        const float ca = fast_exp2(mr - mm);
+        const float cb = fast_exp2(md.x - mm);
+        acc = ca * acc + cb * ob;
+        den = ca * den + cb * md.y;
+        mr = mm;
     }
     if (j >= a.M) return;
     const float inv = den > 0.f ? 1.f / den : 0.f;
@@ -610,7 +642,8 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL((attn_split_kernel<BF16, D, MB, GATHER, COLLECT>), dim3(split_grid),
                            dim3(kAttnWaves * 64), 0, stream, a);
     if (comb_grid > 0)
-        hipLaunchKernelGGL((attn_combine_kernel<BF16, D, MB, GATHER>), dim3(comb_grid), dim3(64), 0, stream, a);
+        hipLaunchKernelGGL((attn_combine_kernel<BF16, D, MB, GATHER>), dim3(comb_grid), dim3(kCombineWaves * 64), 0,
+                           stream, a);
     return hipGetLastError();
 }
 

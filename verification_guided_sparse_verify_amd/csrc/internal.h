@@ -14,6 +14,9 @@ constexpr int kAttnBlock = 16;
 // Longest position range one workgroup takes in gather mode: its index list
 // is staged in LDS.
 constexpr int kMaxGatherChunk = 2048;
+// Longest position range one workgroup takes in verification with
+// collection: its collected scores are buffered in LDS.
+constexpr int kMaxCollectChunk = 4352;
 
 // Arguments of the split attention kernel and of its combine kernel.
 // One kernel serves both the verification pass (contiguous positions, causal
@@ -46,17 +49,25 @@ struct SelectArgs {
     const int32_t* cu_seqlens_k;   // [batch+1]
     const int32_t* cu_k;           // [batch+1]
     int32_t* indices;              // [cu_k[batch]]
-    uint32_t* keys;                // [total_kv]
-    uint32_t* hist;                // [batch][kSelBins]
-    int32_t* tmp_pos;              // [total_kv]
-    uint32_t* tmp_key;             // [total_kv]
+    uint32_t* keys;                // [total_kv] order-preserving image of S
+    uint32_t* cand_key;            // [total_kv] threshold-bin candidates, per sequence at its offset
+    int32_t* cand_pos;             // [total_kv]
+    uint32_t* zeroed;              // [batch*kSelBins + batch]: histograms, then candidate counts
+    uint32_t* seq_info;            // [batch][4]: top digit d1, count above d1, theta key
+    uint32_t* chunk_above;         // [batch][nchunks]: positions above the threshold bin
+    uint32_t* chunk_off;           // [batch][nchunks]: first output slot of the chunk
+    uint32_t* chunk_ties;          // [batch][nchunks]: keys equal to theta the chunk contributes
     int32_t batch, hkv, W, total_kv;
-    int32_t nchunks;               // pass-1 workgroups per sequence
+    int32_t nchunks;               // chunks per sequence
 };
 
 constexpr int kSelDigitBits = 12;
 constexpr int kSelBins = 1 << kSelDigitBits;
-constexpr int kSelChunk = 8192;    // positions per pass-1 workgroup
+constexpr int kSelThreads = 256;
+constexpr int kSelPer = 8;                        // positions per thread per chunk
+constexpr int kSelChunk = kSelThreads * kSelPer;  // positions per chunk workgroup
+constexpr int kSelChunkShift = 11;
+constexpr int kSelMaxChunks = 4096;               // longest prefix: kSelMaxChunks * kSelChunk
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 

@@ -1,33 +1,33 @@
 // Exact top-k KV selection for gfx950.
 //
-// The selected set (gist.science summary of Vegas, sec. 2A) is the k prefix
-// positions with the largest score summed over collected rows and query
-// heads.  The verification kernel leaves one fp32 sum per (KV head, position);
-// here S[i] = sum over KV heads, then an exact radix select on the
-// order-preserving 32-bit image of S:
+// The selected set (gist.science "Technical Summary" of Vegas, sec. 2A
+// "Formulation") is the size-k subset of the prefix maximising the collected
+// logits summed over rows and query heads; for a sum of per-position terms it
+// is the k positions with the largest per-position sum.  The verification
+// kernel leaves one fp32 sum per (KV head, position); here
+// S[i] = sum over KV heads, then an exact radix select on the
+// order-preserving 32-bit image ("key") of S.
 //
-//   pass 1 (many workgroups per sequence): S, its key, a 12-bit histogram of
-//           the top digit in LDS, merged into a per-sequence global histogram;
-//   pass 2 (one workgroup per sequence):
-//     a. from the histogram: the top digit d1 that holds the k-th largest key;
-//     b. ordered compaction of every position whose top digit is >= d1 (a
-//        superset of T, about k plus one histogram bin) into a scratch list,
-//        in ascending position order;
-//     c. two 10-bit refinement histograms over that list give the exact k-th
-//        largest key theta and how many positions equal to theta to take;
-//     d. ordered compaction of the list: key > theta, or key == theta among
-//        the first ones in position order -> ascending T.
-// Ordered compaction uses wave ballots and lane-prefix popcounts; workgroup
-// offsets go through LDS with one barrier per 8192 positions.
+// Four launches, the last three spread over one workgroup per 2048-position
+// chunk so that a long sequence is never left to a handful of compute units.
+// Workgroups exchange results only across launch boundaries (on a multi-die
+// part an in-kernel hand-off would need an L2 write-back per workgroup).
+//   zero      clear the per-sequence histograms and candidate counters;
+//   keys      S, its key, a 12-bit top-digit histogram (LDS, merged into the
+//             per-sequence histogram with global atomics);
+//   cand      every chunk finds the top digit d1 holding the k-th largest
+//             key, counts its keys above d1 and appends the keys in bin d1
+//             (the only undecided ones, typically ~1% of the prefix) to a
+//             per-sequence candidate list;
+//   write     every chunk recomputes, from the candidates, the exact k-th
+//             largest key theta (two 10-bit refinement histograms), how many
+//             keys equal to theta are taken (lowest positions first), and
+//             the output offset and tie share of each chunk before it; then
+//             writes its selected positions in ascending order at its offset.
 #include "internal.h"
 
 namespace vegas {
 namespace {
-
-constexpr int kFinishThreads = 1024;
-constexpr int kFinishWaves = kFinishThreads / 64;
-constexpr int kPer = 8;                       // consecutive items per thread per round
-constexpr int kRound = kFinishThreads * kPer;
 
 __device__ __forceinline__ uint32_t order_key(float f) {
     f = f + 0.0f;                             // -0 and +0 share one key
@@ -35,36 +35,31 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Clamped geometry of sequence b: first row, candidate count L (prefix), k
+// and the first output slot.
+struct SeqGeo {
+    int seq0, L, k, kout;
+};
+__device__ __forceinline__ SeqGeo seq_geo(const SelectArgs& a, int b) {
+    SeqGeo s;
+    s.seq0 = min(max(a.cu_seqlens_k[b], 0), a.total_kv);
+    const int end = min(max(a.cu_seqlens_k[b + 1], s.seq0), a.total_kv);
+    s.L = max(end - s.seq0 - a.W, 0);
+    s.L = min(s.L, a.nchunks * kSelChunk);
+    const int kend = max(a.cu_k[a.batch], 0);
+    s.kout = min(max(a.cu_k[b], 0), kend);
+    s.k = min(min(max(a.cu_k[b + 1] - s.kout, 0), s.L), kend - s.kout);
+    return s;
+}
+
 __global__ void sel_zero_kernel(uint32_t* __restrict__ p, int n) {
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
 }
 
-__global__ void __launch_bounds__(256) sel_keys_kernel(const SelectArgs a) {
-    __shared__ uint32_t h[kSelBins];
-    const int b = blockIdx.y;
-    const int seq0 = a.cu_seqlens_k[b];
-    const int L = a.cu_seqlens_k[b + 1] - seq0 - a.W;
-    const int start = blockIdx.x * kSelChunk;
-    if (start >= L) return;
-    const int end = min(start + kSelChunk, L);
-    for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) h[i] = 0u;
-    __syncthreads();
-    for (int p = start + threadIdx.x; p < end; p += blockDim.x) {
-        const size_t col = (size_t)seq0 + p;
-        float s = 0.f;
-        for (int g = 0; g < a.hkv; ++g) s += a.scores[(size_t)g * a.total_kv + col];
-        const uint32_t key = order_key(s);
-        a.keys[col] = key;
-        atomicAdd(&h[key >> (32 - kSelDigitBits)], 1u);
-    }
-    __syncthreads();
-    uint32_t* gh = a.hist + (size_t)b * kSelBins;
-    for (int i = threadIdx.x; i < kSelBins; i += blockDim.x)
-        if (h[i]) atomicAdd(&gh[i], h[i]);
-}
-
-// Exclusive prefix sum over the workgroup's threads in thread order.
+// Exclusive prefix sum of x over the workgroup's threads, in thread order;
+// *total receives the sum.  wsum: kSelThreads/64 ints of LDS.
 __device__ __forceinline__ int wg_exclusive_scan(int x, int* wsum, int* total) {
+    constexpr int NW = kSelThreads / 64;
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     int v = x;
@@ -76,7 +71,8 @@ __device__ __forceinline__ int wg_exclusive_scan(int x, int* wsum, int* total) {
     if (lane == 63) wsum[w] = v;
     __syncthreads();
     int before = 0, all = 0;
-    for (int i = 0; i < kFinishWaves; ++i) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
         const int t = wsum[i];
         before += (i < w) ? t : 0;
         all += t;
@@ -86,171 +82,259 @@ __device__ __forceinline__ int wg_exclusive_scan(int x, int* wsum, int* total) {
     return before + v - x;
 }
 
-// Position of every true predicate among all true predicates of the round,
-// items ordered by (thread, item).  Returns the round's total.
-__device__ __forceinline__ int round_offsets(const bool (&pred)[kPer], int (&off)[kPer], int* wsum) {
-    const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int lower_lanes = 0, wave_total = 0, mine = 0;
+// Ordered compaction offsets: items are ordered by (thread, e); off[e] is the
+// number of true predicates before item e.  Returns the total.
+template <int PER>
+__device__ __forceinline__ int ordered_offsets(const bool (&pred)[PER], int (&off)[PER], int* wsum) {
+    int mine = 0;
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-        const uint64_t bal = __ballot(pred[e]);
-        lower_lanes += __popcll(bal & below);
-        wave_total += __popcll(bal);
-    }
-    if (lane == 0) wsum[w] = wave_total;
-    __syncthreads();
-    int before = 0, all = 0;
-    for (int i = 0; i < kFinishWaves; ++i) {
-        const int t = wsum[i];
-        before += (i < w) ? t : 0;
-        all += t;
-    }
+    for (int e = 0; e < PER; ++e) mine += pred[e] ? 1 : 0;
+    int total;
+    int base = wg_exclusive_scan(mine, wsum, &total);
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-        off[e] = before + lower_lanes + mine;
-        mine += pred[e] ? 1 : 0;
+    for (int e = 0; e < PER; ++e) {
+        off[e] = base;
+        base += pred[e] ? 1 : 0;
     }
-    return all;
+    return total;
 }
 
-// Over `nbins` LDS bins taken from the top, find the bin holding the
-// `need`-th largest item; returns the bin and the count strictly above it.
-__device__ __forceinline__ void find_crossing(const uint32_t* bins, int nbins, int need, int* wsum,
-                                              uint32_t* bc) {
-    const int per = nbins / kFinishThreads;   // bins per thread, taken in descending order
-    const int top = nbins - 1 - per * (int)threadIdx.x;
+// Over NBINS LDS bins taken from the top, find the bin holding the
+// `need`-th largest item (1 <= need <= sum of bins): out[0] = bin,
+// out[1] = count of items in bins strictly above it.
+template <int NBINS>
+__device__ __forceinline__ void find_crossing(const uint32_t* bins, int need, int* wsum, uint32_t* out) {
+    constexpr int PER = NBINS / kSelThreads;  // bins per thread, taken in descending order
+    const int top = NBINS - 1 - PER * (int)threadIdx.x;
+    uint32_t h[PER];
     int local = 0;
-    for (int q = 0; q < per; ++q) local += (int)bins[top - q];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        h[q] = bins[top - q];
+        local += (int)h[q];
+    }
     int total;
     int c = wg_exclusive_scan(local, wsum, &total);
-    for (int q = 0; q < per; ++q) {
-        const int hcount = (int)bins[top - q];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int hcount = (int)h[q];
         if (c < need && c + hcount >= need) {
-            bc[0] = (uint32_t)(top - q);
-            bc[1] = (uint32_t)c;
+            out[0] = (uint32_t)(top - q);
+            out[1] = (uint32_t)c;
         }
         c += hcount;
     }
     __syncthreads();
 }
 
-__global__ void __launch_bounds__(kFinishThreads) sel_finish_kernel(const SelectArgs a) {
-    __shared__ uint32_t bins[kSelBins];
-    __shared__ int wsum[2][kFinishWaves];
-    __shared__ uint32_t bc[2];
+__global__ void __launch_bounds__(kSelThreads) sel_keys_kernel(const SelectArgs a) {
+    __shared__ uint32_t h[kSelBins];
+    const int b = blockIdx.y;
+    const SeqGeo sg = seq_geo(a, b);
+    const int start = blockIdx.x * kSelChunk;
+    if (start >= sg.L) return;                         // uniform per workgroup
+    for (int i = threadIdx.x; i < kSelBins; i += kSelThreads) h[i] = 0u;
 
-    const int b = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int seq0 = a.cu_seqlens_k[b];
-    const int L = a.cu_seqlens_k[b + 1] - seq0 - a.W;
-    const int kout = a.cu_k[b];
-    const int k = min(a.cu_k[b + 1] - kout, L);
-    if (k <= 0) return;
-    int32_t* out = a.indices + kout;
-
-    // a. top digit holding the k-th largest key.
-    for (int i = tid; i < kSelBins; i += kFinishThreads) bins[i] = a.hist[(size_t)b * kSelBins + i];
-    __syncthreads();
-    find_crossing(bins, kSelBins, k, wsum[0], bc);
-    const uint32_t d1 = bc[0];
-    int above = (int)bc[1];
-
-    // b. ordered compaction of positions whose top digit is >= d1.
-    const uint32_t* keys = a.keys + seq0;
-    int32_t* tpos = a.tmp_pos + seq0;
-    uint32_t* tkey = a.tmp_key + seq0;
-    int nsup = 0;
-    int parity = 0;
-    for (int base = 0; base < L; base += kRound) {
-        const int p = base + kPer * tid;
-        uint32_t kk[kPer];
-        bool pred[kPer];
+    float s[kSelPer];
+    bool in[kSelPer];
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) {
-            const bool in = (p + e) < L;
-            kk[e] = in ? keys[p + e] : 0u;
-            pred[e] = in && ((kk[e] >> (32 - kSelDigitBits)) >= d1);
-        }
-        int off[kPer];
-        const int tot = round_offsets(pred, off, wsum[parity]);
-#pragma unroll
-        for (int e = 0; e < kPer; ++e)
-            if (pred[e]) {
-                tpos[nsup + off[e]] = p + e;
-                tkey[nsup + off[e]] = kk[e];
-            }
-        nsup += tot;
-        parity ^= 1;
+    for (int e = 0; e < kSelPer; ++e) {
+        in[e] = start + e * kSelThreads + (int)threadIdx.x < sg.L;
+        s[e] = 0.f;
     }
-    __syncthreads();   // scratch list complete and visible to the whole workgroup
+    const float* col = a.scores + sg.seq0 + start + threadIdx.x;
+    // S = sum over KV heads 0, 1, ... in this order; eight heads' loads in flight.
+    for (int g0 = 0; g0 < a.hkv; g0 += 8) {
+        float x[8][kSelPer];
+#pragma unroll
+        for (int gi = 0; gi < 8; ++gi) {
+            const float* row = col + (size_t)(g0 + gi) * a.total_kv;
+#pragma unroll
+            for (int e = 0; e < kSelPer; ++e) x[gi][e] = (in[e] && g0 + gi < a.hkv) ? row[e * kSelThreads] : 0.f;
+        }
+#pragma unroll
+        for (int gi = 0; gi < 8; ++gi)
+#pragma unroll
+            for (int e = 0; e < kSelPer; ++e)
+                if (g0 + gi < a.hkv) s[e] += x[gi][e];
+    }
+    __syncthreads();                                   // histogram cleared
+    uint32_t* keys = a.keys + sg.seq0 + start + threadIdx.x;
+#pragma unroll
+    for (int e = 0; e < kSelPer; ++e) {
+        if (!in[e]) continue;
+        const uint32_t key = order_key(s[e]);
+        keys[e * kSelThreads] = key;
+        atomicAdd(&h[key >> (32 - kSelDigitBits)], 1u);
+    }
+    __syncthreads();
+    uint32_t* gh = a.zeroed + (size_t)b * kSelBins;
+    for (int i = threadIdx.x; i < kSelBins; i += kSelThreads)
+        if (h[i]) atomicAdd(&gh[i], h[i]);
+}
 
-    // c. refine: two 10-bit digits below the top digit.
+__global__ void __launch_bounds__(kSelThreads) sel_cand_kernel(const SelectArgs a) {
+    __shared__ uint32_t bins[kSelBins];
+    __shared__ int wsum[kSelThreads / 64];
+    __shared__ uint32_t cross[2];
+    __shared__ uint32_t base_s;
+    const int b = blockIdx.y;
+    const int chunk = blockIdx.x;
+    const SeqGeo sg = seq_geo(a, b);
+    const int start = chunk * kSelChunk;
+    if (sg.k <= 0 || start >= sg.L) return;            // uniform per workgroup
+
+    // This chunk's keys (in flight while the histogram is scanned).
+    const uint32_t* keys = a.keys + sg.seq0 + start + threadIdx.x;
+    uint32_t kk[kSelPer];
+    bool in[kSelPer];
+#pragma unroll
+    for (int e = 0; e < kSelPer; ++e) {
+        in[e] = start + e * kSelThreads + (int)threadIdx.x < sg.L;
+        kk[e] = in[e] ? keys[e * kSelThreads] : 0u;
+    }
+    for (int i = threadIdx.x; i < kSelBins; i += kSelThreads) bins[i] = a.zeroed[(size_t)b * kSelBins + i];
+    __syncthreads();
+    find_crossing<kSelBins>(bins, sg.k, wsum, cross);
+    const uint32_t d1 = cross[0];
+    if (chunk == 0 && threadIdx.x == 0) {
+        a.seq_info[4 * b + 0] = d1;
+        a.seq_info[4 * b + 1] = cross[1];
+    }
+
+    bool cand[kSelPer];
+    int above = 0, ncand = 0;
+#pragma unroll
+    for (int e = 0; e < kSelPer; ++e) {
+        const uint32_t dig = kk[e] >> (32 - kSelDigitBits);
+        above += (in[e] && dig > d1) ? 1 : 0;
+        cand[e] = in[e] && dig == d1;
+        ncand += cand[e] ? 1 : 0;
+    }
+    // One counter update per workgroup; candidate order does not matter.
+    int total;
+    int off = wg_exclusive_scan(ncand, wsum, &total);
+    if (threadIdx.x == 0)
+        base_s = total ? atomicAdd(&a.zeroed[(size_t)a.batch * kSelBins + b], (uint32_t)total) : 0u;
+    int above_all;
+    wg_exclusive_scan(above, wsum, &above_all);        // also orders base_s before the reads
+    const uint32_t base = base_s;
+#pragma unroll
+    for (int e = 0; e < kSelPer; ++e) {
+        if (!cand[e]) continue;
+        const int slot = (int)base + off++;
+        if (slot < sg.L) {
+            a.cand_key[sg.seq0 + slot] = kk[e];
+            a.cand_pos[sg.seq0 + slot] = start + e * kSelThreads + (int)threadIdx.x;
+        }
+    }
+    if (threadIdx.x == 0) a.chunk_above[(size_t)b * a.nchunks + chunk] = (uint32_t)above_all;
+}
+
+__global__ void __launch_bounds__(kSelThreads) sel_write_kernel(const SelectArgs a) {
+    __shared__ uint32_t bins[1024];
+    __shared__ uint32_t gt[kSelMaxChunks];
+    __shared__ uint32_t ties[kSelMaxChunks];
+    __shared__ int wsum[kSelThreads / 64];
+    __shared__ uint32_t cross[2];
+    const int b = blockIdx.y;
+    const int chunk = blockIdx.x;
+    const int tid = threadIdx.x;
+    const SeqGeo sg = seq_geo(a, b);
+    const int start = chunk * kSelChunk;
+    if (sg.k <= 0 || start >= sg.L) return;            // uniform per workgroup
+
+    // This chunk's keys: thread t owns the consecutive positions start + kSelPer*t + e.
+    const int p0 = start + kSelPer * tid;
+    uint32_t kk[kSelPer];
+#pragma unroll
+    for (int e = 0; e < kSelPer; ++e) kk[e] = (p0 + e < sg.L) ? a.keys[sg.seq0 + p0 + e] : 0u;
+
+    const uint32_t d1 = a.seq_info[4 * b + 0];
+    const int above1 = (int)a.seq_info[4 * b + 1];
+    const int nc = min((int)a.zeroed[(size_t)a.batch * kSelBins + b], sg.L);
+    const uint32_t* ck = a.cand_key + sg.seq0;
+    const int32_t* cp = a.cand_pos + sg.seq0;
+    const int nch = min((sg.L + kSelChunk - 1) / kSelChunk, a.nchunks);
+
+    // Exact theta: two 10-bit digits below the top digit, over the candidates.
     uint32_t prefix = d1;
-    int need = k - above;
+    int need = sg.k - above1;                 // keys of bin d1 still to take, >= 1
 #pragma unroll 1
     for (int level = 0; level < 2; ++level) {
-        const int shift = (level == 0) ? 10 : 0;
-        const int pshift = shift + 10;
-        for (int i = tid; i < 1024; i += kFinishThreads) bins[i] = 0u;
+        const int shift = level == 0 ? 10 : 0;
+        for (int i = tid; i < 1024; i += kSelThreads) bins[i] = 0u;
         __syncthreads();
-        for (int i = tid; i < nsup; i += kFinishThreads) {
-            const uint32_t key = tkey[i];
-            if ((key >> pshift) == prefix) atomicAdd(&bins[(key >> shift) & 1023u], 1u);
+        for (int i = tid; i < nc; i += kSelThreads) {
+            const uint32_t key = ck[i];
+            if ((key >> (shift + 10)) == prefix) atomicAdd(&bins[(key >> shift) & 1023u], 1u);
         }
         __syncthreads();
-        find_crossing(bins, 1024, need, wsum[0], bc);
-        prefix = (prefix << 10) | bc[0];
-        need -= (int)bc[1];
-        above += (int)bc[1];
+        find_crossing<1024>(bins, need, wsum, cross);
+        prefix = (prefix << 10) | cross[0];
+        need -= (int)cross[1];
         __syncthreads();
     }
-    const uint32_t theta = prefix;     // exact k-th largest key
-    const int take_ties = need;        // positions equal to theta still to take (>= 1)
+    const uint32_t theta = prefix;            // the k-th largest key
+    const int take = need;                    // keys equal to theta to take, lowest positions first
 
-    // d. ordered compaction of the scratch list into T.
-    int ties_seen = 0, written = 0;
-    for (int base = 0; base < nsup; base += kRound) {
-        const int i0 = base + kPer * tid;
-        uint32_t kk[kPer];
-        int32_t pp[kPer];
-        bool tie[kPer];
-#pragma unroll
-        for (int e = 0; e < kPer; ++e) {
-            const bool in = (i0 + e) < nsup;
-            kk[e] = in ? tkey[i0 + e] : 0u;
-            pp[e] = in ? tpos[i0 + e] : 0;
-            tie[e] = in && kk[e] == theta;
-        }
-        int toff[kPer];
-        const int ntie = round_offsets(tie, toff, wsum[parity]);
-        parity ^= 1;
-        bool sel[kPer];
-#pragma unroll
-        for (int e = 0; e < kPer; ++e) {
-            const bool in = (i0 + e) < nsup;
-            sel[e] = in && (kk[e] > theta || (tie[e] && ties_seen + toff[e] < take_ties));
-        }
-        int soff[kPer];
-        const int nsel = round_offsets(sel, soff, wsum[parity]);
-        parity ^= 1;
-#pragma unroll
-        for (int e = 0; e < kPer; ++e)
-            if (sel[e] && written + soff[e] < k) out[written + soff[e]] = pp[e];
-        ties_seen += ntie;
-        written += nsel;
+    // Chunks up to this one: candidates above theta and equal to theta.
+    for (int c = tid; c <= chunk; c += kSelThreads) {
+        gt[c] = 0u;
+        ties[c] = 0u;
     }
+    __syncthreads();
+    for (int i = tid; i < nc; i += kSelThreads) {
+        const int c = min(max(cp[i], 0) >> kSelChunkShift, nch - 1);
+        if (c > chunk) continue;
+        const uint32_t key = ck[i];
+        if (key > theta) atomicAdd(&gt[c], 1u);
+        else if (key == theta) atomicAdd(&ties[c], 1u);
+    }
+    __syncthreads();
+    // Output offset of this chunk and its tie share, from the chunks before it.
+    int tl = 0, sl = 0;
+    for (int c = tid; c < chunk; c += kSelThreads) {
+        tl += (int)ties[c];
+        sl += (int)a.chunk_above[(size_t)b * a.nchunks + c] + (int)gt[c];
+    }
+    int ties_before, sel_before;
+    wg_exclusive_scan(tl, wsum, &ties_before);
+    wg_exclusive_scan(sl, wsum, &sel_before);
+    const int off0 = sel_before + min(ties_before, take);
+    const int tq = min(max(take - ties_before, 0), (int)ties[chunk]);
+
+    bool gtp[kSelPer], tie[kSelPer];
+#pragma unroll
+    for (int e = 0; e < kSelPer; ++e) {
+        const bool in = p0 + e < sg.L;
+        gtp[e] = in && kk[e] > theta;
+        tie[e] = in && kk[e] == theta;
+    }
+    int trank[kSelPer];
+    ordered_offsets(tie, trank, wsum);
+    bool sel[kSelPer];
+#pragma unroll
+    for (int e = 0; e < kSelPer; ++e) sel[e] = gtp[e] || (tie[e] && trank[e] < tq);
+    int o[kSelPer];
+    ordered_offsets(sel, o, wsum);
+    int32_t* out = a.indices + sg.kout;
+#pragma unroll
+    for (int e = 0; e < kSelPer; ++e)
+        if (sel[e] && off0 + o[e] < sg.k) out[off0 + o[e]] = p0 + e;
 }
 
 }  // namespace
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
-    const int nh = a.batch * kSelBins;
-    hipLaunchKernelGGL(sel_zero_kernel, dim3((nh + 255) / 256), dim3(256), 0, stream, a.hist, nh);
-    if (a.nchunks > 0)
-        hipLaunchKernelGGL(sel_keys_kernel, dim3(a.nchunks, a.batch), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(sel_finish_kernel, dim3(a.batch), dim3(kFinishThreads), 0, stream, a);
+    const int nz = a.batch * kSelBins + a.batch;
+    hipLaunchKernelGGL(sel_zero_kernel, dim3((nz + 1023) / 1024), dim3(256), 0, stream, a.zeroed, nz);
+    if (a.nchunks > 0) {
+        const dim3 grid(a.nchunks, a.batch);
+        hipLaunchKernelGGL(sel_keys_kernel, grid, dim3(kSelThreads), 0, stream, a);
+        hipLaunchKernelGGL(sel_cand_kernel, grid, dim3(kSelThreads), 0, stream, a);
+        hipLaunchKernelGGL(sel_write_kernel, grid, dim3(kSelThreads), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -6,6 +6,8 @@ libvegas.so on one HIP stream.
 """
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
 from . import vegas as V
@@ -68,3 +70,35 @@ class LayerStep:
         self.select(stream)
         for j in range(self.n_drafts):
             self.draft(j, stream)
+
+    def bind(self, stream=None):
+        """Return argument-free callables (verify, verify_plain, select, [draft_j]) with every
+        ctypes argument converted once, for launch loops where host time matters."""
+        i = self.inp
+        st = V._stream(stream)
+        shape = ctypes.byref(self.shape)
+        ws, wsb = self.workspace.data_ptr(), self.workspace.numel()
+        L = V.lib()
+
+        def call(fn, name, args):
+            def go():
+                rc = fn(*args)
+                if rc:
+                    V._check(rc, name)
+            return go
+
+        common = (shape, self.gamma, i["q"].data_ptr(), i["k"].data_ptr(), i["v"].data_ptr(),
+                  i["cu_seqlens_k"].data_ptr(), self.max_seqlen, self.total_kv)
+        verify = call(L.vegas_verify_attn, "vegas_verify_attn",
+                      common + (self.collect_mask, self.scores.data_ptr(), self.out.data_ptr(), ws, wsb, st))
+        plain = call(L.vegas_verify_attn, "vegas_verify_attn",
+                     common + (0, None, self.out.data_ptr(), ws, wsb, st))
+        select = call(L.vegas_select_topk, "vegas_select_topk",
+                      (self.batch, self.hkv, self.gamma, self.scores.data_ptr(), i["cu_seqlens_k"].data_ptr(),
+                       self.max_seqlen, self.total_kv, i["cu_k"].data_ptr(), self.indices.data_ptr(), ws, wsb, st))
+        drafts = [call(L.vegas_sparse_decode_attn, "vegas_sparse_decode_attn",
+                       (shape, i["draft_q"][j].data_ptr(), i["k"].data_ptr(), i["v"].data_ptr(),
+                        i["cu_seqlens_k"].data_ptr(), self.total_kv, self.indices.data_ptr(), i["cu_k"].data_ptr(),
+                        self.max_k, self.draft_out[j].data_ptr(), ws, wsb, st))
+                  for j in range(self.n_drafts)]
+        return verify, plain, select, drafts
