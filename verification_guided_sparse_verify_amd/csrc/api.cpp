@@ -28,10 +28,10 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Workgroups the split kernel should expose on a 256-CU part (the kernel
-// holds one workgroup per CU): a few rounds for verification, whose splits
-// are long, and a single round for the short gathered lists of drafting.
-constexpr int kVerifyWorkgroups = 1024;
+// Workgroups the split kernel should expose: one round on the 256 CUs (the
+// kernel holds one workgroup per CU).  Each further round costs a workgroup's
+// start-up and drain on the critical path, about 10 us at 128K positions.
+constexpr int kVerifyWorkgroups = 256;
 constexpr int kGatherWorkgroups = 256;
 
 struct AttnPlan {
@@ -43,7 +43,7 @@ struct AttnPlan {
     size_t total() const { return align_up(part_o) + align_up(part_ml); }
 };
 
-AttnPlan plan_attn(int batch, int hkv, int M, int head_dim, int max_n, bool gather) {
+AttnPlan plan_attn(bool bf16, int batch, int hkv, int M, int head_dim, int max_n, bool gather) {
     AttnPlan p;
     p.mb = (M + 15) / 16;
     const int unit = vegas::kAttnWaves * vegas::kAttnBlock;
@@ -58,7 +58,7 @@ AttnPlan plan_attn(int batch, int hkv, int M, int head_dim, int max_n, bool gath
     chunk = (chunk + unit - 1) / unit * unit;
     // Both caps are multiples of `unit`.  Verification uses the same plan with
     // and without collection, so the two give bit-identical outputs.
-    const int cap = gather ? vegas::kMaxGatherChunk : vegas::kMaxCollectChunk;
+    const int cap = gather ? vegas::kMaxGatherChunk : vegas::collect_chunk_cap(bf16, head_dim);
     if (chunk > cap) chunk = cap;
     p.chunk = chunk;
     p.nsplit = (n + chunk - 1) / chunk;
@@ -160,7 +160,8 @@ vegas_status_t vegas_verify_workspace_size(const vegas_attn_shape_t* shape, int3
     if (max_seqlen_k < gamma + 1)
         return fail(VEGAS_ERR_INVALID_ARGUMENT, "max_seqlen_k %d < gamma+1", max_seqlen_k);
     const int G = shape->num_q_heads / shape->num_kv_heads;
-    *bytes = plan_attn(shape->batch, shape->num_kv_heads, (gamma + 1) * G, shape->head_dim,
+    *bytes = plan_attn(shape->dtype == VEGAS_DTYPE_BF16, shape->batch, shape->num_kv_heads, (gamma + 1) * G,
+                       shape->head_dim,
                        max_seqlen_k, false).total();
     return VEGAS_OK;
 }
@@ -190,7 +191,8 @@ vegas_status_t vegas_verify_attn(const vegas_attn_shape_t* shape, int32_t gamma,
     if (!rows_fit_32bit(shape, max_seqlen_k))
         return fail(VEGAS_ERR_UNSUPPORTED, "one sequence's K/V rows span 4 GiB or more");
     const int G = shape->num_q_heads / shape->num_kv_heads;
-    const AttnPlan plan = plan_attn(shape->batch, shape->num_kv_heads, W * G, shape->head_dim,
+    const AttnPlan plan = plan_attn(shape->dtype == VEGAS_DTYPE_BF16, shape->batch, shape->num_kv_heads, W * G,
+                                    shape->head_dim,
                                     max_seqlen_k, false);
     if (workspace_bytes < plan.total())
         return fail(VEGAS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.total(),
@@ -287,7 +289,8 @@ vegas_status_t vegas_sparse_decode_workspace_size(const vegas_attn_shape_t* shap
     const int G = shape->num_q_heads / shape->num_kv_heads;
     if (G > max_rows(shape))
         return fail(VEGAS_ERR_UNSUPPORTED, "Hq/Hkv = %d exceeds %d", G, max_rows(shape));
-    *bytes = plan_attn(shape->batch, shape->num_kv_heads, G, shape->head_dim, max_idx, true).total();
+    *bytes = plan_attn(shape->dtype == VEGAS_DTYPE_BF16, shape->batch, shape->num_kv_heads, G, shape->head_dim,
+                       max_idx, true).total();
     return VEGAS_OK;
 }
 
@@ -309,7 +312,8 @@ vegas_status_t vegas_sparse_decode_attn(const vegas_attn_shape_t* shape, const v
         return fail(VEGAS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
     if (!workspace) return fail(VEGAS_ERR_INVALID_ARGUMENT, "workspace is NULL");
     const int G = shape->num_q_heads / shape->num_kv_heads;
-    const AttnPlan plan = plan_attn(shape->batch, shape->num_kv_heads, G, shape->head_dim, max_idx, true);
+    const AttnPlan plan = plan_attn(shape->dtype == VEGAS_DTYPE_BF16, shape->batch, shape->num_kv_heads, G,
+                                    shape->head_dim, max_idx, true);
     vegas::AttnArgs a{};
     a.q = q;
     a.k = k;

@@ -10,21 +10,29 @@
 // token).
 //
 // Work decomposition.  A workgroup owns one (sequence b, KV head g, position
-// split).  Its four waves take 32-position blocks in turn.  All W*G query rows
-// that share KV head g (at most 64) are processed together, so every K/V byte
-// is read from HBM exactly once for all rows.  Per block and wave:
-//   S^T[pos, row] = K[pos, :] . Q[row, :]         16x16x32 bf16 MFMA; K straight
-//                                                  into registers, Q from LDS
+// split); the host sizes splits so that the grid is one round of workgroups
+// on the 256 CUs.  All W*G query rows that share KV head g (at most 64) are
+// processed together, so every K/V byte is read from HBM exactly once for all
+// rows.  The four waves take 16-position blocks in turn; each wave streams its
+// blocks through a private two-stage LDS ring filled by the load-to-LDS path
+// (no VGPR round trip), computing one block while the next is in flight.  Per
+// block and wave:
+//   S^T[pos, row] = K[pos, :] . Q[row, :]          16x16x32 bf16 MFMA; K from
+//                                                   the ring, Q in registers
+//   collection (verification only)                 collected rows summed over
+//                                                   the query heads of g: a
+//                                                   16-lane DPP reduction,
+//                                                   buffered in LDS
 //   online softmax over positions (exp2 domain)    rows are MFMA columns, so a
-//                                                  row max is in-lane + 2 shuffles
-//   O^T[d, row] += V^T[d, pos] . P^T[pos, row]     V copied HBM -> LDS by the
-//                                                  load-to-LDS path, read transposed
+//                                                   row max is in-lane + 2 shuffles
+//   O^T[d, row] += V^T[d, pos] . P^T[pos, row]     16x16x16 bf16 MFMA; V^T read
+//                                                   transposed from the ring
 // The P^T operand is the S^T accumulator itself: the k order of an MFMA is a
-// free permutation, so the four S^T values a lane owns for each of two
-// 16-position tiles are exactly its eight k slots, and V^T is read in that
-// order.  The next block's K and V are in flight while a block is computed.
-// Partials (m, l, O) of the four waves are merged in LDS and one partial per
-// workgroup goes to the workspace; attn_combine merges the splits.
+// free permutation, so the four S^T values a lane owns are exactly its four k
+// slots, and V^T is read in that order.  Partials (m, l, O) of the four waves
+// are merged in LDS and one partial per workgroup goes to the workspace; the
+// collected scores of the split are written with coalesced stores;
+// attn_combine merges the splits.
 #include "internal.h"
 
 namespace vegas {
@@ -161,7 +169,7 @@ struct Geo {
     static constexpr int TLD = kAttnBlock / RPI;  // copies per lane per K (or V) tile
     static constexpr int TILE = kAttnBlock * ROWB;
     static constexpr int STAGE = 2 * TILE;        // K tile then V tile
-    static constexpr int NST = (kAttnWaves * 4 * STAGE <= 128 * 1024) ? 4 : 2;   // ring depth
+    static constexpr int NST = kAttnStages;       // ring depth
     static constexpr int RING = kAttnWaves * NST * STAGE;
     static constexpr int BLOCK_OPS = 2 * TLD;     // copies one block issues
     static constexpr int SWZU = 16 / EPC;         // chunks per 16-element d tile
@@ -369,7 +377,7 @@ attn_split_kernel(const AttnArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[GEO::MAIN];
     __shared__ int idx_s[GATHER ? kMaxGatherChunk : 1];
     // Collected scores of this split, written to HBM once the split is done.
-    __shared__ float score_s[COLLECT ? kMaxCollectChunk : 1];
+    __shared__ float score_s[COLLECT ? collect_chunk_cap(BF16, D) : 1];
 
     const int lane = threadIdx.x & 63;
     // wave index as a scalar: every branch on it is uniform

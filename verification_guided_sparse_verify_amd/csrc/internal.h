@@ -8,15 +8,28 @@
 
 namespace vegas {
 
-// Waves per attention workgroup and positions per wave iteration.
+// Waves per attention workgroup, positions per wave iteration, and depth of
+// each wave's LDS ring of K/V blocks (one block computed while the next one
+// is in flight; deeper rings measured slower).
 constexpr int kAttnWaves = 4;
 constexpr int kAttnBlock = 16;
+constexpr int kAttnStages = 2;
 // Longest position range one workgroup takes in gather mode: its index list
 // is staged in LDS.
 constexpr int kMaxGatherChunk = 2048;
-// Longest position range one workgroup takes in verification with
-// collection: its collected scores are buffered in LDS.
-constexpr int kMaxCollectChunk = 4352;
+
+// Bytes of one workgroup's K/V ring.
+__host__ __device__ constexpr int attn_ring_bytes(bool bf16, int head_dim) {
+    return kAttnWaves * kAttnStages * 2 * kAttnBlock * head_dim * (bf16 ? 2 : 4);
+}
+// Longest position range one workgroup takes in verification: the collected
+// scores of its range are buffered in LDS next to the ring (150 KB in all of
+// the 160 KB), at most 16896 positions, a multiple of kAttnWaves*kAttnBlock.
+__host__ __device__ constexpr int collect_chunk_cap(bool bf16, int head_dim) {
+    return ((150 * 1024 - attn_ring_bytes(bf16, head_dim)) / 4 / 64 * 64) < 16896
+               ? (150 * 1024 - attn_ring_bytes(bf16, head_dim)) / 4 / 64 * 64
+               : 16896;
+}
 
 // Arguments of the split attention kernel and of its combine kernel.
 // One kernel serves both the verification pass (contiguous positions, causal
