@@ -207,17 +207,22 @@ __device__ __forceinline__ uint32_t row_offset(const SplitCtx& c, int p) {
 // on rows 4 apart, hit distinct banks).
 template <class GEO, bool GATHER>
 __device__ __forceinline__ void issue_block(const SplitCtx& c, int p0, int lane, unsigned char* stage) {
+    // All row offsets first (in gather mode, LDS reads of the index list that
+    // then complete together), then the copies back to back.
+    uint32_t off[GEO::TLD];
+#pragma unroll
+    for (int i = 0; i < GEO::TLD; ++i) off[i] = row_offset<GATHER>(c, p0 + i * GEO::RPI + lane / GEO::CPR);
 #pragma unroll
     for (int i = 0; i < GEO::TLD; ++i) {
         const int row = i * GEO::RPI + lane / GEO::CPR;
         const int cc = (lane % GEO::CPR) ^ (row & GEO::KSWZ);
-        copy16_to_lds(c.kseq + row_offset<GATHER>(c, p0 + row) + cc * 16, stage + i * 1024);
+        copy16_to_lds(c.kseq + off[i] + cc * 16, stage + i * 1024);
     }
 #pragma unroll
     for (int i = 0; i < GEO::TLD; ++i) {
         const int row = i * GEO::RPI + lane / GEO::CPR;
         const int cc = (lane % GEO::CPR) ^ (GEO::SWZU * ((row >> 2) & 3));
-        copy16_to_lds(c.vseq + row_offset<GATHER>(c, p0 + row) + cc * 16, stage + GEO::TILE + i * 1024);
+        copy16_to_lds(c.vseq + off[i] + cc * 16, stage + GEO::TILE + i * 1024);
     }
 }
 
@@ -225,6 +230,7 @@ __device__ __forceinline__ void issue_block(const SplitCtx& c, int p0, int lane,
 template <bool BF16, int D, int MB>
 struct WaveState {
     Frag<BF16> qf[MB][D / 32];
+    bool qvalid[MB];
     float cmask[MB];
     int rrow[MB];
     float m_run[MB], l_run[MB];
@@ -406,14 +412,6 @@ attn_split_kernel(const AttnArgs a) {
     if (seq0 < 0 || n_b <= 0 || start >= count) return;          // uniform per workgroup
     const int end = min(start + a.chunk, count);
 
-    if constexpr (GATHER) {
-        for (int i = threadIdx.x; i < end - start; i += blockDim.x) {
-            const int t = a.indices[ib0 + start + i];
-            idx_s[i] = min(max(t, 0), n_b - 1);
-        }
-        __syncthreads();
-    }
-
     WaveState<BF16, D, MB> ws;
 #pragma unroll
     for (int qb = 0; qb < MB; ++qb) {
@@ -424,21 +422,35 @@ attn_split_kernel(const AttnArgs a) {
         const int hl = valid ? j % a.G : 0;
         ws.rrow[qb] = r;
         ws.cmask[qb] = (COLLECT && valid && ((a.collect_mask >> r) & 1u)) ? 1.f : 0.f;
+        // Padding rows load a real row (no divergent branch, so all loads stay
+        // in flight together) and are zeroed afterwards.
         const T* qp = static_cast<const T*>(a.q) +
                       ((size_t)(b * a.W + r) * a.hq + (size_t)g * a.G + hl) * D + 8 * lg;
 #pragma unroll
-        for (int ch = 0; ch < DC; ++ch) ws.qf[qb][ch] = valid ? load_frag<BF16>(qp + 32 * ch) : zero_frag<BF16>();
+        for (int ch = 0; ch < DC; ++ch) ws.qf[qb][ch] = load_frag<BF16>(qp + 32 * ch);
+        ws.qvalid[qb] = valid;
         ws.m_run[qb] = kNegInf;
         ws.l_run[qb] = 0.f;
 #pragma unroll
         for (int db = 0; db < DB; ++db) ws.o[db][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    // Retire the Q loads here, where the compiler can see it, so that its own
-    // wait for them is not placed inside the block loop.
+    // Gather mode: stage this split's index list (clamped into the sequence)
+    // while the Q loads are in flight.
+    if constexpr (GATHER) {
+        constexpr int IPT = kMaxGatherChunk / (kAttnWaves * 64);   // indices per thread
+        int t[IPT];
 #pragma unroll
-    for (int qb = 0; qb < MB; ++qb)
+        for (int e = 0; e < IPT; ++e) {   // clamped, branch-free: all loads in flight together
+            const int i = min(e * kAttnWaves * 64 + (int)threadIdx.x, end - start - 1);
+            t[e] = a.indices[ib0 + start + i];
+        }
 #pragma unroll
-        for (int ch = 0; ch < DC; ++ch) keep_live(ws.qf[qb][ch]);
+        for (int e = 0; e < IPT; ++e) {
+            const int i = e * kAttnWaves * 64 + threadIdx.x;
+            if (i < end - start) idx_s[i] = min(max(t[e], 0), n_b - 1);
+        }
+        __syncthreads();
+    }
 
     SplitCtx c;
     c.row_stride = a.hkv * D * GEO::ES;
@@ -460,6 +472,18 @@ attn_split_kernel(const AttnArgs a) {
     if (nmine > 0) {
 #pragma unroll
         for (int st = 0; st < NST - 1; ++st) issue_block<GEO, GATHER>(c, block_pos(st), lane, ring + st * GEO::STAGE);
+    }
+    // Retire the Q loads here, where the compiler can see it (its wait also
+    // covers the first blocks' copies, issued after them), so that its own
+    // wait for them is not placed inside the block loop.
+#pragma unroll
+    for (int qb = 0; qb < MB; ++qb)
+#pragma unroll
+        for (int ch = 0; ch < DC; ++ch) {
+            keep_live(ws.qf[qb][ch]);
+            if (!ws.qvalid[qb]) ws.qf[qb][ch] = zero_frag<BF16>();
+        }
+    if (nmine > 0) {
         for (int jj = 0; jj < nmine; ++jj) {
             wait_vmem<(NST - 2) * GEO::BLOCK_OPS>();      // block jj has landed
             issue_block<GEO, GATHER>(c, block_pos(jj + NST - 1), lane, ring + ((jj + NST - 1) % NST) * GEO::STAGE);

@@ -193,7 +193,15 @@ __global__ void __launch_bounds__(kSelThreads) sel_cand_kernel(const SelectArgs 
         in[e] = start + e * kSelThreads + (int)threadIdx.x < sg.L;
         kk[e] = in[e] ? keys[e * kSelThreads] : 0u;
     }
-    for (int i = threadIdx.x; i < kSelBins; i += kSelThreads) bins[i] = a.zeroed[(size_t)b * kSelBins + i];
+    {
+        const uint4* src = reinterpret_cast<const uint4*>(a.zeroed + (size_t)b * kSelBins);
+        uint4 h4[kSelBins / 4 / kSelThreads];
+#pragma unroll
+        for (int q = 0; q < kSelBins / 4 / kSelThreads; ++q) h4[q] = src[q * kSelThreads + threadIdx.x];
+#pragma unroll
+        for (int q = 0; q < kSelBins / 4 / kSelThreads; ++q)
+            reinterpret_cast<uint4*>(bins)[q * kSelThreads + threadIdx.x] = h4[q];
+    }
     __syncthreads();
     find_crossing<kSelBins>(bins, sg.k, wsum, cross);
     const uint32_t d1 = cross[0];
@@ -257,6 +265,39 @@ __global__ void __launch_bounds__(kSelThreads) sel_write_kernel(const SelectArgs
     const int32_t* cp = a.cand_pos + sg.seq0;
     const int nch = min((sg.L + kSelChunk - 1) / kSelChunk, a.nchunks);
 
+    // Candidates: the first kSelThreads*kCandPer stay in registers for all
+    // passes (typically all of them); any beyond are re-read per pass.
+    constexpr int kCandPer = 8;
+    constexpr int kCandHeld = kSelThreads * kCandPer;
+    uint32_t hk[kCandPer];
+    int32_t hp[kCandPer];
+#pragma unroll
+    for (int e = 0; e < kCandPer; ++e) {
+        const int i = e * kSelThreads + tid;
+        hk[e] = i < nc ? ck[i] : 0u;
+        hp[e] = i < nc ? cp[i] : 0;
+    }
+    // Visit every candidate (key, position) once: held ones first, then the rest
+    // in batches of kCandPer loads per thread.
+    auto for_each_cand = [&](auto&& fn) {
+#pragma unroll
+        for (int e = 0; e < kCandPer; ++e)
+            if (e * kSelThreads + tid < nc) fn(hk[e], hp[e]);
+        for (int base = kCandHeld; base < nc; base += kCandHeld) {
+            uint32_t bk[kCandPer];
+            int32_t bp[kCandPer];
+#pragma unroll
+            for (int e = 0; e < kCandPer; ++e) {
+                const int i = base + e * kSelThreads + tid;
+                bk[e] = i < nc ? ck[i] : 0u;
+                bp[e] = i < nc ? cp[i] : 0;
+            }
+#pragma unroll
+            for (int e = 0; e < kCandPer; ++e)
+                if (base + e * kSelThreads + tid < nc) fn(bk[e], bp[e]);
+        }
+    };
+
     // Exact theta: two 10-bit digits below the top digit, over the candidates.
     uint32_t prefix = d1;
     int need = sg.k - above1;                 // keys of bin d1 still to take, >= 1
@@ -265,10 +306,9 @@ __global__ void __launch_bounds__(kSelThreads) sel_write_kernel(const SelectArgs
         const int shift = level == 0 ? 10 : 0;
         for (int i = tid; i < 1024; i += kSelThreads) bins[i] = 0u;
         __syncthreads();
-        for (int i = tid; i < nc; i += kSelThreads) {
-            const uint32_t key = ck[i];
+        for_each_cand([&](uint32_t key, int32_t) {
             if ((key >> (shift + 10)) == prefix) atomicAdd(&bins[(key >> shift) & 1023u], 1u);
-        }
+        });
         __syncthreads();
         find_crossing<1024>(bins, need, wsum, cross);
         prefix = (prefix << 10) | cross[0];
@@ -284,13 +324,13 @@ __global__ void __launch_bounds__(kSelThreads) sel_write_kernel(const SelectArgs
         ties[c] = 0u;
     }
     __syncthreads();
-    for (int i = tid; i < nc; i += kSelThreads) {
-        const int c = min(max(cp[i], 0) >> kSelChunkShift, nch - 1);
-        if (c > chunk) continue;
-        const uint32_t key = ck[i];
-        if (key > theta) atomicAdd(&gt[c], 1u);
-        else if (key == theta) atomicAdd(&ties[c], 1u);
-    }
+    for_each_cand([&](uint32_t key, int32_t pos) {
+        const int c = min(max(pos, 0) >> kSelChunkShift, nch - 1);
+        if (c <= chunk) {
+            if (key > theta) atomicAdd(&gt[c], 1u);
+            else if (key == theta) atomicAdd(&ties[c], 1u);
+        }
+    });
     __syncthreads();
     // Output offset of this chunk and its tie share, from the chunks before it.
     int tl = 0, sl = 0;
