@@ -118,6 +118,56 @@ def cpu_baseline(wl, layer_inputs, min_seconds=10.0):
     }
 
 
+def collect_sweep(base, gammas=(1, 3, 5, 7, 11, 15), reps=8):
+    """Verification time of one layer of `base` (its prefix, heads and batch) with collection
+    off, Collect-2-Query (rows 0 and gamma) and all gamma+1 rows, for several gamma.  The pages
+    report that collecting every row of an instrumented FlashAttention-3 grows with the row
+    count while Collect-2-Query stays flat ("Vegas ...", sec. 3.3, Fig. 6); here collection is
+    a head-summed reduction inside the kernel, whose cost does not depend on which rows are
+    collected.  Prints one JSON line."""
+    import dataclasses
+    import torch
+    from verification_guided_sparse_verify_amd import workloads as W
+    from verification_guided_sparse_verify_amd.step import LayerStep
+
+    stream = torch.cuda.current_stream()
+    rows = []
+    for gamma in gammas:
+        if (gamma + 1) * (base.num_q_heads // base.num_kv_heads) > 64:
+            continue
+        wl = dataclasses.replace(base, gamma=gamma, layers=1, draft_steps=1)
+        inps = [W.make_inputs(wl, seed=0, device="cuda:0", layer=l) for l in range(2)]
+        masks = {"off": 0, "collect2": 1 | (1 << gamma), "all_rows": (1 << (gamma + 1)) - 1}
+        res = {"gamma": gamma, "query_rows_per_kv_head": (gamma + 1) * (wl.num_q_heads // wl.num_kv_heads)}
+        for name, mask in masks.items():
+            steps = [LayerStep(inp, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, gamma, wl.seqlens,
+                               wl.k_per_seq, wl.scale, n_drafts=1, collect_mask=mask if mask else None)
+                     for inp in inps]
+            calls = [st.bind(stream)[0 if mask else 1] for st in steps]
+            for c in calls:
+                c()
+            pairs = []
+            for _ in range(reps):
+                for c in calls:
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    c()
+                    b.record(stream)
+                    pairs.append((a, b))
+            torch.cuda.synchronize()
+            res[name + "_us"] = round(statistics.fmean(a.elapsed_time(b) * 1e3 for a, b in pairs), 2)
+            del steps, calls
+        res["collect2_overhead"] = round(res["collect2_us"] / res["off_us"] - 1, 4)
+        res["all_rows_overhead"] = round(res["all_rows_us"] / res["off_us"] - 1, 4)
+        rows.append(res)
+        print(f"# gamma {gamma}: {res}", file=sys.stderr, flush=True)
+        del inps
+        torch.cuda.empty_cache()
+    print(json.dumps({"collect_sweep": base.name, "unit": "us per verification call (split + combine)",
+                      "rows": rows}), flush=True)
+
+
 def copy_calibration(nbytes):
     """A plain device-to-device copy of known size, for scaling the HBM byte counters."""
     import torch
@@ -139,6 +189,9 @@ def main():
     ap.add_argument("--layers", type=int, default=None, help="override the layer count (profiling runs only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--collect-sweep", action="store_true",
+                    help="only time verification of one layer with collection off, Collect-2-Query and "
+                         "all rows, over gamma")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a device copy of BYTES bytes three times (counter calibration)")
     args = ap.parse_args()
@@ -163,6 +216,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
     wl = W.named_workload(args.workload)
+    if args.collect_sweep:
+        collect_sweep(wl)
+        return
     layers = args.layers if args.layers is not None else wl.layers
     dev = "cuda:0"
     t_gen = time.perf_counter()

@@ -203,3 +203,26 @@ def test_select_exact_on_tied_integer_scores(case):
     torch.cuda.synchronize()
     got = out[: int(cuk[-1])].cpu().numpy()
     assert np.array_equal(got, idx_ref)
+
+
+MASK_CASES = [
+    # dtype, batch, Hq, Hkv, D, gamma, prefix lengths, collect mask (None: Collect-2-Query)
+    ("bf16", 2, 32, 8, 128, 5, [3000, 700], "all"),
+    ("bf16", 2, 16, 8, 64, 7, [1500, 2049], 0b10110010),
+    ("f32", 1, 8, 2, 64, 3, [900], "all"),
+    ("bf16", 3, 8, 1, 128, 2, [130, 1, 4100], 0b010),
+]
+
+
+@pytest.mark.parametrize("case", MASK_CASES, ids=lambda c: f"{c[0]}-B{c[1]}-{c[2]}x{c[3]}-D{c[4]}-g{c[5]}-m{c[7]}")
+def test_collect_mask_variants(case):
+    """Collection of any set of verification rows (all rows, as in the pages' first design;
+    or an arbitrary subset): scores, selection and drafts match the oracle."""
+    dtype, B, hq, hkv, d, gamma, prefixes, mask = case
+    if mask == "all":
+        mask = (1 << (gamma + 1)) - 1
+    wl = W.custom_workload(dtype, B, hq, hkv, d, gamma, prefixes)
+    log(f"case: {wl.name} L={prefixes} mask={mask:#x}")
+    inp, st = run_layer(wl, seed=8, collect_mask=mask)
+    worst = check_layer(wl, inp, st, collect_mask=mask)
+    log(f"  worst {worst}")
