@@ -189,6 +189,9 @@ def main():
     ap.add_argument("--layers", type=int, default=None, help="override the layer count (profiling runs only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="keep every layer's KV cache as a randomly permuted page pool of this page size and "
+                         "run the paged entry points (0: contiguous cache)")
     ap.add_argument("--collect-sweep", action="store_true",
                     help="only time verification of one layer with collection off, Collect-2-Query and "
                          "all rows, over gamma")
@@ -221,13 +224,17 @@ def main():
         return
     layers = args.layers if args.layers is not None else wl.layers
     dev = "cuda:0"
+    cpu_leg = not args.no_cpu_baseline and not args.page_size
     t_gen = time.perf_counter()
     layer_inputs, steps = [], []
     for layer in range(layers):
         inp = W.make_inputs(wl, seed=0, device=dev, layer=layer)
+        paged = None
+        if args.page_size:
+            paged = W.page_cache(wl, inp, args.page_size, seed=layer, drop_contiguous=True)
         layer_inputs.append(inp)
         steps.append(LayerStep(inp, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.gamma,
-                               wl.seqlens, wl.k_per_seq, wl.scale, n_drafts=wl.n_drafts))
+                               wl.seqlens, wl.k_per_seq, wl.scale, n_drafts=wl.n_drafts, paged=paged))
         if layer % 6 == 5:
             torch.cuda.synchronize()
             print(f"# generated layer {layer + 1}/{layers}", file=sys.stderr, flush=True)
@@ -320,6 +327,8 @@ def main():
             "gamma": wl.gamma, "k_per_seq": wl.k_per_seq if len(set(wl.k_per_seq)) > 1 else wl.k_per_seq[0],
             "kv_cache_bytes": wl.total_kv * wl.num_kv_heads * wl.head_dim * (2 if wl.dtype == "bf16" else 4) * 2 * layers,
             "order": "verify+select over all layers, then gamma drafting passes over all layers",
+            "kv_cache": (f"paged, {args.page_size}-token pages in a randomly permuted pool" if args.page_size
+                         else "contiguous varlen"),
         },
         "layer_step_gbps": round(step_gbps, 1),
         "layer_step_frac_of_peak": round(step_gbps / PEAK_HBM_GBPS, 4),
@@ -354,7 +363,7 @@ def main():
     result["plain_verify_us"] = round(plain_us, 2)
     result["collect_select_overhead_vs_plain_verify"] = round((verify_mean + mean["select"]) / plain_us - 1, 4)
 
-    if not args.no_cpu_baseline:
+    if cpu_leg:
         result["cpu_baseline"] = cpu_baseline(wl, layer_inputs, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 

@@ -170,6 +170,55 @@ vegas_status_t vegas_sparse_decode_attn(const vegas_attn_shape_t* shape, const v
                                         int32_t max_idx, void* out, void* workspace,
                                         size_t workspace_bytes, void* stream);
 
+/*
+ * Paged KV cache (NEXT to the contiguous layout above).
+ * The pages hook vLLM's attention, whose KV cache is paged, and run drafting
+ * as paged attention with a page size of one token ("Vegas ...", sec. 4
+ * "Serving framework integration"; its Appendix D reports the same latency
+ * for page sizes 1 to 16).  These variants read K and V from a page pool:
+ *
+ *  k, v           [num_pages, page_size, Hkv, D]: pool page p holds page_size
+ *                 consecutive token rows.
+ *  block_table    device int32 [batch, max_pages_per_seq]: position t of
+ *                 sequence b is row t % page_size of pool page
+ *                 block_table[b * max_pages_per_seq + t / page_size].
+ *  page_size      a power of two, 1 .. 256.
+ *  num_pages      pages in the pool; num_pages * page_size < 2^31.  Page
+ *                 numbers read from the table are clamped into the pool.
+ *  max_pages_per_seq * page_size must be >= max_seqlen_k.
+ *
+ * Sequence lengths still come from cu_seqlens_k (length of sequence b =
+ * cu_seqlens_k[b+1] - cu_seqlens_k[b]), which also packs `scores` exactly as
+ * in vegas_verify_attn; q, out, indices and the workspace are as in the
+ * contiguous entry points, and the results are the same.
+ */
+typedef struct {
+    const int32_t* block_table;
+    int32_t max_pages_per_seq;
+    int32_t page_size;
+    int32_t num_pages;
+} vegas_paged_kv_t;
+
+/* Workspace of vegas_verify_attn_paged for a cache of `page_size` (0: the
+ * contiguous cache, same as vegas_verify_workspace_size).  Small pages cap the
+ * positions one split covers, so they can need more workspace. */
+vegas_status_t vegas_verify_paged_workspace_size(const vegas_attn_shape_t* shape, int32_t gamma,
+                                                 int32_t max_seqlen_k, int32_t page_size, size_t* bytes);
+vegas_status_t vegas_verify_attn_paged(const vegas_attn_shape_t* shape, int32_t gamma,
+                                       const void* q, const void* k, const void* v,
+                                       const vegas_paged_kv_t* pages, const int32_t* cu_seqlens_k,
+                                       int32_t max_seqlen_k, int32_t total_kv, uint32_t collect_mask,
+                                       float* scores, void* out, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+/* Workspace: vegas_sparse_decode_workspace_size. */
+vegas_status_t vegas_sparse_decode_attn_paged(const vegas_attn_shape_t* shape, const void* q,
+                                              const void* k, const void* v,
+                                              const vegas_paged_kv_t* pages,
+                                              const int32_t* cu_seqlens_k, int32_t total_kv,
+                                              const int32_t* indices, const int32_t* cu_idx,
+                                              int32_t max_idx, void* out, void* workspace,
+                                              size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -135,3 +135,32 @@ def test_product_code_never_imports_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "vegas_oracle" not in text, f
+
+
+def test_paged_argument_errors(V):
+    s = shape(V)
+    L = V.lib()
+    ws = V.vegas_verify_paged_workspace_size(s, 4, 1000, 16)
+    assert ws >= V.vegas_verify_workspace_size(s, 4, 1000)
+    assert V.vegas_verify_paged_workspace_size(s, 4, 1000, 1) >= ws     # tiny pages cap the split length
+    for bad in (3, 512, -1):
+        with pytest.raises(V.VegasError) as e:
+            V.vegas_verify_paged_workspace_size(s, 4, 1000, bad)
+        assert e.value.status == 2
+
+    def verify(pages, wsb=ws):
+        return L.vegas_verify_attn_paged(ctypes.byref(s), 4, FAKE, FAKE, FAKE, pages, FAKE, 1000, 4000, 1 | 16,
+                                         FAKE, FAKE, FAKE, wsb, None)
+
+    assert verify(None) == 1
+    assert verify(ctypes.byref(V.PagedKV(FAKE, 62, 16, 100))) == 1     # 62 pages of 16 < 1000 positions
+    assert verify(ctypes.byref(V.PagedKV(None, 63, 16, 100))) == 1     # no block table
+    assert verify(ctypes.byref(V.PagedKV(FAKE, 63, 24, 100))) == 2     # not a power of two
+    assert verify(ctypes.byref(V.PagedKV(FAKE, 64, 16, 0))) == 1       # empty pool
+    assert verify(ctypes.byref(V.PagedKV(FAKE, 64, 16, 100)), ws - 1) == 3
+    dws = V.vegas_sparse_decode_workspace_size(s, 50)
+    assert L.vegas_sparse_decode_attn_paged(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, 200, FAKE, FAKE, 50,
+                                            FAKE, FAKE, dws, None) == 1
+    assert L.vegas_sparse_decode_attn_paged(ctypes.byref(s), FAKE, FAKE, FAKE,
+                                            ctypes.byref(V.PagedKV(FAKE, 4, 128, 10)), FAKE, 200, FAKE, FAKE, 50,
+                                            FAKE, FAKE, dws - 1, None) == 3

@@ -226,3 +226,47 @@ def test_collect_mask_variants(case):
     inp, st = run_layer(wl, seed=8, collect_mask=mask)
     worst = check_layer(wl, inp, st, collect_mask=mask)
     log(f"  worst {worst}")
+
+
+PAGED_CASES = [
+    # dtype, batch, Hq, Hkv, D, gamma, prefix lengths, page size
+    ("bf16", 3, 16, 4, 128, 3, [1000, 4097, 129], 16),
+    ("bf16", 3, 16, 4, 128, 3, [1000, 4097, 129], 1),
+    ("bf16", 2, 32, 8, 64, 5, [3000, 40], 256),
+    ("f32", 2, 8, 2, 64, 2, [300, 77], 4),
+    ("bf16", 1, 64, 8, 128, 6, [2000], 32),
+]
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=lambda c: f"{c[0]}-B{c[1]}-{c[2]}x{c[3]}-D{c[4]}-g{c[5]}-P{c[7]}")
+def test_paged_cache_matches_contiguous(case):
+    """The paged entry points read the same logical K/V through a block table, so verification,
+    the scores, the selection and the drafts equal the contiguous path bit for bit (same splits,
+    same arithmetic), and hence the oracle."""
+    dtype, B, hq, hkv, d, gamma, prefixes, P = case
+    wl = W.custom_workload(dtype, B, hq, hkv, d, gamma, prefixes)
+    log(f"case: paged {wl.name} L={prefixes} page={P}")
+    inp, st = run_layer(wl, seed=9)
+    pg = W.page_cache(wl, inp, P, seed=9)
+    pages = V.paged_kv(pg["block_table"], P, pg["num_pages"])
+    out = torch.empty_like(st.out)
+    scores = torch.empty_like(st.scores)
+    ws = torch.empty(max(V.vegas_verify_paged_workspace_size(st.shape, gamma, st.max_seqlen, P), st.workspace.numel()),
+                     dtype=torch.uint8, device="cuda")
+    V.vegas_verify_attn_paged(st.shape, gamma, inp["q"], pg["k_pool"], pg["v_pool"], pages, inp["cu_seqlens_k"],
+                              st.max_seqlen, st.total_kv, st.collect_mask, scores, out, ws)
+    idx = torch.empty_like(st.indices)
+    V.vegas_select_topk(B, hkv, gamma, scores, inp["cu_seqlens_k"], st.max_seqlen, st.total_kv, inp["cu_k"], idx, ws)
+    drafts = torch.empty_like(st.draft_out)
+    for j in range(wl.n_drafts):
+        V.vegas_sparse_decode_attn_paged(st.shape, inp["draft_q"][j], pg["k_pool"], pg["v_pool"], pages,
+                                         inp["cu_seqlens_k"], st.total_kv, idx, inp["cu_k"], st.max_k, drafts[j], ws)
+    torch.cuda.synchronize()
+    cu = wl.cu_seqlens()
+    assert torch.equal(out.view(torch.uint8), st.out.view(torch.uint8))
+    for b in range(B):   # scores are defined on prefix positions only
+        s0, L = cu[b], wl.prefix_lens[b]
+        assert torch.equal(scores[:, s0:s0 + L], st.scores[:, s0:s0 + L])
+    assert torch.equal(idx[: wl.cu_k()[-1]], st.indices[: wl.cu_k()[-1]])
+    assert torch.equal(drafts.view(torch.uint8), st.draft_out.view(torch.uint8))
+    check_layer(wl, inp, st)   # and the contiguous path against the oracle

@@ -11,5 +11,7 @@ from .vegas import (  # noqa: F401
     vegas_abi_version, vegas_verify_workspace_size, vegas_verify_attn,
     vegas_select_workspace_size, vegas_select_topk,
     vegas_sparse_decode_workspace_size, vegas_sparse_decode_attn,
+    PagedKV, paged_kv, vegas_verify_paged_workspace_size, vegas_verify_attn_paged,
+    vegas_sparse_decode_attn_paged,
     VEGAS_DTYPE_F32, VEGAS_DTYPE_BF16,
 )

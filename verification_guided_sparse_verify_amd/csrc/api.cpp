@@ -43,7 +43,8 @@ struct AttnPlan {
     size_t total() const { return align_up(part_o) + align_up(part_ml); }
 };
 
-AttnPlan plan_attn(bool bf16, int batch, int hkv, int M, int head_dim, int max_n, bool gather) {
+AttnPlan plan_attn(bool bf16, int batch, int hkv, int M, int head_dim, int max_n, bool gather,
+                   int page_size = 0) {
     AttnPlan p;
     p.mb = (M + 15) / 16;
     const int unit = vegas::kAttnWaves * vegas::kAttnBlock;
@@ -58,7 +59,12 @@ AttnPlan plan_attn(bool bf16, int batch, int hkv, int M, int head_dim, int max_n
     chunk = (chunk + unit - 1) / unit * unit;
     // Both caps are multiples of `unit`.  Verification uses the same plan with
     // and without collection, so the two give bit-identical outputs.
-    const int cap = gather ? vegas::kMaxGatherChunk : vegas::collect_chunk_cap(bf16, head_dim);
+    int cap = gather ? vegas::kMaxGatherChunk : vegas::collect_chunk_cap(bf16, head_dim);
+    if (!gather && page_size > 0) {
+        // a paged split stages its page list in LDS: at most kMaxPagesPerSplit pages
+        const int64_t page_cap = (int64_t)(vegas::kMaxPagesPerSplit - 2) * page_size / unit * unit;
+        if (page_cap < cap) cap = (int)page_cap;
+    }
     if (chunk > cap) chunk = cap;
     p.chunk = chunk;
     p.nsplit = (n + chunk - 1) / chunk;
@@ -106,6 +112,27 @@ bool rows_fit_32bit(const vegas_attn_shape_t* s, int64_t rows) {
     return rows * s->num_kv_heads * s->head_dim * es < (int64_t(1) << 32);
 }
 
+// log2 of the page size of a paged cache descriptor, after validation; -1 for NULL.
+vegas_status_t check_pages(const vegas_paged_kv_t* pages, int32_t batch, int32_t max_seqlen_k, int* shift) {
+    *shift = -1;
+    if (!pages) return VEGAS_OK;
+    const int ps = pages->page_size;
+    if (ps < 1 || ps > vegas::kMaxPageSize || (ps & (ps - 1)) != 0)
+        return fail(VEGAS_ERR_UNSUPPORTED, "page_size %d is not a power of two in 1..%d", ps, vegas::kMaxPageSize);
+    if (!pages->block_table) return fail(VEGAS_ERR_INVALID_ARGUMENT, "block_table is NULL");
+    if (pages->num_pages < 1 || (int64_t)pages->num_pages * ps >= (int64_t(1) << 31))
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "num_pages %d gives an empty or over-long page pool",
+                    pages->num_pages);
+    if ((int64_t)pages->max_pages_per_seq * ps < max_seqlen_k)
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "max_pages_per_seq %d x page_size %d < max_seqlen_k %d",
+                    pages->max_pages_per_seq, ps, max_seqlen_k);
+    (void)batch;
+    int sh = 0;
+    while ((1 << sh) < ps) ++sh;
+    *shift = sh;
+    return VEGAS_OK;
+}
+
 vegas_status_t hip_status(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(VEGAS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
     return VEGAS_OK;
@@ -151,26 +178,36 @@ const char* vegas_status_string(vegas_status_t s) {
 
 const char* vegas_last_error_message(void) { return g_last_error.c_str(); }
 
-vegas_status_t vegas_verify_workspace_size(const vegas_attn_shape_t* shape, int32_t gamma,
-                                           int32_t max_seqlen_k, size_t* bytes) {
+vegas_status_t vegas_verify_paged_workspace_size(const vegas_attn_shape_t* shape, int32_t gamma,
+                                                 int32_t max_seqlen_k, int32_t page_size, size_t* bytes) {
     vegas_status_t st = check_shape(shape);
     if (st != VEGAS_OK) return st;
     if ((st = check_gamma(gamma, shape)) != VEGAS_OK) return st;
     if (!bytes) return fail(VEGAS_ERR_INVALID_ARGUMENT, "bytes is NULL");
     if (max_seqlen_k < gamma + 1)
         return fail(VEGAS_ERR_INVALID_ARGUMENT, "max_seqlen_k %d < gamma+1", max_seqlen_k);
+    if (page_size < 0 || page_size > vegas::kMaxPageSize || (page_size & (page_size - 1)) != 0)
+        return fail(VEGAS_ERR_UNSUPPORTED, "page_size %d is not 0 or a power of two up to %d", page_size,
+                    vegas::kMaxPageSize);
     const int G = shape->num_q_heads / shape->num_kv_heads;
     *bytes = plan_attn(shape->dtype == VEGAS_DTYPE_BF16, shape->batch, shape->num_kv_heads, (gamma + 1) * G,
-                       shape->head_dim,
-                       max_seqlen_k, false).total();
+                       shape->head_dim, max_seqlen_k, false, page_size).total();
     return VEGAS_OK;
 }
 
-vegas_status_t vegas_verify_attn(const vegas_attn_shape_t* shape, int32_t gamma, const void* q,
-                                 const void* k, const void* v, const int32_t* cu_seqlens_k,
-                                 int32_t max_seqlen_k, int32_t total_kv, uint32_t collect_mask,
-                                 float* scores, void* out, void* workspace, size_t workspace_bytes,
-                                 void* stream) {
+vegas_status_t vegas_verify_workspace_size(const vegas_attn_shape_t* shape, int32_t gamma,
+                                           int32_t max_seqlen_k, size_t* bytes) {
+    return vegas_verify_paged_workspace_size(shape, gamma, max_seqlen_k, 0, bytes);
+}
+
+}  // extern "C"
+
+namespace {
+
+vegas_status_t verify_impl(const vegas_attn_shape_t* shape, int32_t gamma, const void* q, const void* k,
+                           const void* v, const vegas_paged_kv_t* pages, const int32_t* cu_seqlens_k,
+                           int32_t max_seqlen_k, int32_t total_kv, uint32_t collect_mask, float* scores,
+                           void* out, void* workspace, size_t workspace_bytes, void* stream) {
     vegas_status_t st = check_shape(shape);
     if (st != VEGAS_OK) return st;
     if ((st = check_gamma(gamma, shape)) != VEGAS_OK) return st;
@@ -188,12 +225,13 @@ vegas_status_t vegas_verify_attn(const vegas_attn_shape_t* shape, int32_t gamma,
         return fail(VEGAS_ERR_INVALID_ARGUMENT, "max_seqlen_k %d < gamma+1 = %d", max_seqlen_k, W);
     if (total_kv < shape->batch * W)
         return fail(VEGAS_ERR_INVALID_ARGUMENT, "total_kv %d < batch*(gamma+1)", total_kv);
-    if (!rows_fit_32bit(shape, max_seqlen_k))
+    int shift = -1;
+    if ((st = check_pages(pages, shape->batch, max_seqlen_k, &shift)) != VEGAS_OK) return st;
+    if (!pages && !rows_fit_32bit(shape, max_seqlen_k))
         return fail(VEGAS_ERR_UNSUPPORTED, "one sequence's K/V rows span 4 GiB or more");
     const int G = shape->num_q_heads / shape->num_kv_heads;
     const AttnPlan plan = plan_attn(shape->dtype == VEGAS_DTYPE_BF16, shape->batch, shape->num_kv_heads, W * G,
-                                    shape->head_dim,
-                                    max_seqlen_k, false);
+                                    shape->head_dim, max_seqlen_k, false, pages ? pages->page_size : 0);
     if (workspace_bytes < plan.total())
         return fail(VEGAS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.total(),
                     workspace_bytes);
@@ -220,9 +258,93 @@ vegas_status_t vegas_verify_attn(const vegas_attn_shape_t* shape, int32_t gamma,
     a.scale = shape->softmax_scale;
     a.scale_log2 = shape->softmax_scale * 1.4426950408889634f;
     a.collect_mask = collect_mask;
+    a.page_shift = shift;
+    if (pages) {
+        a.block_table = pages->block_table;
+        a.max_pages = pages->max_pages_per_seq;
+        a.num_pages = pages->num_pages;
+    }
     return hip_status(vegas::launch_attn(a, shape->dtype == VEGAS_DTYPE_BF16, shape->head_dim, plan.mb,
                                          false, collect_mask != 0u, static_cast<hipStream_t>(stream)),
                       "verify launch");
+}
+
+vegas_status_t decode_impl(const vegas_attn_shape_t* shape, const void* q, const void* k, const void* v,
+                           const vegas_paged_kv_t* pages, const int32_t* cu_seqlens_k, int32_t total_kv,
+                           const int32_t* indices, const int32_t* cu_idx, int32_t max_idx, void* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    size_t need = 0;
+    vegas_status_t st = vegas_sparse_decode_workspace_size(shape, max_idx, &need);
+    if (st != VEGAS_OK) return st;
+    if (!q || !k || !v || !cu_seqlens_k || !cu_idx || !out)
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "q, k, v, cu_seqlens_k, cu_idx and out must be non-NULL");
+    if (max_idx > 0 && !indices) return fail(VEGAS_ERR_INVALID_ARGUMENT, "indices is NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "q, k, v and out must be 16-byte aligned");
+    if (total_kv < 1) return fail(VEGAS_ERR_INVALID_ARGUMENT, "total_kv must be >= 1");
+    int shift = -1;
+    if ((st = check_pages(pages, shape->batch, 1, &shift)) != VEGAS_OK) return st;
+    if (workspace_bytes < need)
+        return fail(VEGAS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+    if (!workspace) return fail(VEGAS_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    const int G = shape->num_q_heads / shape->num_kv_heads;
+    const AttnPlan plan = plan_attn(shape->dtype == VEGAS_DTYPE_BF16, shape->batch, shape->num_kv_heads, G,
+                                    shape->head_dim, max_idx, true);
+    vegas::AttnArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.cu_seqlens_k = cu_seqlens_k;
+    a.indices = indices;
+    a.cu_idx = cu_idx;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(plan.part_o));
+    a.scores = nullptr;
+    a.out = out;
+    a.batch = shape->batch;
+    a.hq = shape->num_q_heads;
+    a.hkv = shape->num_kv_heads;
+    a.G = G;
+    a.W = 1;
+    a.M = G;
+    a.total_kv = total_kv;
+    a.chunk = plan.chunk;
+    a.nsplit = plan.nsplit;
+    a.scale = shape->softmax_scale;
+    a.scale_log2 = shape->softmax_scale * 1.4426950408889634f;
+    a.collect_mask = 0u;
+    a.page_shift = shift;
+    if (pages) {
+        a.block_table = pages->block_table;
+        a.max_pages = pages->max_pages_per_seq;
+        a.num_pages = pages->num_pages;
+    }
+    return hip_status(vegas::launch_attn(a, shape->dtype == VEGAS_DTYPE_BF16, shape->head_dim, plan.mb,
+                                         true, false, static_cast<hipStream_t>(stream)),
+                      "sparse decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+vegas_status_t vegas_verify_attn(const vegas_attn_shape_t* shape, int32_t gamma, const void* q,
+                                 const void* k, const void* v, const int32_t* cu_seqlens_k,
+                                 int32_t max_seqlen_k, int32_t total_kv, uint32_t collect_mask,
+                                 float* scores, void* out, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    return verify_impl(shape, gamma, q, k, v, nullptr, cu_seqlens_k, max_seqlen_k, total_kv, collect_mask,
+                       scores, out, workspace, workspace_bytes, stream);
+}
+
+vegas_status_t vegas_verify_attn_paged(const vegas_attn_shape_t* shape, int32_t gamma, const void* q,
+                                       const void* k, const void* v, const vegas_paged_kv_t* pages,
+                                       const int32_t* cu_seqlens_k, int32_t max_seqlen_k, int32_t total_kv,
+                                       uint32_t collect_mask, float* scores, void* out, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    if (!pages) return fail(VEGAS_ERR_INVALID_ARGUMENT, "pages is NULL");
+    return verify_impl(shape, gamma, q, k, v, pages, cu_seqlens_k, max_seqlen_k, total_kv, collect_mask,
+                       scores, out, workspace, workspace_bytes, stream);
 }
 
 vegas_status_t vegas_select_workspace_size(int32_t batch, int32_t num_kv_heads, int32_t gamma,
@@ -299,47 +421,19 @@ vegas_status_t vegas_sparse_decode_attn(const vegas_attn_shape_t* shape, const v
                                         const int32_t* indices, const int32_t* cu_idx, int32_t max_idx,
                                         void* out, void* workspace, size_t workspace_bytes,
                                         void* stream) {
-    size_t need = 0;
-    vegas_status_t st = vegas_sparse_decode_workspace_size(shape, max_idx, &need);
-    if (st != VEGAS_OK) return st;
-    if (!q || !k || !v || !cu_seqlens_k || !cu_idx || !out)
-        return fail(VEGAS_ERR_INVALID_ARGUMENT, "q, k, v, cu_seqlens_k, cu_idx and out must be non-NULL");
-    if (max_idx > 0 && !indices) return fail(VEGAS_ERR_INVALID_ARGUMENT, "indices is NULL");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-        return fail(VEGAS_ERR_INVALID_ARGUMENT, "q, k, v and out must be 16-byte aligned");
-    if (total_kv < 1) return fail(VEGAS_ERR_INVALID_ARGUMENT, "total_kv must be >= 1");
-    if (workspace_bytes < need)
-        return fail(VEGAS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
-    if (!workspace) return fail(VEGAS_ERR_INVALID_ARGUMENT, "workspace is NULL");
-    const int G = shape->num_q_heads / shape->num_kv_heads;
-    const AttnPlan plan = plan_attn(shape->dtype == VEGAS_DTYPE_BF16, shape->batch, shape->num_kv_heads, G,
-                                    shape->head_dim, max_idx, true);
-    vegas::AttnArgs a{};
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.cu_seqlens_k = cu_seqlens_k;
-    a.indices = indices;
-    a.cu_idx = cu_idx;
-    a.part_o = static_cast<float*>(workspace);
-    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(plan.part_o));
-    a.scores = nullptr;
-    a.out = out;
-    a.batch = shape->batch;
-    a.hq = shape->num_q_heads;
-    a.hkv = shape->num_kv_heads;
-    a.G = G;
-    a.W = 1;
-    a.M = G;
-    a.total_kv = total_kv;
-    a.chunk = plan.chunk;
-    a.nsplit = plan.nsplit;
-    a.scale = shape->softmax_scale;
-    a.scale_log2 = shape->softmax_scale * 1.4426950408889634f;
-    a.collect_mask = 0u;
-    return hip_status(vegas::launch_attn(a, shape->dtype == VEGAS_DTYPE_BF16, shape->head_dim, plan.mb,
-                                         true, false, static_cast<hipStream_t>(stream)),
-                      "sparse decode launch");
+    return decode_impl(shape, q, k, v, nullptr, cu_seqlens_k, total_kv, indices, cu_idx, max_idx, out,
+                       workspace, workspace_bytes, stream);
+}
+
+vegas_status_t vegas_sparse_decode_attn_paged(const vegas_attn_shape_t* shape, const void* q, const void* k,
+                                              const void* v, const vegas_paged_kv_t* pages,
+                                              const int32_t* cu_seqlens_k, int32_t total_kv,
+                                              const int32_t* indices, const int32_t* cu_idx, int32_t max_idx,
+                                              void* out, void* workspace, size_t workspace_bytes,
+                                              void* stream) {
+    if (!pages) return fail(VEGAS_ERR_INVALID_ARGUMENT, "pages is NULL");
+    return decode_impl(shape, q, k, v, pages, cu_seqlens_k, total_kv, indices, cu_idx, max_idx, out,
+                       workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

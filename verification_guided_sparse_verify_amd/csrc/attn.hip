@@ -182,20 +182,31 @@ struct Geo {
 // Per-workgroup constants of the split kernel.  Offsets are 32-bit byte
 // offsets from the first token row of the sequence (the host bounds them).
 struct SplitCtx {
-    const unsigned char* kseq;
-    const unsigned char* vseq;
-    const int* idx_s;     // gather: staged index list of this split
+    const unsigned char* kbase;   // contiguous: the sequence's first K row; paged: the page pool
+    const unsigned char* vbase;
+    const int* idx_s;     // gather: staged rows of this split (positions, or pool rows if paged)
+    const int* page_s;    // paged verification: pool pages of the split's positions
+    int page0;            // paged verification: first page of the split
+    int page_shift;       // log2(page size), or -1 for a contiguous cache
     int row_stride;       // bytes per token row: Hkv * D * element size
     int head_off;         // g * D * element size
     int start, end;       // position range of this split
 };
 
-// Byte offset of the row of position p (clamped into the split).
+// Byte offset from kbase/vbase of the row of position p (clamped into the split).
 template <bool GATHER>
-__device__ __forceinline__ uint32_t row_offset(const SplitCtx& c, int p) {
+__device__ __forceinline__ uint64_t row_offset(const SplitCtx& c, int p) {
     const int pc = min(p, c.end - 1);
-    const int t = GATHER ? c.idx_s[pc - c.start] : pc;
-    return (uint32_t)t * (uint32_t)c.row_stride + (uint32_t)c.head_off;
+    uint32_t row;
+    if constexpr (GATHER) {
+        row = (uint32_t)c.idx_s[pc - c.start];
+    } else if (c.page_shift >= 0) {
+        const uint32_t page = (uint32_t)c.page_s[(pc >> c.page_shift) - c.page0];
+        row = (page << c.page_shift) | ((uint32_t)pc & ((1u << c.page_shift) - 1u));
+    } else {
+        row = (uint32_t)pc;
+    }
+    return (uint64_t)row * (uint32_t)c.row_stride + (uint32_t)c.head_off;
 }
 
 // Copy the K and V rows of the 16 positions from p0 into one ring stage.
@@ -209,20 +220,20 @@ template <class GEO, bool GATHER>
 __device__ __forceinline__ void issue_block(const SplitCtx& c, int p0, int lane, unsigned char* stage) {
     // All row offsets first (in gather mode, LDS reads of the index list that
     // then complete together), then the copies back to back.
-    uint32_t off[GEO::TLD];
+    uint64_t off[GEO::TLD];
 #pragma unroll
     for (int i = 0; i < GEO::TLD; ++i) off[i] = row_offset<GATHER>(c, p0 + i * GEO::RPI + lane / GEO::CPR);
 #pragma unroll
     for (int i = 0; i < GEO::TLD; ++i) {
         const int row = i * GEO::RPI + lane / GEO::CPR;
         const int cc = (lane % GEO::CPR) ^ (row & GEO::KSWZ);
-        copy16_to_lds(c.kseq + off[i] + cc * 16, stage + i * 1024);
+        copy16_to_lds(c.kbase + off[i] + cc * 16, stage + i * 1024);
     }
 #pragma unroll
     for (int i = 0; i < GEO::TLD; ++i) {
         const int row = i * GEO::RPI + lane / GEO::CPR;
         const int cc = (lane % GEO::CPR) ^ (GEO::SWZU * ((row >> 2) & 3));
-        copy16_to_lds(c.vseq + off[i] + cc * 16, stage + GEO::TILE + i * 1024);
+        copy16_to_lds(c.vbase + off[i] + cc * 16, stage + GEO::TILE + i * 1024);
     }
 }
 
@@ -382,6 +393,7 @@ attn_split_kernel(const AttnArgs a) {
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[GEO::MAIN];
     __shared__ int idx_s[GATHER ? kMaxGatherChunk : 1];
+    __shared__ int page_s[GATHER ? 1 : kMaxPagesPerSplit];
     // Collected scores of this split, written to HBM once the split is done.
     __shared__ float score_s[COLLECT ? collect_chunk_cap(BF16, D) : 1];
 
@@ -436,28 +448,54 @@ attn_split_kernel(const AttnArgs a) {
     }
     // Gather mode: stage this split's index list (clamped into the sequence)
     // while the Q loads are in flight.
+    const bool paged = a.page_shift >= 0;
+    const int pmask = paged ? (1 << a.page_shift) - 1 : 0;
+    int page0 = 0;
     if constexpr (GATHER) {
         constexpr int IPT = kMaxGatherChunk / (kAttnWaves * 64);   // indices per thread
         int t[IPT];
 #pragma unroll
         for (int e = 0; e < IPT; ++e) {   // clamped, branch-free: all loads in flight together
             const int i = min(e * kAttnWaves * 64 + (int)threadIdx.x, end - start - 1);
-            t[e] = a.indices[ib0 + start + i];
+            t[e] = min(max(a.indices[ib0 + start + i], 0), n_b - 1);
+        }
+        if (paged) {                      // position -> row of the page pool
+            int pg[IPT];
+#pragma unroll
+            for (int e = 0; e < IPT; ++e)
+                pg[e] = a.block_table[(size_t)b * a.max_pages + min(t[e] >> a.page_shift, a.max_pages - 1)];
+#pragma unroll
+            for (int e = 0; e < IPT; ++e)
+                t[e] = (min(max(pg[e], 0), a.num_pages - 1) << a.page_shift) | (t[e] & pmask);
         }
 #pragma unroll
         for (int e = 0; e < IPT; ++e) {
             const int i = e * kAttnWaves * 64 + threadIdx.x;
-            if (i < end - start) idx_s[i] = min(max(t[e], 0), n_b - 1);
+            if (i < end - start) idx_s[i] = t[e];
         }
         __syncthreads();
+    } else {
+        if (paged) {                      // the pool pages of positions start .. end-1
+            page0 = start >> a.page_shift;
+            const int npg = min(((end - 1) >> a.page_shift) - page0 + 1, kMaxPagesPerSplit);
+            for (int i = threadIdx.x; i < npg; i += blockDim.x) {
+                const int pg = a.block_table[(size_t)b * a.max_pages + min(page0 + i, a.max_pages - 1)];
+                page_s[i] = min(max(pg, 0), a.num_pages - 1);
+            }
+            __syncthreads();
+        }
     }
 
     SplitCtx c;
     c.row_stride = a.hkv * D * GEO::ES;
     c.head_off = g * D * GEO::ES;
-    c.kseq = static_cast<const unsigned char*>(a.k) + (size_t)seq0 * c.row_stride;
-    c.vseq = static_cast<const unsigned char*>(a.v) + (size_t)seq0 * c.row_stride;
+    const size_t first = paged ? 0 : (size_t)seq0 * c.row_stride;
+    c.kbase = static_cast<const unsigned char*>(a.k) + first;
+    c.vbase = static_cast<const unsigned char*>(a.v) + first;
     c.idx_s = idx_s;
+    c.page_s = page_s;
+    c.page0 = page0;
+    c.page_shift = GATHER ? -1 : a.page_shift;
     c.start = start;
     c.end = end;
 

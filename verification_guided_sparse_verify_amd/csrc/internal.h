@@ -17,17 +17,20 @@ constexpr int kAttnStages = 2;
 // Longest position range one workgroup takes in gather mode: its index list
 // is staged in LDS.
 constexpr int kMaxGatherChunk = 2048;
+// Paged KV cache: pool pages of one verification split, staged in LDS.
+constexpr int kMaxPagesPerSplit = 2048;
+constexpr int kMaxPageSize = 256;
 
 // Bytes of one workgroup's K/V ring.
 __host__ __device__ constexpr int attn_ring_bytes(bool bf16, int head_dim) {
     return kAttnWaves * kAttnStages * 2 * kAttnBlock * head_dim * (bf16 ? 2 : 4);
 }
 // Longest position range one workgroup takes in verification: the collected
-// scores of its range are buffered in LDS next to the ring (150 KB in all of
-// the 160 KB), at most 16896 positions, a multiple of kAttnWaves*kAttnBlock.
+// scores of its range are buffered in LDS next to the ring (144 KB in all of
+// the 160 KB, leaving room for a paged cache's page list), at most 16896 positions, a multiple of kAttnWaves*kAttnBlock.
 __host__ __device__ constexpr int collect_chunk_cap(bool bf16, int head_dim) {
-    return ((150 * 1024 - attn_ring_bytes(bf16, head_dim)) / 4 / 64 * 64) < 16896
-               ? (150 * 1024 - attn_ring_bytes(bf16, head_dim)) / 4 / 64 * 64
+    return ((144 * 1024 - attn_ring_bytes(bf16, head_dim)) / 4 / 64 * 64) < 16896
+               ? (144 * 1024 - attn_ring_bytes(bf16, head_dim)) / 4 / 64 * 64
                : 16896;
 }
 
@@ -52,6 +55,12 @@ struct AttnArgs {
     float scale;                   // softmax scale s
     float scale_log2;              // s * log2(e)
     uint32_t collect_mask;
+    // Paged KV cache (page_shift >= 0): k, v are pools [num_pages, page size, hkv, D];
+    // position t of sequence b is row t % page of pool page block_table[b*max_pages + t/page].
+    const int32_t* block_table;
+    int32_t max_pages;
+    int32_t num_pages;
+    int32_t page_shift;            // log2(page size); -1: contiguous varlen cache
 };
 
 hipError_t launch_attn(const AttnArgs& a, bool bf16, int head_dim, int mblocks, bool gather,

@@ -22,9 +22,14 @@ class LayerStep:
 
     def __init__(self, inputs: dict, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                  gamma: int, seqlens, k_per_seq, softmax_scale: float, n_drafts: int | None = None,
-                 collect_mask: int | None = None):
+                 collect_mask: int | None = None, paged: dict | None = None):
         self.inp = inputs
         self.gamma = gamma
+        # paged: a page pool from workloads.page_cache (k_pool, v_pool, block_table, num_pages); the
+        # paged entry points then read K/V through the block table.
+        self.paged = paged
+        self.page_size = paged["k_pool"].shape[1] if paged else 0
+        self.pages = V.paged_kv(paged["block_table"], self.page_size, paged["num_pages"]) if paged else None
         q = inputs["q"]
         dev = q.device
         dtype = V.VEGAS_DTYPE_BF16 if q.dtype == torch.bfloat16 else V.VEGAS_DTYPE_F32
@@ -40,7 +45,7 @@ class LayerStep:
         self.scores = torch.empty(num_kv_heads, self.total_kv, dtype=torch.float32, device=dev)
         self.indices = torch.empty(max(self.total_k, 1), dtype=torch.int32, device=dev)
         self.draft_out = torch.empty(max(self.n_drafts, 1), batch, num_q_heads, head_dim, dtype=q.dtype, device=dev)
-        ws = max(V.vegas_verify_workspace_size(self.shape, gamma, self.max_seqlen),
+        ws = max(V.vegas_verify_paged_workspace_size(self.shape, gamma, self.max_seqlen, self.page_size),
                  V.vegas_select_workspace_size(batch, num_kv_heads, gamma, self.max_seqlen, self.total_kv),
                  V.vegas_sparse_decode_workspace_size(self.shape, self.max_k))
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
@@ -51,9 +56,14 @@ class LayerStep:
 
     def verify(self, collect: bool = True, stream=None):
         i = self.inp
+        mask, scores = (self.collect_mask, self.scores) if collect else (0, None)
+        if self.paged:
+            V.vegas_verify_attn_paged(self.shape, self.gamma, i["q"], self.paged["k_pool"], self.paged["v_pool"],
+                                      self.pages, i["cu_seqlens_k"], self.max_seqlen, self.total_kv, mask, scores,
+                                      self.out, self.workspace, stream)
+            return
         V.vegas_verify_attn(self.shape, self.gamma, i["q"], i["k"], i["v"], i["cu_seqlens_k"], self.max_seqlen,
-                            self.total_kv, self.collect_mask if collect else 0,
-                            self.scores if collect else None, self.out, self.workspace, stream)
+                            self.total_kv, mask, scores, self.out, self.workspace, stream)
 
     def select(self, stream=None):
         i = self.inp
@@ -62,6 +72,11 @@ class LayerStep:
 
     def draft(self, j: int, stream=None):
         i = self.inp
+        if self.paged:
+            V.vegas_sparse_decode_attn_paged(self.shape, i["draft_q"][j], self.paged["k_pool"], self.paged["v_pool"],
+                                             self.pages, i["cu_seqlens_k"], self.total_kv, self.indices, i["cu_k"],
+                                             self.max_k, self.draft_out[j], self.workspace, stream)
+            return
         V.vegas_sparse_decode_attn(self.shape, i["draft_q"][j], i["k"], i["v"], i["cu_seqlens_k"], self.total_kv,
                                    self.indices, i["cu_k"], self.max_k, self.draft_out[j], self.workspace, stream)
 
@@ -87,18 +102,28 @@ class LayerStep:
                     V._check(rc, name)
             return go
 
-        common = (shape, self.gamma, i["q"].data_ptr(), i["k"].data_ptr(), i["v"].data_ptr(),
-                  i["cu_seqlens_k"].data_ptr(), self.max_seqlen, self.total_kv)
-        verify = call(L.vegas_verify_attn, "vegas_verify_attn",
-                      common + (self.collect_mask, self.scores.data_ptr(), self.out.data_ptr(), ws, wsb, st))
-        plain = call(L.vegas_verify_attn, "vegas_verify_attn",
-                     common + (0, None, self.out.data_ptr(), ws, wsb, st))
+        if self.paged:
+            kp, vp = self.paged["k_pool"].data_ptr(), self.paged["v_pool"].data_ptr()
+            pages = ctypes.byref(self.pages)
+            vfn, vname = L.vegas_verify_attn_paged, "vegas_verify_attn_paged"
+            common = (shape, self.gamma, i["q"].data_ptr(), kp, vp, pages, i["cu_seqlens_k"].data_ptr(),
+                      self.max_seqlen, self.total_kv)
+            dfn, dname = L.vegas_sparse_decode_attn_paged, "vegas_sparse_decode_attn_paged"
+            kv = (kp, vp, pages)
+        else:
+            vfn, vname = L.vegas_verify_attn, "vegas_verify_attn"
+            common = (shape, self.gamma, i["q"].data_ptr(), i["k"].data_ptr(), i["v"].data_ptr(),
+                      i["cu_seqlens_k"].data_ptr(), self.max_seqlen, self.total_kv)
+            dfn, dname = L.vegas_sparse_decode_attn, "vegas_sparse_decode_attn"
+            kv = (i["k"].data_ptr(), i["v"].data_ptr())
+        verify = call(vfn, vname, common + (self.collect_mask, self.scores.data_ptr(), self.out.data_ptr(), ws, wsb, st))
+        plain = call(vfn, vname, common + (0, None, self.out.data_ptr(), ws, wsb, st))
         select = call(L.vegas_select_topk, "vegas_select_topk",
                       (self.batch, self.hkv, self.gamma, self.scores.data_ptr(), i["cu_seqlens_k"].data_ptr(),
                        self.max_seqlen, self.total_kv, i["cu_k"].data_ptr(), self.indices.data_ptr(), ws, wsb, st))
-        drafts = [call(L.vegas_sparse_decode_attn, "vegas_sparse_decode_attn",
-                       (shape, i["draft_q"][j].data_ptr(), i["k"].data_ptr(), i["v"].data_ptr(),
-                        i["cu_seqlens_k"].data_ptr(), self.total_kv, self.indices.data_ptr(), i["cu_k"].data_ptr(),
+        drafts = [call(dfn, dname,
+                       (shape, i["draft_q"][j].data_ptr()) + kv +
+                       (i["cu_seqlens_k"].data_ptr(), self.total_kv, self.indices.data_ptr(), i["cu_k"].data_ptr(),
                         self.max_k, self.draft_out[j].data_ptr(), ws, wsb, st))
                   for j in range(self.n_drafts)]
         return verify, plain, select, drafts

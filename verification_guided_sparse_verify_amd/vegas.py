@@ -28,6 +28,7 @@ EXPORTED = (
     "vegas_verify_workspace_size", "vegas_verify_attn",
     "vegas_select_workspace_size", "vegas_select_topk",
     "vegas_sparse_decode_workspace_size", "vegas_sparse_decode_attn",
+    "vegas_verify_paged_workspace_size", "vegas_verify_attn_paged", "vegas_sparse_decode_attn_paged",
 )
 
 
@@ -44,6 +45,12 @@ class AttnShape(ctypes.Structure):
                 ("softmax_scale", ctypes.c_float)]
 
 
+class PagedKV(ctypes.Structure):
+    """vegas_paged_kv_t."""
+    _fields_ = [("block_table", ctypes.c_void_p), ("max_pages_per_seq", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -55,6 +62,7 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         P, I32, U32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
         SP = ctypes.POINTER(AttnShape)
+        PP = ctypes.POINTER(PagedKV)
         PSZ = ctypes.POINTER(ctypes.c_size_t)
         sig = {
             "vegas_abi_version": ([], I32),
@@ -66,6 +74,9 @@ def lib():
             "vegas_select_topk": ([I32, I32, I32, P, P, I32, I32, P, P, P, SZ, P], ctypes.c_int),
             "vegas_sparse_decode_workspace_size": ([SP, I32, PSZ], ctypes.c_int),
             "vegas_sparse_decode_attn": ([SP, P, P, P, P, I32, P, P, I32, P, P, SZ, P], ctypes.c_int),
+            "vegas_verify_paged_workspace_size": ([SP, I32, I32, I32, PSZ], ctypes.c_int),
+            "vegas_verify_attn_paged": ([SP, I32, P, P, P, PP, P, I32, I32, U32, P, P, P, SZ, P], ctypes.c_int),
+            "vegas_sparse_decode_attn_paged": ([SP, P, P, P, PP, P, I32, P, P, I32, P, P, SZ, P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -160,3 +171,34 @@ def vegas_sparse_decode_attn(shape: AttnShape, q, k, v, cu_seqlens_k, total_kv: 
                                           total_kv, _ptr(indices), _ptr(cu_idx), max_idx, _ptr(out),
                                           _ptr(workspace), _nbytes(workspace), _stream(stream)),
            "vegas_sparse_decode_attn")
+
+
+def paged_kv(block_table, page_size: int, num_pages: int) -> PagedKV:
+    """block_table: device int32 tensor [batch, max_pages_per_seq]."""
+    return PagedKV(_ptr(block_table), block_table.shape[1], page_size, num_pages)
+
+
+def vegas_verify_paged_workspace_size(shape: AttnShape, gamma: int, max_seqlen_k: int, page_size: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().vegas_verify_paged_workspace_size(ctypes.byref(shape), gamma, max_seqlen_k, page_size,
+                                                   ctypes.byref(n)),
+           "vegas_verify_paged_workspace_size")
+    return n.value
+
+
+def vegas_verify_attn_paged(shape: AttnShape, gamma: int, q, k, v, pages: PagedKV, cu_seqlens_k,
+                            max_seqlen_k: int, total_kv: int, collect_mask: int, scores, out, workspace,
+                            stream=None) -> None:
+    _check(lib().vegas_verify_attn_paged(ctypes.byref(shape), gamma, _ptr(q), _ptr(k), _ptr(v), ctypes.byref(pages),
+                                         _ptr(cu_seqlens_k), max_seqlen_k, total_kv, collect_mask & 0xFFFFFFFF,
+                                         _ptr(scores), _ptr(out), _ptr(workspace), _nbytes(workspace),
+                                         _stream(stream)),
+           "vegas_verify_attn_paged")
+
+
+def vegas_sparse_decode_attn_paged(shape: AttnShape, q, k, v, pages: PagedKV, cu_seqlens_k, total_kv: int, indices,
+                                   cu_idx, max_idx: int, out, workspace, stream=None) -> None:
+    _check(lib().vegas_sparse_decode_attn_paged(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(pages),
+                                                _ptr(cu_seqlens_k), total_kv, _ptr(indices), _ptr(cu_idx), max_idx,
+                                                _ptr(out), _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "vegas_sparse_decode_attn_paged")

@@ -235,3 +235,42 @@ def host_bits(t: torch.Tensor):
     if t.dtype == torch.int32:
         return t.numpy()
     raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def page_cache(wl: Workload, inp: dict, page_size: int, seed: int = 0, spare_pages: int = 3,
+               drop_contiguous: bool = False) -> dict:
+    """Lay the contiguous K/V of `inp` out as a paged cache: the token rows of every sequence
+    are cut into pages of `page_size` rows and the pages are scattered over a randomly
+    permuted page pool (with a few unused pages).  A data layout only: no values change.
+
+    Returns {"k_pool", "v_pool": [num_pages, page_size, Hkv, D], "block_table": int32
+    [batch, max_pages] (unused slots point at pool page 0), "num_pages"}.
+    """
+    k, v = inp["k"], inp["v"]
+    dev = k.device
+    cu = wl.cu_seqlens()
+    lens = wl.seqlens
+    per = [(n + page_size - 1) // page_size for n in lens]
+    maxp = max(per)
+    num_pages = sum(per) + spare_pages
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed * 7919 + page_size)
+    perm = torch.randperm(num_pages, generator=g)
+    Hkv, D = k.shape[1], k.shape[2]
+    out = {"num_pages": num_pages}
+    bt = torch.zeros(wl.batch, maxp, dtype=torch.int32)
+    used = 0
+    for b in range(wl.batch):
+        bt[b, : per[b]] = perm[used: used + per[b]].to(torch.int32)
+        used += per[b]
+    out["block_table"] = bt.to(dev)
+    for name, src in (("k", k), ("v", v)):
+        pool = torch.zeros(num_pages * page_size, Hkv, D, dtype=src.dtype, device=dev)
+        for b in range(wl.batch):
+            t = torch.arange(lens[b], device=dev)
+            rows = out["block_table"][b].long()[t // page_size] * page_size + t % page_size
+            pool.index_copy_(0, rows, src[cu[b]: cu[b + 1]])
+        out[name + "_pool"] = pool.view(num_pages, page_size, Hkv, D)
+        if drop_contiguous:
+            inp[name] = None
+    return out
