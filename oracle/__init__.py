@@ -50,6 +50,10 @@ def _lib():
         U32 = ctypes.c_uint32
         lib.vo_verify_attn.argtypes = [I, I, I, I, I, I, D, P, P, P, P, I64, U32, P, P]
         lib.vo_verify_attn.restype = I
+        lib.vo_verify_attn_local.argtypes = [I, I, I, I, I, I, D, P, P, P, P, I64, I, U32, P, P]
+        lib.vo_verify_attn_local.restype = I
+        lib.vo_streaming_indices.argtypes = [I, I, I, P, P, P]
+        lib.vo_streaming_indices.restype = I
         lib.vo_select_topk.argtypes = [I, I, I, P, P, I64, P, P, P, P]
         lib.vo_select_topk.restype = I
         lib.vo_sparse_decode_attn.argtypes = [I, I, I, I, I, D, P, P, P, P, P, P, P]
@@ -75,11 +79,12 @@ def _c(a, dtype=None):
 
 
 def verify_attn(q, k, v, cu_seqlens_k, gamma: int, scale: float,
-                collect_mask: int | None = None, want_scores: bool = True):
+                collect_mask: int | None = None, want_scores: bool = True, window: int = 0):
     """Verification attention over the gamma+1 new rows of each sequence.
 
     q: [batch*(gamma+1), Hq, D]; k, v: [total_kv, Hkv, D]; cu_seqlens_k: [batch+1].
-    collect_mask defaults to the Collect-2-Query rows {0, gamma}.
+    collect_mask defaults to the Collect-2-Query rows {0, gamma}.  window > 0 applies a local
+    mask (row r sees the `window` newest keys up to its position) and needs want_scores=False.
     Returns (out float64 [batch*(gamma+1), Hq, D], scores float64 [Hkv, total_kv] or None).
     """
     q, k, v = _c(q), _c(k), _c(v)
@@ -94,9 +99,9 @@ def verify_attn(q, k, v, cu_seqlens_k, gamma: int, scale: float,
         collect_mask = (1 | (1 << gamma))
     out = np.zeros(q.shape, dtype=np.float64)
     scores = np.zeros((hkv, total), dtype=np.float64) if want_scores else None
-    rc = _lib().vo_verify_attn(code, batch, hq, hkv, d, gamma, float(scale),
-                               _ptr(q), _ptr(k), _ptr(v), _ptr(cu), total,
-                               collect_mask & 0xFFFFFFFF, _ptr(out), _ptr(scores))
+    rc = _lib().vo_verify_attn_local(code, batch, hq, hkv, d, gamma, float(scale),
+                                     _ptr(q), _ptr(k), _ptr(v), _ptr(cu), total, int(window),
+                                     collect_mask & 0xFFFFFFFF, _ptr(out), _ptr(scores))
     if rc != 0:
         raise ValueError("vo_verify_attn rejected its arguments")
     return out, scores
@@ -143,3 +148,14 @@ def sparse_decode_attn(q, k, v, cu_seqlens_k, indices, cu_idx, scale: float):
     if rc != 0:
         raise ValueError("vo_sparse_decode_attn rejected its arguments")
     return out
+
+
+def streaming_indices(cu_seqlens_k, gamma: int, sinks: int, cu_idx):
+    """Sink-plus-recent lists with per-sequence budgets cu_idx; returns int32 [cu_idx[-1]]."""
+    cu = _c(cu_seqlens_k, np.int32)
+    cui = _c(cu_idx, np.int32)
+    out = np.zeros(max(int(cui[-1]), 1), dtype=np.int32)
+    rc = _lib().vo_streaming_indices(cu.shape[0] - 1, gamma, sinks, _ptr(cu), _ptr(cui), _ptr(out))
+    if rc != 0:
+        raise ValueError("vo_streaming_indices rejected its arguments")
+    return out[: int(cui[-1])]

@@ -76,8 +76,26 @@ int vo_verify_attn(int dtype, int batch, int num_q_heads, int num_kv_heads,
                    const void* q, const void* k, const void* v,
                    const int32_t* cu_seqlens_k, int64_t total_kv,
                    uint32_t collect_mask, double* out, double* scores) {
+    return vo_verify_attn_local(dtype, batch, num_q_heads, num_kv_heads, head_dim, gamma, scale, q, k, v,
+                                cu_seqlens_k, total_kv, 0, collect_mask, out, scores);
+}
+
+/*
+ * The same with an optional local (banded) mask, the "local masking" the
+ * page's sec. 4 names beside the causal one (gpt-oss alternates banded and
+ * dense layers, sec. 5.1): with window > 0, row r sees only the `window`
+ * newest keys up to its own position, L_b + r - window < j <= L_b + r.
+ * Collection under a local mask is not defined here (the pages select only
+ * in dense layers): scores must be NULL or collect_mask 0 when window > 0.
+ */
+int vo_verify_attn_local(int dtype, int batch, int num_q_heads, int num_kv_heads,
+                         int head_dim, int gamma, double scale,
+                         const void* q, const void* k, const void* v,
+                         const int32_t* cu_seqlens_k, int64_t total_kv, int window,
+                         uint32_t collect_mask, double* out, double* scores) {
     if (!shape_ok(dtype, batch, num_q_heads, num_kv_heads, head_dim)) return -1;
     if (gamma < 0 || gamma > 31 || !cu_seqlens_k || !out) return -1;
+    if (window < 0 || (window > 0 && scores && collect_mask)) return -1;
     const int W = gamma + 1;
     const int G = num_q_heads / num_kv_heads;
     if (cu_seqlens_k[0] != 0 || cu_seqlens_k[batch] != total_kv) return -1;
@@ -105,9 +123,11 @@ int vo_verify_attn(int dtype, int batch, int num_q_heads, int num_kv_heads,
             const int h = g * G + hl;
             for (int r = 0; r < W; ++r) {
                 const int64_t q_off = ((int64_t)b * W + r) * q_row + (int64_t)h * head_dim;
-                const int64_t visible = L + r + 1;   /* keys 0 .. L+r */
+                /* keys first .. L+r: all of them, or the last `window` under a local mask */
+                const int64_t first = (window > 0 && L + r + 1 > window) ? L + r + 1 - window : 0;
+                const int64_t visible = L + r + 1 - first;
                 for (int64_t j = 0; j < visible; ++j) {
-                    rows[j] = (start + j) * kv_row + (int64_t)g * head_dim;
+                    rows[j] = (start + first + j) * kv_row + (int64_t)g * head_dim;
                     z[j] = scale * dot_rows(q, q_off, k, rows[j], dtype, head_dim);
                 }
                 softmax_weighted_sum(z, rows, visible, v, dtype, head_dim,
@@ -232,6 +252,29 @@ int vo_sparse_decode_attn(int dtype, int batch, int num_q_heads,
         softmax_weighted_sum(z, rows, n, v, dtype, head_dim, o);
         free(z);
         free(rows);
+    }
+    return 0;
+}
+
+/*
+ * StreamingLLM-style query-agnostic lists (the "MagicDec-Stream" baseline the
+ * page's sec. 5.1 compares against; sec. 2.2 describes the sink-plus-recent
+ * pattern): with a budget of k_b positions, sequence b's list is the first
+ * min(sinks, k_b) prefix positions followed by the most recent remaining
+ * ones, ascending, no duplicates, all inside the prefix [0, L_b).
+ */
+int vo_streaming_indices(int batch, int gamma, int sinks, const int32_t* cu_seqlens_k,
+                         const int32_t* cu_idx, int32_t* indices) {
+    if (batch < 0 || gamma < 0 || gamma > 31 || sinks < 0 || !cu_seqlens_k || !cu_idx) return -1;
+    const int W = gamma + 1;
+    for (int b = 0; b < batch; ++b) {
+        const int64_t L = (int64_t)cu_seqlens_k[b + 1] - cu_seqlens_k[b] - W;
+        const int64_t kb = (int64_t)cu_idx[b + 1] - cu_idx[b];
+        if (L < 0 || kb < 0 || kb > L) return -1;
+        int32_t* dst = indices + cu_idx[b];
+        const int64_t ns = sinks < kb ? sinks : kb;
+        for (int64_t j = 0; j < ns; ++j) dst[j] = (int32_t)j;
+        for (int64_t j = ns; j < kb; ++j) dst[j] = (int32_t)(L - (kb - j));
     }
     return 0;
 }

@@ -53,6 +53,22 @@ int vo_verify_attn(int dtype, int batch, int num_q_heads, int num_kv_heads,
                    const int32_t* cu_seqlens_k, int64_t total_kv,
                    uint32_t collect_mask, double* out, double* scores);
 
+/* As vo_verify_attn, with an optional local mask: window > 0 limits row r
+ * to the keys L_b + r - window < j <= L_b + r.  Collection must be off
+ * (scores NULL or collect_mask 0) when window > 0. */
+int vo_verify_attn_local(int dtype, int batch, int num_q_heads, int num_kv_heads,
+                         int head_dim, int gamma, double scale,
+                         const void* q, const void* k, const void* v,
+                         const int32_t* cu_seqlens_k, int64_t total_kv, int window,
+                         uint32_t collect_mask, double* out, double* scores);
+
+/* Query-agnostic sink-plus-recent lists with a budget of
+ * k_b = cu_idx[b+1] - cu_idx[b] <= L_b positions: the first min(sinks, k_b)
+ * prefix positions, then the k_b - min(sinks, k_b) most recent ones
+ * (ending at L_b - 1), ascending. */
+int vo_streaming_indices(int batch, int gamma, int sinks, const int32_t* cu_seqlens_k,
+                         const int32_t* cu_idx, int32_t* indices);
+
 /* Exact top-k of the score summed over KV heads, per sequence.
  * S_b[i] = sum_g scores[g, cu_seqlens_k[b] + i] for i < L_b.  The k_b
  * (= cu_k[b+1] - cu_k[b]) positions with the largest S_b are written to

@@ -327,3 +327,86 @@ def test_oracle_rejects_bad_arguments():
         oracle.sparse_decode_attn(q[:1], k, v, cu, np.array([12], np.int32), [0, 1], scale=1.0)
     with pytest.raises(ValueError):
         oracle.verify_attn(q, k, v, [0, 1], 1, scale=1.0)    # sequence shorter than gamma+1
+
+
+# ---------------------------------------------------------------- local mask and StreamingLLM lists
+
+def band_sdpa_reference(q, k, v, cu, gamma, scale, hq, hkv, window):
+    """torch fp64 SDPA with an explicit band mask: row r sees L+r-window < j <= L+r."""
+    W = gamma + 1
+    G = hq // hkv
+    outs = []
+    for b in range(len(cu) - 1):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        n = s1 - s0
+        L = n - W
+        qb = torch.from_numpy(as_f64(q[b * W:(b + 1) * W])).permute(1, 0, 2)
+        kb = torch.from_numpy(as_f64(k[s0:s1])).permute(1, 0, 2).repeat_interleave(G, 0)
+        vb = torch.from_numpy(as_f64(v[s0:s1])).permute(1, 0, 2).repeat_interleave(G, 0)
+        j = torch.arange(n)[None, :]
+        last = (L + torch.arange(W))[:, None]
+        mask = (j <= last) & (j > last - window)
+        o = torch.nn.functional.scaled_dot_product_attention(qb, kb, vb, attn_mask=mask, scale=scale)
+        outs.append(o.permute(1, 0, 2).numpy())
+    return np.concatenate(outs, axis=0)
+
+
+@pytest.mark.parametrize("window", [1, 3, 17, 128])
+def test_local_mask_matches_torch_band_sdpa(window):
+    gamma, hq, hkv, d = 3, 8, 2, 32
+    q, k, v, cu = rand_case(18, 3, hq, hkv, d, gamma, [200, 5, 60], "bf16")
+    out, sc = oracle.verify_attn(q, k, v, cu, gamma, scale=0.2, want_scores=False, window=window)
+    assert sc is None
+    ref = band_sdpa_reference(q, k, v, cu, gamma, 0.2, hq, hkv, window)
+    assert np.abs(out - ref).max() < 1e-12
+
+
+def test_window_one_sees_only_its_own_key():
+    gamma = 4
+    q, k, v, cu = rand_case(19, 2, 4, 2, 16, gamma, [30, 0])
+    out, _ = oracle.verify_attn(q, k, v, cu, gamma, scale=1.0, want_scores=False, window=1)
+    W = gamma + 1
+    for b in range(2):
+        L = int(cu[b + 1] - cu[b]) - W
+        for r in range(W):
+            for h in range(4):
+                assert np.array_equal(out[b * W + r, h], v[cu[b] + L + r, h // 2].astype(np.float64))
+
+
+def test_local_mask_boundary():
+    """Keys before the band do not matter; the first key inside it does."""
+    gamma, L, window = 2, 50, 8
+    q, k, v, cu = rand_case(20, 1, 2, 1, 8, gamma, [L])
+    base, _ = oracle.verify_attn(q, k, v, cu, gamma, scale=0.5, want_scores=False, window=window)
+    for r in range(gamma + 1):
+        lo = L + r - window + 1
+        k2, v2 = k.copy(), v.copy()
+        k2[:lo] += 3.0
+        v2[:lo] -= 2.0
+        o2, _ = oracle.verify_attn(q, k2, v2, cu, gamma, scale=0.5, want_scores=False, window=window)
+        assert np.array_equal(o2[r], base[r])
+        k3 = k.copy()
+        k3[lo] += 1.0
+        o3, _ = oracle.verify_attn(q, k3, v, cu, gamma, scale=0.5, want_scores=False, window=window)
+        assert not np.allclose(o3[r], base[r], atol=1e-9)
+
+
+def test_local_mask_rejects_collection():
+    q, k, v, cu = rand_case(21, 1, 2, 1, 8, 1, [20])
+    with pytest.raises(ValueError):
+        oracle.verify_attn(q, k, v, cu, 1, scale=1.0, window=4)
+
+
+def test_streaming_lists_closed_form():
+    gamma = 2
+    lens = [100 + 3, 10 + 3, 7 + 3]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    budgets = [12, 10, 0]
+    cui = np.concatenate([[0], np.cumsum(budgets)]).astype(np.int32)
+    got = oracle.streaming_indices(cu, gamma, 4, cui)
+    assert got[:12].tolist() == [0, 1, 2, 3] + list(range(92, 100))
+    assert got[12:22].tolist() == list(range(10))          # budget = whole prefix
+    got = oracle.streaming_indices(cu, gamma, 0, cui)
+    assert got[:12].tolist() == list(range(88, 100))       # no sinks: pure sliding window
+    with pytest.raises(ValueError):
+        oracle.streaming_indices(cu, gamma, 4, np.array([0, 101, 101, 101], np.int32))
