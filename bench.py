@@ -192,6 +192,9 @@ def main():
     ap.add_argument("--page-size", type=int, default=0,
                     help="keep every layer's KV cache as a randomly permuted page pool of this page size and "
                          "run the paged entry points (0: contiguous cache)")
+    ap.add_argument("--selection", choices=("vegas", "streaming"), default="vegas",
+                    help="vegas: verification-guided selection (the method); streaming: query-agnostic "
+                         "sinks + recent tokens with the same budget, no collection (a baseline)")
     ap.add_argument("--collect-sweep", action="store_true",
                     help="only time verification of one layer with collection off, Collect-2-Query and "
                          "all rows, over gamma")
@@ -224,7 +227,7 @@ def main():
         return
     layers = args.layers if args.layers is not None else wl.layers
     dev = "cuda:0"
-    cpu_leg = not args.no_cpu_baseline and not args.page_size
+    cpu_leg = not args.no_cpu_baseline and not args.page_size and args.selection == "vegas"
     t_gen = time.perf_counter()
     layer_inputs, steps = [], []
     for layer in range(layers):
@@ -234,7 +237,8 @@ def main():
             paged = W.page_cache(wl, inp, args.page_size, seed=layer, drop_contiguous=True)
         layer_inputs.append(inp)
         steps.append(LayerStep(inp, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.gamma,
-                               wl.seqlens, wl.k_per_seq, wl.scale, n_drafts=wl.n_drafts, paged=paged))
+                               wl.seqlens, wl.k_per_seq, wl.scale, n_drafts=wl.n_drafts, paged=paged,
+                               selection=args.selection))
         if layer % 6 == 5:
             torch.cuda.synchronize()
             print(f"# generated layer {layer + 1}/{layers}", file=sys.stderr, flush=True)
@@ -329,6 +333,8 @@ def main():
             "order": "verify+select over all layers, then gamma drafting passes over all layers",
             "kv_cache": (f"paged, {args.page_size}-token pages in a randomly permuted pool" if args.page_size
                          else "contiguous varlen"),
+            "selection": ("verification-guided (Collect-2-Query + exact top-k)" if args.selection == "vegas"
+                          else "query-agnostic: 4 sinks + most recent tokens, same k, no collection"),
         },
         "layer_step_gbps": round(step_gbps, 1),
         "layer_step_frac_of_peak": round(step_gbps / PEAK_HBM_GBPS, 4),

@@ -219,6 +219,43 @@ vegas_status_t vegas_sparse_decode_attn_paged(const vegas_attn_shape_t* shape, c
                                               int32_t max_idx, void* out, void* workspace,
                                               size_t workspace_bytes, void* stream);
 
+/*
+ * Local (banded) verification attention.
+ * The page's sec. 4 takes logits "after causal or local masking"; gpt-oss
+ * alternates banded and dense attention layers and Vegas drafts sparsely only
+ * in the dense ones (sec. 5.1).  This entry point computes the banded layers'
+ * verification: row r of sequence b attends to keys j with
+ * L_b + r - window < j <= L_b + r, and only those keys are read.  Arguments as
+ * for vegas_verify_attn; there is no collection (nothing is selected in a
+ * banded layer).  window >= 1.
+ */
+vegas_status_t vegas_verify_local_workspace_size(const vegas_attn_shape_t* shape, int32_t gamma,
+                                                 int32_t max_seqlen_k, int32_t window, size_t* bytes);
+vegas_status_t vegas_verify_attn_local(const vegas_attn_shape_t* shape, int32_t gamma,
+                                       const void* q, const void* k, const void* v,
+                                       const int32_t* cu_seqlens_k, int32_t max_seqlen_k,
+                                       int32_t total_kv, int32_t window, void* out,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Query-agnostic index lists: attention sinks plus the most recent tokens
+ * (the StreamingLLM selection behind the MagicDec-Stream baseline of the
+ * page's sec. 5.1, described in sec. 2.2).  With the same budget k_b as Vegas'
+ * selection they feed vegas_sparse_decode_attn unchanged.
+ *
+ *  cu_idx       device int32 [batch+1]: budget k_b = cu_idx[b+1] - cu_idx[b]
+ *               <= L_b (larger budgets are clamped to L_b and the extra slots
+ *               repeat the last position).
+ *  total_idx    host scalar = cu_idx[batch].
+ *  indices      device int32 [total_idx]: sequence b gets the positions
+ *               0 .. min(sinks, k_b)-1, then L_b - (k_b - min(sinks, k_b)) ..
+ *               L_b - 1, ascending.
+ */
+vegas_status_t vegas_streaming_indices(int32_t batch, int32_t gamma, int32_t sinks,
+                                       const int32_t* cu_seqlens_k, int32_t total_kv,
+                                       const int32_t* cu_idx, int32_t total_idx, int32_t* indices,
+                                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

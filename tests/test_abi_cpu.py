@@ -164,3 +164,19 @@ def test_paged_argument_errors(V):
     assert L.vegas_sparse_decode_attn_paged(ctypes.byref(s), FAKE, FAKE, FAKE,
                                             ctypes.byref(V.PagedKV(FAKE, 4, 128, 10)), FAKE, 200, FAKE, FAKE, 50,
                                             FAKE, FAKE, dws - 1, None) == 3
+
+
+def test_local_and_streaming_argument_errors(V):
+    s = shape(V)
+    L = V.lib()
+    ws = V.vegas_verify_local_workspace_size(s, 4, 100000, 128)
+    assert ws <= V.vegas_verify_workspace_size(s, 4, 100000)      # the band bounds the splits
+    with pytest.raises(V.VegasError):
+        V.vegas_verify_local_workspace_size(s, 4, 100000, 0)
+    assert L.vegas_verify_attn_local(ctypes.byref(s), 4, FAKE, FAKE, FAKE, FAKE, 1000, 4000, 0, FAKE, FAKE, ws,
+                                     None) == 1
+    assert L.vegas_verify_attn_local(ctypes.byref(s), 4, FAKE, FAKE, FAKE, FAKE, 1000, 4000, 128, FAKE, FAKE, 0,
+                                     None) == 3
+    assert L.vegas_streaming_indices(0, 4, 4, FAKE, 100, FAKE, 10, FAKE, None) == 1
+    assert L.vegas_streaming_indices(2, 4, -1, FAKE, 100, FAKE, 10, FAKE, None) == 1
+    assert L.vegas_streaming_indices(2, 4, 4, FAKE, 100, FAKE, 10, None, None) == 1

@@ -14,7 +14,7 @@ from verification_guided_sparse_verify_amd.step import LayerStep
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
-    from parity_util import check_layer, log, run_layer
+    from parity_util import ATOL, check_layer, log, run_layer
 
 
 @pytest.fixture(autouse=True)
@@ -270,3 +270,55 @@ def test_paged_cache_matches_contiguous(case):
     assert torch.equal(idx[: wl.cu_k()[-1]], st.indices[: wl.cu_k()[-1]])
     assert torch.equal(drafts.view(torch.uint8), st.draft_out.view(torch.uint8))
     check_layer(wl, inp, st)   # and the contiguous path against the oracle
+
+
+LOCAL_CASES = [
+    # dtype, batch, Hq, Hkv, D, gamma, prefix lengths, window
+    ("bf16", 3, 16, 4, 128, 3, [1000, 4097, 129], 128),
+    ("bf16", 3, 16, 4, 128, 3, [1000, 4097, 129], 1),
+    ("bf16", 2, 64, 8, 64, 3, [20000, 50], 128),
+    ("f32", 2, 8, 2, 64, 2, [300, 77], 64),
+    ("bf16", 1, 32, 8, 128, 5, [700], 5000),
+]
+
+
+@pytest.mark.parametrize("case", LOCAL_CASES, ids=lambda c: f"{c[0]}-B{c[1]}-{c[2]}x{c[3]}-D{c[4]}-g{c[5]}-w{c[7]}")
+def test_local_window_verify_matches_oracle(case):
+    """Banded verification (row r sees keys L+r-window < j <= L+r) against the oracle."""
+    dtype, B, hq, hkv, d, gamma, prefixes, window = case
+    wl = W.custom_workload(dtype, B, hq, hkv, d, gamma, prefixes)
+    log(f"case: local {wl.name} L={prefixes} window={window}")
+    inp = W.make_inputs(wl, seed=10, device="cuda")
+    shape = V.attn_shape(V.VEGAS_DTYPE_BF16 if dtype == "bf16" else V.VEGAS_DTYPE_F32, B, hq, hkv, d, wl.scale)
+    out = torch.empty_like(inp["q"])
+    ws = torch.empty(V.vegas_verify_local_workspace_size(shape, gamma, max(wl.seqlens), window),
+                     dtype=torch.uint8, device="cuda")
+    V.vegas_verify_attn_local(shape, gamma, inp["q"], inp["k"], inp["v"], inp["cu_seqlens_k"], max(wl.seqlens),
+                              wl.total_kv, window, out, ws)
+    torch.cuda.synchronize()
+    ref, _ = oracle.verify_attn(W.host_bits(inp["q"]), W.host_bits(inp["k"]), W.host_bits(inp["v"]),
+                                wl.cu_seqlens(), gamma, wl.scale, want_scores=False, window=window)
+    err = float(np.abs(out.float().cpu().numpy() - ref).max())
+    log(f"  max abs err {err}")
+    assert err <= ATOL[dtype]
+
+
+def test_streaming_lists_and_drafts_match_oracle():
+    """Sink-plus-recent lists with the Vegas budget are bit-exact, and drafting over them matches."""
+    wl = W.custom_workload("bf16", 3, 32, 8, 128, 4, [6000, 300, 2049])
+    inp = W.make_inputs(wl, seed=11, device="cuda")
+    cuk = wl.cu_k()
+    idx = torch.full((cuk[-1],), -1, dtype=torch.int32, device="cuda")
+    V.vegas_streaming_indices(wl.batch, wl.gamma, 4, inp["cu_seqlens_k"], wl.total_kv, inp["cu_k"], cuk[-1], idx)
+    torch.cuda.synchronize()
+    ref = oracle.streaming_indices(wl.cu_seqlens(), wl.gamma, 4, cuk)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+    shape = V.attn_shape(V.VEGAS_DTYPE_BF16, wl.batch, 32, 8, 128, wl.scale)
+    out = torch.empty_like(inp["draft_q"][0])
+    ws = torch.empty(V.vegas_sparse_decode_workspace_size(shape, max(wl.k_per_seq)), dtype=torch.uint8, device="cuda")
+    V.vegas_sparse_decode_attn(shape, inp["draft_q"][0], inp["k"], inp["v"], inp["cu_seqlens_k"], wl.total_kv, idx,
+                               inp["cu_k"], max(wl.k_per_seq), out, ws)
+    torch.cuda.synchronize()
+    d_ref = oracle.sparse_decode_attn(W.host_bits(inp["draft_q"][0]), W.host_bits(inp["k"]), W.host_bits(inp["v"]),
+                                      wl.cu_seqlens(), ref, cuk, wl.scale)
+    assert np.abs(out.float().cpu().numpy() - d_ref).max() <= 2e-2

@@ -12,6 +12,7 @@ from .vegas import (  # noqa: F401
     vegas_select_workspace_size, vegas_select_topk,
     vegas_sparse_decode_workspace_size, vegas_sparse_decode_attn,
     PagedKV, paged_kv, vegas_verify_paged_workspace_size, vegas_verify_attn_paged,
-    vegas_sparse_decode_attn_paged,
+    vegas_sparse_decode_attn_paged, vegas_verify_local_workspace_size, vegas_verify_attn_local,
+    vegas_streaming_indices,
     VEGAS_DTYPE_F32, VEGAS_DTYPE_BF16,
 )

@@ -3,6 +3,7 @@
 // synchronises with the device or allocates device memory.
 #include "vegas.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -204,10 +205,15 @@ vegas_status_t vegas_verify_workspace_size(const vegas_attn_shape_t* shape, int3
 
 namespace {
 
+// Positions of one sequence a verification split plan has to cover.
+int verify_span(int32_t max_seqlen_k, int32_t gamma, int32_t window) {
+    return window > 0 ? std::min<int64_t>(max_seqlen_k, (int64_t)window + gamma) : max_seqlen_k;
+}
+
 vegas_status_t verify_impl(const vegas_attn_shape_t* shape, int32_t gamma, const void* q, const void* k,
                            const void* v, const vegas_paged_kv_t* pages, const int32_t* cu_seqlens_k,
                            int32_t max_seqlen_k, int32_t total_kv, uint32_t collect_mask, float* scores,
-                           void* out, void* workspace, size_t workspace_bytes, void* stream) {
+                           void* out, void* workspace, size_t workspace_bytes, void* stream, int32_t window = 0) {
     vegas_status_t st = check_shape(shape);
     if (st != VEGAS_OK) return st;
     if ((st = check_gamma(gamma, shape)) != VEGAS_OK) return st;
@@ -230,8 +236,12 @@ vegas_status_t verify_impl(const vegas_attn_shape_t* shape, int32_t gamma, const
     if (!pages && !rows_fit_32bit(shape, max_seqlen_k))
         return fail(VEGAS_ERR_UNSUPPORTED, "one sequence's K/V rows span 4 GiB or more");
     const int G = shape->num_q_heads / shape->num_kv_heads;
+    if (window < 0) return fail(VEGAS_ERR_INVALID_ARGUMENT, "window %d < 0", window);
+    if (window > 0 && collect_mask != 0u)
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "collection is not defined under a local mask");
     const AttnPlan plan = plan_attn(shape->dtype == VEGAS_DTYPE_BF16, shape->batch, shape->num_kv_heads, W * G,
-                                    shape->head_dim, max_seqlen_k, false, pages ? pages->page_size : 0);
+                                    shape->head_dim, verify_span(max_seqlen_k, gamma, window), false,
+                                    pages ? pages->page_size : 0);
     if (workspace_bytes < plan.total())
         return fail(VEGAS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.total(),
                     workspace_bytes);
@@ -258,6 +268,7 @@ vegas_status_t verify_impl(const vegas_attn_shape_t* shape, int32_t gamma, const
     a.scale = shape->softmax_scale;
     a.scale_log2 = shape->softmax_scale * 1.4426950408889634f;
     a.collect_mask = collect_mask;
+    a.window = window;
     a.page_shift = shift;
     if (pages) {
         a.block_table = pages->block_table;
@@ -345,6 +356,37 @@ vegas_status_t vegas_verify_attn_paged(const vegas_attn_shape_t* shape, int32_t 
     if (!pages) return fail(VEGAS_ERR_INVALID_ARGUMENT, "pages is NULL");
     return verify_impl(shape, gamma, q, k, v, pages, cu_seqlens_k, max_seqlen_k, total_kv, collect_mask,
                        scores, out, workspace, workspace_bytes, stream);
+}
+
+vegas_status_t vegas_verify_local_workspace_size(const vegas_attn_shape_t* shape, int32_t gamma,
+                                                 int32_t max_seqlen_k, int32_t window, size_t* bytes) {
+    if (window < 1) return fail(VEGAS_ERR_INVALID_ARGUMENT, "window %d < 1", window);
+    if (max_seqlen_k < gamma + 1)
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "max_seqlen_k %d < gamma+1", max_seqlen_k);
+    return vegas_verify_workspace_size(shape, gamma, verify_span(max_seqlen_k, gamma, window), bytes);
+}
+
+vegas_status_t vegas_verify_attn_local(const vegas_attn_shape_t* shape, int32_t gamma, const void* q,
+                                       const void* k, const void* v, const int32_t* cu_seqlens_k,
+                                       int32_t max_seqlen_k, int32_t total_kv, int32_t window, void* out,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+    if (window < 1) return fail(VEGAS_ERR_INVALID_ARGUMENT, "window %d < 1", window);
+    return verify_impl(shape, gamma, q, k, v, nullptr, cu_seqlens_k, max_seqlen_k, total_kv, 0u, nullptr, out,
+                       workspace, workspace_bytes, stream, window);
+}
+
+vegas_status_t vegas_streaming_indices(int32_t batch, int32_t gamma, int32_t sinks, const int32_t* cu_seqlens_k,
+                                       int32_t total_kv, const int32_t* cu_idx, int32_t total_idx,
+                                       int32_t* indices, void* stream) {
+    if (batch < 1) return fail(VEGAS_ERR_INVALID_ARGUMENT, "batch must be >= 1");
+    if (gamma < 0 || gamma > 31) return fail(VEGAS_ERR_INVALID_ARGUMENT, "gamma %d outside 0..31", gamma);
+    if (sinks < 0 || total_kv < 1 || total_idx < 0)
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "sinks, total_idx must be >= 0 and total_kv >= 1");
+    if (!cu_seqlens_k || !cu_idx || (total_idx > 0 && !indices))
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "cu_seqlens_k, cu_idx and indices must be non-NULL");
+    return hip_status(vegas::launch_streaming_indices(batch, gamma + 1, sinks, cu_seqlens_k, total_kv, cu_idx,
+                                                      total_idx, indices, static_cast<hipStream_t>(stream)),
+                      "streaming indices launch");
 }
 
 vegas_status_t vegas_select_workspace_size(int32_t batch, int32_t num_kv_heads, int32_t gamma,

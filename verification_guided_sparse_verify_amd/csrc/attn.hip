@@ -322,14 +322,17 @@ __device__ __forceinline__ void compute_block(const AttnArgs& a, WaveState<BF16,
         }
     }
 
-    const bool need_mask = GATHER ? (p0 + kAttnBlock > end) : (p0 + kAttnBlock > min(end, L + 1));
+    // Causal tail, end of the split, and (local mask) keys older than a row's band.
+    const bool need_mask = GATHER ? (p0 + kAttnBlock > end)
+                                  : (p0 + kAttnBlock > min(end, L + 1) || (a.window > 0 && p0 < L + a.W - a.window));
     if (need_mask) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int pos = p0 + 4 * lg + v;
 #pragma unroll
             for (int qb = 0; qb < MB; ++qb) {
-                const bool vis = pos < end && (GATHER || pos <= L + ws.rrow[qb]);
+                const int last = L + ws.rrow[qb];
+                const bool vis = pos < end && (GATHER || (pos <= last && (a.window <= 0 || pos > last - a.window)));
                 if (!vis) s[qb][v] = kNegInf;
             }
         }
@@ -420,7 +423,9 @@ attn_split_kernel(const AttnArgs a) {
         count = n_b;
         L = n_b - a.W;
     }
-    const int start = split * a.chunk;
+    // Under a local mask no row sees a key before row 0's band.
+    const int lo = (!GATHER && a.window > 0) ? max(0, L - a.window + 1) : 0;
+    const int start = lo + split * a.chunk;
     if (seq0 < 0 || n_b <= 0 || start >= count) return;          // uniform per workgroup
     const int end = min(start + a.chunk, count);
 
@@ -634,7 +639,8 @@ __global__ void __launch_bounds__(kCombineWaves * 64) attn_combine_kernel(const 
 
     const int seq0 = a.cu_seqlens_k[b];
     const int n_b = min(a.cu_seqlens_k[b + 1], a.total_kv) - seq0;
-    const int count = GATHER ? (a.cu_idx[b + 1] - a.cu_idx[b]) : n_b;
+    const int lo = (!GATHER && a.window > 0) ? max(0, n_b - a.W - a.window + 1) : 0;
+    const int count = (GATHER ? (a.cu_idx[b + 1] - a.cu_idx[b]) : n_b) - lo;
     int nsv = (seq0 >= 0 && n_b > 0 && count > 0) ? (count + a.chunk - 1) / a.chunk : 0;
     nsv = min(nsv, a.nsplit);
 

@@ -61,7 +61,13 @@ struct AttnArgs {
     int32_t max_pages;
     int32_t num_pages;
     int32_t page_shift;            // log2(page size); -1: contiguous varlen cache
+    int32_t window;                // verification local mask: row r sees keys (L+r-window, L+r]; 0: none
 };
+
+// Query-agnostic sink-plus-recent index lists.
+hipError_t launch_streaming_indices(int batch, int W, int sinks, const int32_t* cu_seqlens_k, int32_t total_kv,
+                                    const int32_t* cu_idx, int32_t total_idx, int32_t* indices,
+                                    hipStream_t stream);
 
 hipError_t launch_attn(const AttnArgs& a, bool bf16, int head_dim, int mblocks, bool gather,
                        bool collect, hipStream_t stream);

@@ -364,7 +364,38 @@ __global__ void __launch_bounds__(kSelThreads) sel_write_kernel(const SelectArgs
         if (sel[e] && off0 + o[e] < sg.k) out[off0 + o[e]] = p0 + e;
 }
 
+// One thread per output slot: find the slot's sequence (binary search over
+// cu_idx), then emit sink j (j < min(sinks, k)) or recent position L-(k-j).
+__global__ void streaming_indices_kernel(int batch, int W, int sinks, const int32_t* __restrict__ cu_seqlens_k,
+                                         int32_t total_kv, const int32_t* __restrict__ cu_idx, int32_t total_idx,
+                                         int32_t* __restrict__ indices) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total_idx) return;
+    int lo = 0, hi = batch;                   // sequence b with cu_idx[b] <= i < cu_idx[b+1]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cu_idx[mid] <= i) lo = mid; else hi = mid;
+    }
+    const int b = lo;
+    const int s0 = min(max(cu_seqlens_k[b], 0), total_kv);
+    const int L = max(min(max(cu_seqlens_k[b + 1], s0), total_kv) - s0 - W, 0);
+    const int k = min(cu_idx[b + 1] - cu_idx[b], L);
+    const int j = i - cu_idx[b];
+    const int ns = min(sinks, k);
+    int pos = j < ns ? j : L - (k - j);
+    indices[i] = min(max(pos, 0), max(L - 1, 0));
+}
+
 }  // namespace
+
+hipError_t launch_streaming_indices(int batch, int W, int sinks, const int32_t* cu_seqlens_k, int32_t total_kv,
+                                    const int32_t* cu_idx, int32_t total_idx, int32_t* indices,
+                                    hipStream_t stream) {
+    if (total_idx > 0)
+        hipLaunchKernelGGL(streaming_indices_kernel, dim3((total_idx + 255) / 256), dim3(256), 0, stream, batch, W,
+                           sinks, cu_seqlens_k, total_kv, cu_idx, total_idx, indices);
+    return hipGetLastError();
+}
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
     const int nz = a.batch * kSelBins + a.batch;

@@ -22,9 +22,15 @@ class LayerStep:
 
     def __init__(self, inputs: dict, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                  gamma: int, seqlens, k_per_seq, softmax_scale: float, n_drafts: int | None = None,
-                 collect_mask: int | None = None, paged: dict | None = None):
+                 collect_mask: int | None = None, paged: dict | None = None, selection: str = "vegas",
+                 sinks: int = 4):
         self.inp = inputs
         self.gamma = gamma
+        # selection: "vegas" (verification-guided top-k of the collected logits) or "streaming"
+        # (query-agnostic sinks + most recent tokens with the same budget; no collection).
+        assert selection in ("vegas", "streaming")
+        self.selection = selection
+        self.sinks = sinks
         # paged: a page pool from workloads.page_cache (k_pool, v_pool, block_table, num_pages); the
         # paged entry points then read K/V through the block table.
         self.paged = paged
@@ -67,6 +73,10 @@ class LayerStep:
 
     def select(self, stream=None):
         i = self.inp
+        if self.selection == "streaming":
+            V.vegas_streaming_indices(self.batch, self.gamma, self.sinks, i["cu_seqlens_k"], self.total_kv, i["cu_k"],
+                                      self.total_k, self.indices, stream)
+            return
         V.vegas_select_topk(self.batch, self.hkv, self.gamma, self.scores, i["cu_seqlens_k"], self.max_seqlen,
                             self.total_kv, i["cu_k"], self.indices, self.workspace, stream)
 
@@ -81,7 +91,7 @@ class LayerStep:
                                    self.indices, i["cu_k"], self.max_k, self.draft_out[j], self.workspace, stream)
 
     def run(self, stream=None):
-        self.verify(True, stream)
+        self.verify(self.selection == "vegas", stream)
         self.select(stream)
         for j in range(self.n_drafts):
             self.draft(j, stream)
@@ -118,9 +128,16 @@ class LayerStep:
             kv = (i["k"].data_ptr(), i["v"].data_ptr())
         verify = call(vfn, vname, common + (self.collect_mask, self.scores.data_ptr(), self.out.data_ptr(), ws, wsb, st))
         plain = call(vfn, vname, common + (0, None, self.out.data_ptr(), ws, wsb, st))
-        select = call(L.vegas_select_topk, "vegas_select_topk",
-                      (self.batch, self.hkv, self.gamma, self.scores.data_ptr(), i["cu_seqlens_k"].data_ptr(),
-                       self.max_seqlen, self.total_kv, i["cu_k"].data_ptr(), self.indices.data_ptr(), ws, wsb, st))
+        if self.selection == "streaming":
+            select = call(L.vegas_streaming_indices, "vegas_streaming_indices",
+                          (self.batch, self.gamma, self.sinks, i["cu_seqlens_k"].data_ptr(), self.total_kv,
+                           i["cu_k"].data_ptr(), self.total_k, self.indices.data_ptr(), st))
+            verify = plain          # nothing is collected for a query-agnostic selection
+        else:
+            select = call(L.vegas_select_topk, "vegas_select_topk",
+                          (self.batch, self.hkv, self.gamma, self.scores.data_ptr(), i["cu_seqlens_k"].data_ptr(),
+                           self.max_seqlen, self.total_kv, i["cu_k"].data_ptr(), self.indices.data_ptr(), ws, wsb,
+                           st))
         drafts = [call(dfn, dname,
                        (shape, i["draft_q"][j].data_ptr()) + kv +
                        (i["cu_seqlens_k"].data_ptr(), self.total_kv, self.indices.data_ptr(), i["cu_k"].data_ptr(),

@@ -29,6 +29,7 @@ EXPORTED = (
     "vegas_select_workspace_size", "vegas_select_topk",
     "vegas_sparse_decode_workspace_size", "vegas_sparse_decode_attn",
     "vegas_verify_paged_workspace_size", "vegas_verify_attn_paged", "vegas_sparse_decode_attn_paged",
+    "vegas_verify_local_workspace_size", "vegas_verify_attn_local", "vegas_streaming_indices",
 )
 
 
@@ -77,6 +78,9 @@ def lib():
             "vegas_verify_paged_workspace_size": ([SP, I32, I32, I32, PSZ], ctypes.c_int),
             "vegas_verify_attn_paged": ([SP, I32, P, P, P, PP, P, I32, I32, U32, P, P, P, SZ, P], ctypes.c_int),
             "vegas_sparse_decode_attn_paged": ([SP, P, P, P, PP, P, I32, P, P, I32, P, P, SZ, P], ctypes.c_int),
+            "vegas_verify_local_workspace_size": ([SP, I32, I32, I32, PSZ], ctypes.c_int),
+            "vegas_verify_attn_local": ([SP, I32, P, P, P, P, I32, I32, I32, P, P, SZ, P], ctypes.c_int),
+            "vegas_streaming_indices": ([I32, I32, I32, P, I32, P, I32, P, P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -202,3 +206,26 @@ def vegas_sparse_decode_attn_paged(shape: AttnShape, q, k, v, pages: PagedKV, cu
                                                 _ptr(cu_seqlens_k), total_kv, _ptr(indices), _ptr(cu_idx), max_idx,
                                                 _ptr(out), _ptr(workspace), _nbytes(workspace), _stream(stream)),
            "vegas_sparse_decode_attn_paged")
+
+
+def vegas_verify_local_workspace_size(shape: AttnShape, gamma: int, max_seqlen_k: int, window: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().vegas_verify_local_workspace_size(ctypes.byref(shape), gamma, max_seqlen_k, window,
+                                                   ctypes.byref(n)),
+           "vegas_verify_local_workspace_size")
+    return n.value
+
+
+def vegas_verify_attn_local(shape: AttnShape, gamma: int, q, k, v, cu_seqlens_k, max_seqlen_k: int, total_kv: int,
+                            window: int, out, workspace, stream=None) -> None:
+    _check(lib().vegas_verify_attn_local(ctypes.byref(shape), gamma, _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k),
+                                         max_seqlen_k, total_kv, window, _ptr(out), _ptr(workspace),
+                                         _nbytes(workspace), _stream(stream)),
+           "vegas_verify_attn_local")
+
+
+def vegas_streaming_indices(batch: int, gamma: int, sinks: int, cu_seqlens_k, total_kv: int, cu_idx, total_idx: int,
+                            indices, stream=None) -> None:
+    _check(lib().vegas_streaming_indices(batch, gamma, sinks, _ptr(cu_seqlens_k), total_kv, _ptr(cu_idx), total_idx,
+                                         _ptr(indices), _stream(stream)),
+           "vegas_streaming_indices")
