@@ -54,6 +54,8 @@ def _lib():
         lib.vo_verify_attn_local.restype = I
         lib.vo_streaming_indices.argtypes = [I, I, I, P, P, P]
         lib.vo_streaming_indices.restype = I
+        lib.vo_spec_accept.argtypes = [I, I, I64, P, P, P, P, P, P, P]
+        lib.vo_spec_accept.restype = I
         lib.vo_select_topk.argtypes = [I, I, I, P, P, I64, P, P, P, P]
         lib.vo_select_topk.restype = I
         lib.vo_sparse_decode_attn.argtypes = [I, I, I, I, I, D, P, P, P, P, P, P, P]
@@ -159,3 +161,22 @@ def streaming_indices(cu_seqlens_k, gamma: int, sinks: int, cu_idx):
     if rc != 0:
         raise ValueError("vo_streaming_indices rejected its arguments")
     return out[: int(cui[-1])]
+
+
+def spec_accept(p, q, draft, u_accept, u_sample):
+    """Speculative-sampling acceptance.  p: float32 [B, gamma+1, V]; q: float32 [B, gamma, V];
+    draft: int32 [B, gamma]; u_accept: float32 [B, gamma]; u_sample: float32 [B].
+    Returns (n_accepted int32 [B], next_token int32 [B])."""
+    p = _c(p, np.float32)
+    B, W, V = p.shape
+    gamma = W - 1
+    q = _c(q, np.float32) if gamma > 0 else None
+    draft = _c(draft, np.int32) if gamma > 0 else None
+    ua = _c(u_accept, np.float32) if gamma > 0 else None
+    us = _c(u_sample, np.float32)
+    n = np.zeros(B, np.int32)
+    t = np.zeros(B, np.int32)
+    rc = _lib().vo_spec_accept(B, gamma, V, _ptr(p), _ptr(q), _ptr(draft), _ptr(ua), _ptr(us), _ptr(n), _ptr(t))
+    if rc != 0:
+        raise ValueError("vo_spec_accept rejected its arguments")
+    return n, t

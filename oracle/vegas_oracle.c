@@ -278,3 +278,72 @@ int vo_streaming_indices(int batch, int gamma, int sinks, const int32_t* cu_seql
     }
     return 0;
 }
+
+/*
+ * Speculative-sampling acceptance (the blog "You Could Have Come Up with
+ * Speculative Decoding", section "Preservation of Target Distribution"): draft
+ * token y_j, proposed from q_j, is kept when u_j <= min(1, p_j(y_j) / q_j(y_j)),
+ * i.e. u_j * q_j(y_j) <= p_j(y_j); at the first rejection a replacement is drawn
+ * from the residual max(0, p_j - q_j) normalised; when all gamma drafts are
+ * kept, the bonus token is drawn from p_{gamma+1} (section "Guessing is
+ * Enough?").  Arithmetic fixed here so that the chosen token does not depend on
+ * summation order:
+ *   - the acceptance test is evaluated exactly: the product of two binary32
+ *     values is exact in binary64;
+ *   - masses are taken in fixed point, m_y = floor(x_y * 2^40) of the binary32
+ *     value x_y (residual or target probability), summed as integers;
+ *   - with u_int = floor(u * 2^24) and M = sum m_y, the drawn token is the
+ *     smallest y with m_0 + ... + m_y > floor(u_int * M / 2^24);
+ *   - if the residual mass is zero (only possible through rounding or
+ *     unnormalised inputs) the replacement is drawn from p_j itself; if that is
+ *     zero too, token 0.
+ */
+static uint64_t fixed_mass(double x) {
+    if (!(x > 0.0)) return 0;
+    double f = floor(x * 1099511627776.0);        /* 2^40 */
+    if (f > 1099511627776.0) f = 1099511627776.0;  /* masses above 1 are capped at 1 */
+    return (uint64_t)f;
+}
+
+static int32_t draw_fixed(const float* p, const float* q, int64_t vocab, float u) {
+    /* q == NULL: masses of p; else residual masses max(0, p - q) */
+    uint64_t total = 0;
+    for (int64_t y = 0; y < vocab; ++y) {
+        double x = q ? (double)p[y] - (double)q[y] : (double)p[y];
+        total += fixed_mass(x);
+    }
+    if (total == 0) return q ? draw_fixed(p, NULL, vocab, u) : 0;
+    double uf = floor((double)u * 16777216.0);    /* 2^24 */
+    uint64_t ui = uf < 0.0 ? 0 : (uf > 16777215.0 ? 16777215u : (uint64_t)uf);
+    const uint64_t thr = (total >> 24) * ui + (((total & 16777215u) * ui) >> 24);
+    uint64_t run = 0;
+    for (int64_t y = 0; y < vocab; ++y) {
+        double x = q ? (double)p[y] - (double)q[y] : (double)p[y];
+        run += fixed_mass(x);
+        if (run > thr) return (int32_t)y;
+    }
+    return (int32_t)(vocab - 1);
+}
+
+int vo_spec_accept(int batch, int gamma, int64_t vocab, const float* p, const float* q,
+                   const int32_t* draft, const float* u_accept, const float* u_sample,
+                   int32_t* n_accepted, int32_t* next_token) {
+    if (batch < 0 || gamma < 0 || vocab < 1 || !p || (gamma > 0 && (!q || !draft || !u_accept)) ||
+        !u_sample || !n_accepted || !next_token)
+        return -1;
+    for (int b = 0; b < batch; ++b) {
+        const float* pb = p + (int64_t)b * (gamma + 1) * vocab;
+        const float* qb = gamma > 0 ? q + (int64_t)b * gamma * vocab : NULL;
+        int j = 0;
+        for (; j < gamma; ++j) {
+            int32_t y = draft[(int64_t)b * gamma + j];
+            if (y < 0 || y >= vocab) return -1;
+            double lhs = (double)u_accept[(int64_t)b * gamma + j] * (double)qb[(int64_t)j * vocab + y];
+            if (!(lhs <= (double)pb[(int64_t)j * vocab + y])) break;   /* rejected */
+        }
+        n_accepted[b] = j;
+        next_token[b] = j < gamma ? draw_fixed(pb + (int64_t)j * vocab, qb + (int64_t)j * vocab, vocab, u_sample[b])
+                                  : draw_fixed(pb + (int64_t)gamma * vocab, NULL, vocab, u_sample[b]);
+    }
+    return 0;
+}

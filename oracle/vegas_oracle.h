@@ -69,6 +69,18 @@ int vo_verify_attn_local(int dtype, int batch, int num_q_heads, int num_kv_heads
 int vo_streaming_indices(int batch, int gamma, int sinks, const int32_t* cu_seqlens_k,
                          const int32_t* cu_idx, int32_t* indices);
 
+/* Speculative-sampling acceptance per sequence: p [batch, gamma+1, vocab]
+ * target probabilities, q [batch, gamma, vocab] draft probabilities, draft
+ * [batch, gamma] tokens, u_accept [batch, gamma] and u_sample [batch] uniforms
+ * in [0, 1).  n_accepted[b] = drafts kept before the first rejection;
+ * next_token[b] = the replacement drawn from the residual at that rejection,
+ * or the bonus token drawn from p_{gamma+1} when all are kept.  The
+ * acceptance test is exact and the draw uses 2^-40 fixed-point masses (see
+ * the source). */
+int vo_spec_accept(int batch, int gamma, int64_t vocab, const float* p, const float* q,
+                   const int32_t* draft, const float* u_accept, const float* u_sample,
+                   int32_t* n_accepted, int32_t* next_token);
+
 /* Exact top-k of the score summed over KV heads, per sequence.
  * S_b[i] = sum_g scores[g, cu_seqlens_k[b] + i] for i < L_b.  The k_b
  * (= cu_k[b+1] - cu_k[b]) positions with the largest S_b are written to

@@ -410,3 +410,90 @@ def test_streaming_lists_closed_form():
     assert got[:12].tolist() == list(range(88, 100))       # no sinks: pure sliding window
     with pytest.raises(ValueError):
         oracle.streaming_indices(cu, gamma, 4, np.array([0, 101, 101, 101], np.int32))
+
+
+# ---------------------------------------------------------------- speculative-sampling acceptance
+
+def _softmax_rows(rng, shape, temp=1.0):
+    x = rng.standard_normal(shape) / temp
+    e = np.exp(x - x.max(-1, keepdims=True))
+    return (e / e.sum(-1, keepdims=True)).astype(np.float32)
+
+
+def test_accept_greedy_special_case():
+    """One-hot p and q (greedy decoding): a draft is kept iff it is the target's argmax, and the
+    replacement at the first mismatch is the target's argmax."""
+    rng = np.random.default_rng(30)
+    B, gamma, V = 64, 4, 11
+    g = rng.integers(0, V, (B, gamma + 1))
+    drafts = np.where(rng.random((B, gamma)) < 0.7, g[:, :gamma], rng.integers(0, V, (B, gamma))).astype(np.int32)
+    p = np.zeros((B, gamma + 1, V), np.float32)
+    q = np.zeros((B, gamma, V), np.float32)
+    for b in range(B):
+        p[b, np.arange(gamma + 1), g[b]] = 1.0
+        q[b, np.arange(gamma), drafts[b]] = 1.0
+    n, t = oracle.spec_accept(p, q, drafts, rng.random((B, gamma)).astype(np.float32),
+                              rng.random(B).astype(np.float32))
+    for b in range(B):
+        want = 0
+        while want < gamma and drafts[b, want] == g[b, want]:
+            want += 1
+        assert n[b] == want
+        assert t[b] == g[b, want]
+
+
+def test_accept_identical_distributions_keep_every_draft():
+    rng = np.random.default_rng(31)
+    B, gamma, V = 16, 3, 50
+    p = _softmax_rows(rng, (B, gamma + 1, V))
+    q = p[:, :gamma].copy()
+    drafts = rng.integers(0, V, (B, gamma)).astype(np.int32)
+    n, _ = oracle.spec_accept(p, q, drafts, (rng.random((B, gamma)) * 0.999).astype(np.float32),
+                              rng.random(B).astype(np.float32))
+    assert np.all(n == gamma)
+
+
+def test_draw_is_the_inverse_cdf_with_half_open_bins():
+    p = np.array([[[0.25, 0.5, 0.25]]], np.float32)
+    cases = {0.0: 0, 0.2499: 0, 0.25: 1, 0.7499: 1, 0.75: 2, 0.9999: 2}
+    for u, want in cases.items():
+        _, t = oracle.spec_accept(p, np.zeros((1, 0, 3), np.float32), np.zeros((1, 0), np.int32),
+                                  np.zeros((1, 0), np.float32), np.array([u], np.float32))
+        assert t[0] == want, (u, t[0], want)
+
+
+def test_first_token_follows_the_target_distribution():
+    """The lossless property: with y ~ q, the first emitted token (the kept draft, or the residual
+    replacement) is distributed as p.  Integrate exactly over y and over grids of both uniforms."""
+    rng = np.random.default_rng(32)
+    V, N1, N2 = 5, 160, 160
+    p1 = _softmax_rows(rng, (V,), 0.7)
+    q1 = _softmax_rows(rng, (V,), 0.7)
+    u1 = (np.arange(N1) + 0.5) / N1
+    u2 = (np.arange(N2) + 0.5) / N2
+    yy, a, s = np.meshgrid(np.arange(V), u1, u2, indexing="ij")
+    B = yy.size
+    p = np.broadcast_to(np.stack([p1, p1]), (B, 2, V)).copy()       # gamma = 1; p_2 unused unless kept
+    q = np.broadcast_to(q1, (B, 1, V)).copy()
+    n, t = oracle.spec_accept(p, q, yy.reshape(B, 1).astype(np.int32), a.reshape(B, 1).astype(np.float32),
+                              s.reshape(B).astype(np.float32))
+    first = np.where(n == 1, yy.reshape(B), t)
+    w = q1[yy.reshape(B)] / (N1 * N2)                                 # probability weight of each instance
+    emp = np.array([w[first == y].sum() for y in range(V)])
+    assert np.abs(emp - p1).max() < 0.02
+    # the acceptance rate is 1 - TV(p, q)
+    assert abs(float(w[n == 1].sum()) - (1 - 0.5 * np.abs(p1 - q1).sum())) < 0.02
+
+
+def test_all_kept_bonus_follows_the_last_target_row():
+    rng = np.random.default_rng(33)
+    V, N = 6, 4000
+    p = _softmax_rows(rng, (1, 3, V))
+    p = np.repeat(p, N, axis=0)
+    q = p[:, :2].copy()
+    drafts = np.zeros((N, 2), np.int32)
+    n, t = oracle.spec_accept(p, q, drafts, np.zeros((N, 2), np.float32),
+                              ((np.arange(N) + 0.5) / N).astype(np.float32))
+    assert np.all(n == 2)
+    emp = np.bincount(t, minlength=V) / N
+    assert np.abs(emp - p[0, 2]).max() < 2.0 / N + 1e-6
