@@ -168,6 +168,40 @@ def collect_sweep(base, gammas=(1, 3, 5, 7, 11, 15), reps=8):
                       "rows": rows}), flush=True)
 
 
+def accept_bench(reps=50):
+    """Time vegas_spec_accept on seeded synthetic distributions; one JSON line.  Bytes: the one
+    or two vocabulary rows each sequence reads for its draw, plus the tested draft entries."""
+    import torch
+    from verification_guided_sparse_verify_amd import workloads as W
+    from verification_guided_sparse_verify_amd import vegas as V
+
+    rows = []
+    for B, gamma, vocab in ((4, 5, 151936), (16, 3, 201088)):
+        inp = W.make_accept_inputs(B, gamma, vocab, seed=0, device="cuda:0")
+        n = torch.empty(B, dtype=torch.int32, device="cuda:0")
+        t = torch.empty(B, dtype=torch.int32, device="cuda:0")
+        ws = torch.empty(V.vegas_spec_accept_workspace_size(B, vocab), dtype=torch.uint8, device="cuda:0")
+        call = lambda: V.vegas_spec_accept(B, gamma, vocab, inp["p"], inp["q"], inp["draft"], inp["u_accept"],
+                                           inp["u_sample"], n, t, ws)
+        call()
+        torch.cuda.synchronize()
+        nacc = n.cpu()
+        rows_read = sum(2 if int(k) < gamma else 1 for k in nacc)
+        nbytes = rows_read * vocab * 4 + B * gamma * (4 + 4 + 4 + 4)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / reps
+        rows.append({"batch": B, "gamma": gamma, "vocab": vocab, "us_per_call": round(us, 2),
+                     "bytes_per_call": nbytes, "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "accepted": nacc.tolist()})
+    print(json.dumps({"accept_bench": rows}), flush=True)
+
+
 def copy_calibration(nbytes):
     """A plain device-to-device copy of known size, for scaling the HBM byte counters."""
     import torch
@@ -198,6 +232,9 @@ def main():
     ap.add_argument("--collect-sweep", action="store_true",
                     help="only time verification of one layer with collection off, Collect-2-Query and "
                          "all rows, over gamma")
+    ap.add_argument("--accept-bench", action="store_true",
+                    help="only time the speculative-sampling acceptance step (batch 4, gamma 5, "
+                         "Qwen3 vocabulary 151936, and batch 16, gamma 3, gpt-oss vocabulary 201088)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a device copy of BYTES bytes three times (counter calibration)")
     args = ap.parse_args()
@@ -209,6 +246,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.accept_bench:
+        accept_bench()
         return
 
     import torch

@@ -256,6 +256,38 @@ vegas_status_t vegas_streaming_indices(int32_t batch, int32_t gamma, int32_t sin
                                        const int32_t* cu_idx, int32_t total_idx, int32_t* indices,
                                        void* stream);
 
+/*
+ * Speculative-sampling acceptance: the step after verification that decides
+ * how many drafts are kept (blog "You Could Have Come Up with Speculative
+ * Decoding", section "Preservation of Target Distribution").  Draft y_j,
+ * proposed from q_j, is kept when u_j * q_j(y_j) <= p_j(y_j); at the first
+ * rejection the replacement is drawn from max(0, p_j - q_j) normalised; if all
+ * gamma drafts are kept, the bonus token is drawn from p_{gamma+1}.  The
+ * emitted tokens then follow p exactly.  The caller supplies the uniforms.
+ *
+ *  p             device fp32 [batch, gamma+1, vocab]: target probabilities of
+ *                the verification rows (after temperature / top-k / top-p).
+ *  q             device fp32 [batch, gamma, vocab]: draft probabilities.
+ *  draft_tokens  device int32 [batch, gamma], in [0, vocab) (out-of-range
+ *                tokens are clamped).
+ *  u_accept      device fp32 [batch, gamma], u_sample device fp32 [batch]:
+ *                uniforms in [0, 1).
+ *  n_accepted    device int32 [batch]: drafts kept before the first rejection.
+ *  next_token    device int32 [batch]: the replacement, or the bonus token.
+ *  workspace     caller-owned device scratch of vegas_spec_accept_workspace_size
+ *                bytes (contents undefined between calls).
+ * Decisions are exact and independent of summation order: the test is
+ * evaluated in binary64 (exact for a product of two binary32 values); draws
+ * use masses floor(x * 2^40) summed as integers and pick the smallest y whose
+ * running mass exceeds floor(floor(u * 2^24) * M / 2^24), M the total mass; an
+ * empty residual falls back to p_j, an empty p to token 0.
+ */
+vegas_status_t vegas_spec_accept_workspace_size(int32_t batch, int32_t vocab, size_t* bytes);
+vegas_status_t vegas_spec_accept(int32_t batch, int32_t gamma, int32_t vocab, const float* p,
+                                 const float* q, const int32_t* draft_tokens, const float* u_accept,
+                                 const float* u_sample, int32_t* n_accepted, int32_t* next_token,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

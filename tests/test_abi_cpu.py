@@ -180,3 +180,14 @@ def test_local_and_streaming_argument_errors(V):
     assert L.vegas_streaming_indices(0, 4, 4, FAKE, 100, FAKE, 10, FAKE, None) == 1
     assert L.vegas_streaming_indices(2, 4, -1, FAKE, 100, FAKE, 10, FAKE, None) == 1
     assert L.vegas_streaming_indices(2, 4, 4, FAKE, 100, FAKE, 10, None, None) == 1
+
+
+def test_spec_accept_argument_errors(V):
+    L = V.lib()
+    ws = V.vegas_spec_accept_workspace_size(4, 151936)
+    assert ws >= 4 * 38 * 16
+    for args, code in [((0, 3, 100), 1), ((2, 32, 100), 1), ((2, 3, 0), 1)]:
+        assert L.vegas_spec_accept(*args, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == code
+    assert L.vegas_spec_accept(2, 3, 100, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == 1
+    assert L.vegas_spec_accept(2, 3, 100, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, ws, None) == 1
+    assert L.vegas_spec_accept(2, 3, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == 3

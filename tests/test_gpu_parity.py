@@ -322,3 +322,54 @@ def test_streaming_lists_and_drafts_match_oracle():
     d_ref = oracle.sparse_decode_attn(W.host_bits(inp["draft_q"][0]), W.host_bits(inp["k"]), W.host_bits(inp["v"]),
                                       wl.cu_seqlens(), ref, cuk, wl.scale)
     assert np.abs(out.float().cpu().numpy() - d_ref).max() <= 2e-2
+
+
+ACCEPT_CASES = [
+    # batch, gamma, vocab, draft noise, temperature
+    (4, 5, 151936, 0.6, 1.0),      # Qwen3 vocabulary
+    (16, 3, 201088, 1.5, 0.6),     # gpt-oss vocabulary, sharper and less aligned drafts
+    (8, 0, 5000, 0.0, 1.0),        # nothing drafted: the bonus token only
+    (32, 7, 17, 0.3, 0.2),         # tiny vocabulary: exact ties and zero masses
+]
+
+
+@pytest.mark.parametrize("case", ACCEPT_CASES, ids=lambda c: f"B{c[0]}-g{c[1]}-V{c[2]}")
+def test_spec_accept_bit_exact(case):
+    """Accepted counts and emitted tokens equal the oracle's exactly (the decision arithmetic
+    is order-independent by construction)."""
+    B, gamma, Vsz, noise, temp = case
+    log(f"case: accept B={B} gamma={gamma} V={Vsz}")
+    inp = W.make_accept_inputs(B, gamma, Vsz, seed=12, device="cuda", draft_noise=noise, temperature=temp)
+    n = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    t = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    V.vegas_spec_accept(B, gamma, Vsz, inp["p"], inp["q"] if gamma else None, inp["draft"] if gamma else None,
+                         inp["u_accept"] if gamma else None, inp["u_sample"], n, t)
+    torch.cuda.synchronize()
+    h = {k: v.cpu().numpy() for k, v in inp.items()}
+    n_ref, t_ref = oracle.spec_accept(h["p"], h["q"], h["draft"], h["u_accept"], h["u_sample"])
+    log(f"  accepted {n.cpu().tolist()[:8]}")
+    assert np.array_equal(n.cpu().numpy(), n_ref)
+    assert np.array_equal(t.cpu().numpy(), t_ref)
+
+
+def test_spec_accept_greedy_and_forced_rejections():
+    """One-hot rows (greedy decoding) and drafts forced out by u = 1: the decision and the
+    residual draw match the oracle."""
+    B, gamma, Vv = 64, 4, 1000
+    g = torch.Generator().manual_seed(13)
+    tgt = torch.randint(0, Vv, (B, gamma + 1), generator=g)
+    draft = torch.where(torch.rand(B, gamma, generator=g) < 0.6, tgt[:, :gamma],
+                        torch.randint(0, Vv, (B, gamma), generator=g)).to(torch.int32)
+    p = torch.zeros(B, gamma + 1, Vv)
+    p.scatter_(2, tgt[..., None], 1.0)
+    q = torch.softmax(torch.randn(B, gamma, Vv, generator=g), dim=-1)
+    q.scatter_(2, draft.long()[..., None], 0.9)
+    ua = torch.ones(B, gamma) * torch.rand(B, 1, generator=g)
+    us = torch.rand(B, generator=g)
+    dev = {k: v.contiguous().cuda() for k, v in dict(p=p, q=q, d=draft, ua=ua, us=us).items()}
+    n = torch.empty(B, dtype=torch.int32, device="cuda")
+    t = torch.empty(B, dtype=torch.int32, device="cuda")
+    V.vegas_spec_accept(B, gamma, Vv, dev["p"], dev["q"], dev["d"], dev["ua"], dev["us"], n, t)
+    torch.cuda.synchronize()
+    n_ref, t_ref = oracle.spec_accept(p.numpy(), q.numpy(), draft.numpy(), ua.numpy(), us.numpy())
+    assert np.array_equal(n.cpu().numpy(), n_ref) and np.array_equal(t.cpu().numpy(), t_ref)

@@ -13,6 +13,6 @@ from .vegas import (  # noqa: F401
     vegas_sparse_decode_workspace_size, vegas_sparse_decode_attn,
     PagedKV, paged_kv, vegas_verify_paged_workspace_size, vegas_verify_attn_paged,
     vegas_sparse_decode_attn_paged, vegas_verify_local_workspace_size, vegas_verify_attn_local,
-    vegas_streaming_indices,
+    vegas_streaming_indices, vegas_spec_accept_workspace_size, vegas_spec_accept,
     VEGAS_DTYPE_F32, VEGAS_DTYPE_BF16,
 )

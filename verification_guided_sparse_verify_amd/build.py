@@ -12,7 +12,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libvegas.so")
 
-SOURCES = ["attn.hip", "select.hip", "api.cpp"]
+SOURCES = ["attn.hip", "select.hip", "accept.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -389,6 +389,47 @@ vegas_status_t vegas_streaming_indices(int32_t batch, int32_t gamma, int32_t sin
                       "streaming indices launch");
 }
 
+vegas_status_t vegas_spec_accept_workspace_size(int32_t batch, int32_t vocab, size_t* bytes) {
+    if (batch < 1 || vocab < 1) return fail(VEGAS_ERR_INVALID_ARGUMENT, "batch and vocab must be >= 1");
+    if (!bytes) return fail(VEGAS_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    const size_t nch = ((size_t)vocab + vegas::kAcceptChunk - 1) / vegas::kAcceptChunk;
+    *bytes = align_up((size_t)batch * nch * 2 * sizeof(uint64_t)) + align_up((size_t)batch * sizeof(int32_t));
+    return VEGAS_OK;
+}
+
+vegas_status_t vegas_spec_accept(int32_t batch, int32_t gamma, int32_t vocab, const float* p, const float* q,
+                                 const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                                 int32_t* n_accepted, int32_t* next_token, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    size_t need = 0;
+    vegas_status_t st = vegas_spec_accept_workspace_size(batch, vocab, &need);
+    if (st != VEGAS_OK) return st;
+    if (gamma < 0 || gamma > 31) return fail(VEGAS_ERR_INVALID_ARGUMENT, "gamma %d outside 0..31", gamma);
+    if (!p || !u_sample || !n_accepted || !next_token || (gamma > 0 && (!q || !draft_tokens || !u_accept)))
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "p, q, draft_tokens, u_accept, u_sample, n_accepted and "
+                                                "next_token must be non-NULL (q, draft_tokens, u_accept may be "
+                                                "NULL when gamma is 0)");
+    if (workspace_bytes < need)
+        return fail(VEGAS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+    if (!workspace) return fail(VEGAS_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    vegas::AcceptArgs a{};
+    a.p = p;
+    a.q = q;
+    a.draft = draft_tokens;
+    a.u_accept = u_accept;
+    a.u_sample = u_sample;
+    a.n_accepted = n_accepted;
+    a.next_token = next_token;
+    a.batch = batch;
+    a.gamma = gamma;
+    a.vocab = vocab;
+    a.nchunks = (int)(((int64_t)vocab + vegas::kAcceptChunk - 1) / vegas::kAcceptChunk);
+    a.part = static_cast<uint64_t*>(workspace);
+    a.first_rej = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                             align_up((size_t)batch * a.nchunks * 2 * sizeof(uint64_t)));
+    return hip_status(vegas::launch_spec_accept(a, static_cast<hipStream_t>(stream)), "spec accept launch");
+}
+
 vegas_status_t vegas_select_workspace_size(int32_t batch, int32_t num_kv_heads, int32_t gamma,
                                            int32_t max_seqlen_k, int32_t total_kv, size_t* bytes) {
     if (batch < 1 || num_kv_heads < 1) return fail(VEGAS_ERR_INVALID_ARGUMENT, "batch and num_kv_heads must be >= 1");

@@ -64,6 +64,23 @@ struct AttnArgs {
     int32_t window;                // verification local mask: row r sees keys (L+r-window, L+r]; 0: none
 };
 
+// Speculative-sampling acceptance: two launches over kAcceptChunk-token chunks.
+constexpr int kAcceptChunk = 4096;
+struct AcceptArgs {
+    const float* p;                // [batch, gamma+1, vocab]
+    const float* q;                // [batch, gamma, vocab]
+    const int32_t* draft;          // [batch, gamma]
+    const float* u_accept;         // [batch, gamma]
+    const float* u_sample;         // [batch]
+    int32_t* n_accepted;           // [batch]
+    int32_t* next_token;           // [batch]
+    uint64_t* part;                // workspace [batch][nchunks][2]: residual and target mass sums
+    int32_t* first_rej;            // workspace [batch]
+    int32_t batch, gamma, nchunks;
+    int64_t vocab;
+};
+hipError_t launch_spec_accept(const AcceptArgs& a, hipStream_t stream);
+
 // Query-agnostic sink-plus-recent index lists.
 hipError_t launch_streaming_indices(int batch, int W, int sinks, const int32_t* cu_seqlens_k, int32_t total_kv,
                                     const int32_t* cu_idx, int32_t total_idx, int32_t* indices,

@@ -30,6 +30,7 @@ EXPORTED = (
     "vegas_sparse_decode_workspace_size", "vegas_sparse_decode_attn",
     "vegas_verify_paged_workspace_size", "vegas_verify_attn_paged", "vegas_sparse_decode_attn_paged",
     "vegas_verify_local_workspace_size", "vegas_verify_attn_local", "vegas_streaming_indices",
+    "vegas_spec_accept_workspace_size", "vegas_spec_accept",
 )
 
 
@@ -81,6 +82,8 @@ def lib():
             "vegas_verify_local_workspace_size": ([SP, I32, I32, I32, PSZ], ctypes.c_int),
             "vegas_verify_attn_local": ([SP, I32, P, P, P, P, I32, I32, I32, P, P, SZ, P], ctypes.c_int),
             "vegas_streaming_indices": ([I32, I32, I32, P, I32, P, I32, P, P], ctypes.c_int),
+            "vegas_spec_accept_workspace_size": ([I32, I32, PSZ], ctypes.c_int),
+            "vegas_spec_accept": ([I32, I32, I32, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -229,3 +232,21 @@ def vegas_streaming_indices(batch: int, gamma: int, sinks: int, cu_seqlens_k, to
     _check(lib().vegas_streaming_indices(batch, gamma, sinks, _ptr(cu_seqlens_k), total_kv, _ptr(cu_idx), total_idx,
                                          _ptr(indices), _stream(stream)),
            "vegas_streaming_indices")
+
+
+def vegas_spec_accept_workspace_size(batch: int, vocab: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().vegas_spec_accept_workspace_size(batch, vocab, ctypes.byref(n)), "vegas_spec_accept_workspace_size")
+    return n.value
+
+
+def vegas_spec_accept(batch: int, gamma: int, vocab: int, p, q, draft_tokens, u_accept, u_sample, n_accepted,
+                      next_token, workspace=None, stream=None) -> None:
+    """workspace: a device uint8 tensor of vegas_spec_accept_workspace_size bytes (allocated here if None)."""
+    if workspace is None:
+        import torch
+        workspace = torch.empty(vegas_spec_accept_workspace_size(batch, vocab), dtype=torch.uint8, device=p.device)
+    _check(lib().vegas_spec_accept(batch, gamma, vocab, _ptr(p), _ptr(q), _ptr(draft_tokens), _ptr(u_accept),
+                                   _ptr(u_sample), _ptr(n_accepted), _ptr(next_token), _ptr(workspace),
+                                   _nbytes(workspace), _stream(stream)),
+           "vegas_spec_accept")

@@ -274,3 +274,21 @@ def page_cache(wl: Workload, inp: dict, page_size: int, seed: int = 0, spare_pag
         if drop_contiguous:
             inp[name] = None
     return out
+
+
+def make_accept_inputs(batch: int, gamma: int, vocab: int, seed: int = 0, device="cpu", draft_noise: float = 0.6,
+                       temperature: float = 1.0) -> dict:
+    """Seeded inputs of the acceptance step: target rows p [batch, gamma+1, vocab] and draft
+    rows q [batch, gamma, vocab] (softmax of correlated random logits), draft tokens drawn from
+    q, and the uniforms the method draws.  Random numbers only."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed * 1000003 + 17)
+    base = torch.randn(batch, gamma + 1, vocab, generator=g) * 3.0
+    p = torch.softmax(base / temperature, dim=-1)
+    noisy = base[:, :gamma] + draft_noise * torch.randn(batch, gamma, vocab, generator=g)
+    q = torch.softmax(noisy / temperature, dim=-1)
+    draft = (torch.multinomial(q.reshape(-1, vocab), 1, generator=g).reshape(batch, gamma).to(torch.int32)
+             if gamma > 0 else torch.zeros(batch, 0, dtype=torch.int32))
+    out = {"p": p.float(), "q": q.float(), "draft": draft,
+           "u_accept": torch.rand(batch, gamma, generator=g), "u_sample": torch.rand(batch, generator=g)}
+    return {k: v.contiguous().to(device) for k, v in out.items()}
