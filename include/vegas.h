@@ -67,7 +67,7 @@ typedef enum { VEGAS_DTYPE_F32 = 0, VEGAS_DTYPE_BF16 = 1 } vegas_dtype_t;
 /* Attention geometry shared by the two attention entry points. */
 typedef struct {
     int32_t dtype;          /* vegas_dtype_t */
-    int32_t batch;          /* number of sequences, >= 1 */
+    int32_t batch;          /* number of sequences, 1 .. 1024 */
     int32_t num_q_heads;    /* Hq, a multiple of num_kv_heads */
     int32_t num_kv_heads;   /* Hkv >= 1 */
     int32_t head_dim;       /* D: 64 or 128 */

@@ -32,32 +32,29 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Workgroups the split kernel should expose: one round on the 256 CUs (the
 // kernel holds one workgroup per CU).  Each further round costs a workgroup's
 // start-up and drain on the critical path, about 10 us at 128K positions.
-constexpr int kVerifyWorkgroups = 256;
-constexpr int kGatherWorkgroups = 256;
+constexpr int kRoundWorkgroups = 256;
 
 struct AttnPlan {
     int mb = 0;          // 16-row query tiles per KV head
-    int chunk = 0;       // positions per split
-    int nsplit = 0;      // splits per (sequence, KV head)
+    int target = 0;      // splits per KV head for the whole batch, shared by length
+    int cap = 0;         // longest split
+    int nsplit = 0;      // most splits one (sequence, KV head) can get: partial slots
+    int max_units = 0;   // most (sequence, split) units over the batch: the grid per KV head
     size_t part_o = 0;   // bytes
     size_t part_ml = 0;  // bytes
-    size_t total() const { return align_up(part_o) + align_up(part_ml); }
+    size_t splits = 0;   // bytes: per-sequence split counts
+    size_t total() const { return align_up(part_o) + align_up(part_ml) + align_up(splits); }
 };
 
+// max_n: the most positions one sequence's pass covers.  The kernels derive
+// each sequence's splits from the device-side lengths (seq_plan in attn.hip);
+// this sizes the grid and the partial slots for any lengths up to max_n.
 AttnPlan plan_attn(bool bf16, int batch, int hkv, int M, int head_dim, int max_n, bool gather,
                    int page_size = 0) {
     AttnPlan p;
     p.mb = (M + 15) / 16;
     const int unit = vegas::kAttnWaves * vegas::kAttnBlock;
-    const int n = max_n > 0 ? max_n : 1;
-    const int units = batch * hkv;
-    const int target = gather ? kGatherWorkgroups : kVerifyWorkgroups;
-    int want = (target + units - 1) / units;
-    const int most = (n + unit - 1) / unit;
-    if (want > most) want = most;
-    if (want < 1) want = 1;
-    int chunk = (n + want - 1) / want;
-    chunk = (chunk + unit - 1) / unit * unit;
+    const int64_t n = max_n > 0 ? max_n : 1;
     // Both caps are multiples of `unit`.  Verification uses the same plan with
     // and without collection, so the two give bit-identical outputs.
     int cap = gather ? vegas::kMaxGatherChunk : vegas::collect_chunk_cap(bf16, head_dim);
@@ -66,12 +63,17 @@ AttnPlan plan_attn(bool bf16, int batch, int hkv, int M, int head_dim, int max_n
         const int64_t page_cap = (int64_t)(vegas::kMaxPagesPerSplit - 2) * page_size / unit * unit;
         if (page_cap < cap) cap = (int)page_cap;
     }
-    if (chunk > cap) chunk = cap;
-    p.chunk = chunk;
-    p.nsplit = (n + chunk - 1) / chunk;
+    p.cap = cap;
+    // Bounds of the device plan (seq_plan / batch_plan in attn.hip): a sequence
+    // gets at most max(target + 1, ceil(len / cap)) splits (the float share can
+    // round one up), the batch at most max(target, ceil(total / cap)) + 2 * batch.
+    p.target = std::max(1, kRoundWorkgroups / hkv);
+    p.nsplit = (int)std::max<int64_t>(p.target + 1, (n + cap - 1) / cap);
+    p.max_units = (int)std::max<int64_t>(p.target, (batch * n + cap - 1) / cap) + 2 * batch;
     const size_t slots = (size_t)batch * hkv * p.nsplit;
     p.part_o = slots * p.mb * 16 * head_dim * sizeof(float);
     p.part_ml = slots * p.mb * 16 * 2 * sizeof(float);
+    p.splits = (size_t)batch * sizeof(int32_t);
     return p;
 }
 
@@ -80,6 +82,8 @@ vegas_status_t check_shape(const vegas_attn_shape_t* s) {
     if (s->dtype != VEGAS_DTYPE_F32 && s->dtype != VEGAS_DTYPE_BF16)
         return fail(VEGAS_ERR_UNSUPPORTED, "dtype %d is not VEGAS_DTYPE_F32 or VEGAS_DTYPE_BF16", s->dtype);
     if (s->batch < 1) return fail(VEGAS_ERR_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", s->batch);
+    if (s->batch > vegas::kMaxBatch)
+        return fail(VEGAS_ERR_UNSUPPORTED, "batch %d exceeds %d", s->batch, vegas::kMaxBatch);
     if (s->num_q_heads < 1 || s->num_kv_heads < 1)
         return fail(VEGAS_ERR_INVALID_ARGUMENT, "head counts must be >= 1 (Hq=%d, Hkv=%d)",
                     s->num_q_heads, s->num_kv_heads);
@@ -254,6 +258,8 @@ vegas_status_t verify_impl(const vegas_attn_shape_t* shape, int32_t gamma, const
     a.cu_seqlens_k = cu_seqlens_k;
     a.part_o = static_cast<float*>(workspace);
     a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(plan.part_o));
+    a.seq_splits = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + align_up(plan.part_o) +
+                                              align_up(plan.part_ml));
     a.scores = scores;
     a.out = out;
     a.batch = shape->batch;
@@ -263,8 +269,10 @@ vegas_status_t verify_impl(const vegas_attn_shape_t* shape, int32_t gamma, const
     a.W = W;
     a.M = W * G;
     a.total_kv = total_kv;
-    a.chunk = plan.chunk;
+    a.target = plan.target;
+    a.chunk_cap = plan.cap;
     a.nsplit = plan.nsplit;
+    a.max_units = plan.max_units;
     a.scale = shape->softmax_scale;
     a.scale_log2 = shape->softmax_scale * 1.4426950408889634f;
     a.collect_mask = collect_mask;
@@ -310,6 +318,8 @@ vegas_status_t decode_impl(const vegas_attn_shape_t* shape, const void* q, const
     a.cu_idx = cu_idx;
     a.part_o = static_cast<float*>(workspace);
     a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(plan.part_o));
+    a.seq_splits = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + align_up(plan.part_o) +
+                                              align_up(plan.part_ml));
     a.scores = nullptr;
     a.out = out;
     a.batch = shape->batch;
@@ -319,8 +329,10 @@ vegas_status_t decode_impl(const vegas_attn_shape_t* shape, const void* q, const
     a.W = 1;
     a.M = G;
     a.total_kv = total_kv;
-    a.chunk = plan.chunk;
+    a.target = plan.target;
+    a.chunk_cap = plan.cap;
     a.nsplit = plan.nsplit;
+    a.max_units = plan.max_units;
     a.scale = shape->softmax_scale;
     a.scale_log2 = shape->softmax_scale * 1.4426950408889634f;
     a.collect_mask = 0u;

@@ -237,6 +237,107 @@ __device__ __forceinline__ void issue_block(const SplitCtx& c, int p0, int lane,
     }
 }
 
+// Positions of sequence b that a pass covers: [lo, lo + len) of its rows for
+// verification (lo > 0 only under a local mask), or its list for gathering.
+struct SeqSpan {
+    int seq0, n_b, L, lo, len, ib0;
+};
+template <bool GATHER>
+__device__ __forceinline__ SeqSpan seq_span(const AttnArgs& a, int b) {
+    SeqSpan s;
+    s.seq0 = min(max(a.cu_seqlens_k[b], 0), a.total_kv);
+    s.n_b = min(max(a.cu_seqlens_k[b + 1], s.seq0), a.total_kv) - s.seq0;
+    s.ib0 = 0;
+    if constexpr (GATHER) {
+        s.ib0 = a.cu_idx[b];
+        s.L = 0;
+        s.lo = 0;
+        s.len = s.n_b > 0 ? max(a.cu_idx[b + 1] - s.ib0, 0) : 0;
+    } else {
+        s.L = s.n_b - a.W;
+        s.lo = a.window > 0 ? max(0, s.L - a.window + 1) : 0;
+        s.len = max(s.n_b - s.lo, 0);
+    }
+    return s;
+}
+
+// Split plan of one sequence: a share of `target` splits (per KV head, for the
+// whole batch) proportional to its positions, but no split longer than
+// a.chunk_cap; split length a multiple of kAttnWaves*kAttnBlock.  Ragged
+// batches so get about equal work per workgroup.  Float arithmetic for the
+// share: every workgroup of a pass evaluates it identically.
+__device__ __forceinline__ void seq_plan(const AttnArgs& a, int len, float inv_total, int target, int& ns,
+                                         int& chunk) {
+    constexpr int unit = kAttnWaves * kAttnBlock;
+    if (len <= 0) {
+        ns = 0;
+        chunk = unit;
+        return;
+    }
+    // (an exact multiple of the share must not round up to the next split count)
+    int want = (int)ceilf((float)len * (float)target * inv_total - 1e-3f);
+    want = max(max(want, 1), (len + a.chunk_cap - 1) / a.chunk_cap);
+    chunk = (len + want - 1) / want;
+    chunk = (chunk + unit - 1) / unit * unit;
+    ns = min((len + chunk - 1) / chunk, a.nsplit);
+}
+
+// Sum of x over the workgroup (all threads get it).  red: kAttnWaves ints of LDS.
+__device__ __forceinline__ int wg_sum(int x, int* red) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+    __syncthreads();
+    int t = 0;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) t += red[w];
+    return t;
+}
+
+// The batch's split plan as every workgroup of a pass sees it.  Thread t holds
+// sequences t, t + blockDim, ... (at most kPlanPerThread of them).  The split
+// target is the largest one <= a.target whose units (rounded up per sequence)
+// fit in a.target, i.e. one round of workgroups when the LDS cap allows it;
+// ns/chunk receive this thread's sequences' plans.
+constexpr int kPlanPerThread = kMaxBatch / (kAttnWaves * 64);
+
+template <bool GATHER>
+__device__ __forceinline__ void batch_plan(const AttnArgs& a, int* red, int (&ns)[kPlanPerThread],
+                                           int (&chunk)[kPlanPerThread]) {
+    int len[kPlanPerThread];
+    int mine = 0;
+#pragma unroll
+    for (int k = 0; k < kPlanPerThread; ++k) {
+        const int b = k * kAttnWaves * 64 + threadIdx.x;
+        len[k] = b < a.batch ? seq_span<GATHER>(a, b).len : 0;
+        mine += len[k];
+    }
+    const int total = wg_sum(mine, red);
+    const float inv_total = total > 0 ? 1.f / (float)total : 0.f;
+    auto plan = [&](int t) {
+        int u = 0;
+#pragma unroll
+        for (int k = 0; k < kPlanPerThread; ++k) {
+            seq_plan(a, len[k], inv_total, t, ns[k], chunk[k]);
+            u += ns[k];
+        }
+        return wg_sum(u, red);
+    };
+    if (total <= 0 || plan(a.target) <= a.target) return;
+    int lo = 1, hi = a.target - 1, best = 1;   // the unit count does not decrease with t
+    while (lo <= hi) {
+        const int mid = (lo + hi) >> 1;
+        if (plan(mid) <= a.target) {
+            best = mid;
+            lo = mid + 1;
+        } else {
+            hi = mid - 1;
+        }
+    }
+    plan(best);
+}
+
 // Per-wave running state of the online softmax.
 template <bool BF16, int D, int MB>
 struct WaveState {
@@ -406,28 +507,58 @@ attn_split_kernel(const AttnArgs a) {
     const int lr = lane & 15;
     const int lg = lane >> 4;
 
-    int wg = blockIdx.x;
-    const int g = wg % a.hkv;
-    wg /= a.hkv;
-    const int split = wg % a.nsplit;
-    const int b = wg / a.nsplit;
-
-    const int seq0 = a.cu_seqlens_k[b];
-    const int n_b = min(a.cu_seqlens_k[b + 1], a.total_kv) - seq0;
-    int count, L, ib0 = 0;
-    if constexpr (GATHER) {
-        ib0 = a.cu_idx[b];
-        count = a.cu_idx[b + 1] - ib0;
-        L = 0;
-    } else {
-        count = n_b;
-        L = n_b - a.W;
+    // Workgroup -> (KV head g, sequence b, split): the units of all sequences'
+    // split plans, in order; workgroups past the last unit have no work.
+    // Workgroup 0 publishes every sequence's split count for the combine.
+    __shared__ int plan_red[kAttnWaves];
+    __shared__ int plan_s[3];
+    const int g = blockIdx.x % a.hkv;
+    const int unit_id = blockIdx.x / a.hkv;
+    int pns[kPlanPerThread], pch[kPlanPerThread];
+    batch_plan<GATHER>(a, plan_red, pns, pch);
+    if (threadIdx.x == 0) plan_s[0] = -1;
+    int before = 0;                                  // units of the sequences of earlier passes
+#pragma unroll
+    for (int k = 0; k < kPlanPerThread; ++k) {
+        if (k * kAttnWaves * 64 >= a.batch) break;   // uniform
+        const int bb = k * kAttnWaves * 64 + threadIdx.x;
+        const int ns = pns[k];
+        if (blockIdx.x == 0 && bb < a.batch) a.seq_splits[bb] = ns;
+        int v = ns;                                  // inclusive scan of ns over the threads
+        const int ln = threadIdx.x & 63;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(v, off);
+            if (ln >= off) v += y;
+        }
+        __syncthreads();
+        if (ln == 63) plan_red[threadIdx.x >> 6] = v;
+        __syncthreads();
+        int wbefore = 0, all = 0;
+#pragma unroll
+        for (int w = 0; w < kAttnWaves; ++w) {
+            wbefore += (w < (int)(threadIdx.x >> 6)) ? plan_red[w] : 0;
+            all += plan_red[w];
+        }
+        const int first_unit = before + wbefore + v - ns;
+        if (ns > 0 && unit_id >= first_unit && unit_id < first_unit + ns) {
+            plan_s[0] = bb;
+            plan_s[1] = unit_id - first_unit;
+            plan_s[2] = pch[k];
+        }
+        before += all;
     }
-    // Under a local mask no row sees a key before row 0's band.
-    const int lo = (!GATHER && a.window > 0) ? max(0, L - a.window + 1) : 0;
-    const int start = lo + split * a.chunk;
-    if (seq0 < 0 || n_b <= 0 || start >= count) return;          // uniform per workgroup
-    const int end = min(start + a.chunk, count);
+    __syncthreads();
+    const int b = plan_s[0];
+    if (b < 0) return;                                            // uniform per workgroup
+    const int split = plan_s[1], chunk = plan_s[2];
+    const SeqSpan sp = seq_span<GATHER>(a, b);
+    const int seq0 = sp.seq0, n_b = sp.n_b, L = sp.L, ib0 = sp.ib0;
+    // Under a local mask no row sees a key before row 0's band (sp.lo).
+    const int count = sp.lo + sp.len;
+    const int start = sp.lo + split * chunk;
+    if (n_b <= 0 || start >= count) return;                       // uniform per workgroup
+    const int end = min(start + chunk, count);
 
     WaveState<BF16, D, MB> ws;
 #pragma unroll
@@ -616,6 +747,7 @@ attn_split_kernel(const AttnArgs a) {
 // splits in turn (four loads in flight each) and their partial merges are
 // combined through LDS in a fixed order.
 constexpr int kCombineWaves = 4;
+static_assert(kCombineWaves == kAttnWaves, "batch_plan's workgroup reductions assume both kernels' width");
 
 template <bool BF16, int D, int MB, bool GATHER>
 __global__ void __launch_bounds__(kCombineWaves * 64) attn_combine_kernel(const AttnArgs a) {
@@ -637,12 +769,7 @@ __global__ void __launch_bounds__(kCombineWaves * 64) attn_combine_kernel(const 
     const int lg = lane >> 4;
     const int j = 16 * qb + lr;
 
-    const int seq0 = a.cu_seqlens_k[b];
-    const int n_b = min(a.cu_seqlens_k[b + 1], a.total_kv) - seq0;
-    const int lo = (!GATHER && a.window > 0) ? max(0, n_b - a.W - a.window + 1) : 0;
-    const int count = (GATHER ? (a.cu_idx[b + 1] - a.cu_idx[b]) : n_b) - lo;
-    int nsv = (seq0 >= 0 && n_b > 0 && count > 0) ? (count + a.chunk - 1) / a.chunk : 0;
-    nsv = min(nsv, a.nsplit);
+    const int nsv = min(max(a.seq_splits[b], 0), a.nsplit);    // published by the split kernel
 
     float mr = kNegInf, den = 0.f;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -712,7 +839,7 @@ __global__ void __launch_bounds__(kCombineWaves * 64) attn_combine_kernel(const 
 
 template <bool BF16, int D, int MB, bool GATHER, bool COLLECT>
 hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
-    const unsigned split_grid = (unsigned)(a.batch * a.hkv * a.nsplit);
+    const unsigned split_grid = (unsigned)(a.hkv * a.max_units);
     const unsigned comb_grid = (unsigned)(a.batch * a.hkv * MB * (D / 16));
     if (split_grid > 0)
         hipLaunchKernelGGL((attn_split_kernel<BF16, D, MB, GATHER, COLLECT>), dim3(split_grid),

@@ -20,6 +20,9 @@ constexpr int kMaxGatherChunk = 2048;
 // Paged KV cache: pool pages of one verification split, staged in LDS.
 constexpr int kMaxPagesPerSplit = 2048;
 constexpr int kMaxPageSize = 256;
+// Largest batch the attention passes take (their split plan keeps a few
+// sequences per thread in registers).
+constexpr int kMaxBatch = 1024;
 
 // Bytes of one workgroup's K/V ring.
 __host__ __device__ constexpr int attn_ring_bytes(bool bf16, int head_dim) {
@@ -27,16 +30,13 @@ __host__ __device__ constexpr int attn_ring_bytes(bool bf16, int head_dim) {
 }
 // Longest position range one workgroup takes in verification: the collected
 // scores of its range are buffered in LDS next to the ring (144 KB in all of
-// the 160 KB, leaving room for a paged cache's page list), at most 16896 positions, a multiple of kAttnWaves*kAttnBlock.
+// the 160 KB, leaving room for the wave merge of the widest row tiles and a
+// paged cache's page list); a multiple of kAttnWaves*kAttnBlock.
 __host__ __device__ constexpr int collect_chunk_cap(bool bf16, int head_dim) {
-    return ((144 * 1024 - attn_ring_bytes(bf16, head_dim)) / 4 / 64 * 64) < 16896
-               ? (144 * 1024 - attn_ring_bytes(bf16, head_dim)) / 4 / 64 * 64
-               : 16896;
+    return (144 * 1024 - attn_ring_bytes(bf16, head_dim)) / 4 / 64 * 64;
 }
 
 // Arguments of the split attention kernel and of its combine kernel.
-// One kernel serves both the verification pass (contiguous positions, causal
-// tail, optional collection) and the drafting pass (gathered positions).
 struct AttnArgs {
     const void* q;
     const void* k;
@@ -50,8 +50,15 @@ struct AttnArgs {
     void* out;                     // [batch*W, hq, D]
     int32_t batch, hq, hkv, G, W, M;   // M = W*G query rows per KV head
     int32_t total_kv;
-    int32_t chunk;                 // positions per split, multiple of kAttnWaves*kAttnBlock
-    int32_t nsplit;                // splits per (sequence, KV head)
+    // Split plan, derived per sequence on the device (each sequence gets a share
+    // of `target` splits per KV head proportional to its positions, none longer
+    // than chunk_cap): nsplit bounds any sequence's splits (the partial slots per
+    // (sequence, KV head)); max_units bounds the sum over sequences (the grid).
+    int32_t target;
+    int32_t chunk_cap;             // multiple of kAttnWaves*kAttnBlock
+    int32_t nsplit;
+    int32_t max_units;
+    int32_t* seq_splits;           // workspace [batch]: splits of each sequence (split kernel -> combine)
     float scale;                   // softmax scale s
     float scale_log2;              // s * log2(e)
     uint32_t collect_mask;
