@@ -676,12 +676,6 @@ attn_split_kernel(const AttnArgs a) {
 
     // Tree merge of the waves' (m, l, O) through LDS, in fragment order.
     __syncthreads();
-    if constexpr (COLLECT) {
-        // Coalesced write of the split's collected scores (prefix positions only).
-        float* dst = a.scores + (size_t)g * a.total_kv + seq0 + start;
-        const int nsc = min(end, L) - start;
-        for (int i = threadIdx.x; i < nsc; i += blockDim.x) dst[i] = score_s[i];
-    }
     float* fs = reinterpret_cast<float*>(smem);
     constexpr int SLOTF = GEO::MSLOT / 4;
 #pragma unroll
@@ -738,6 +732,23 @@ attn_split_kernel(const AttnArgs a) {
                 *pml = make_float2(ws.m_run[qb], ws.l_run[qb]);
             }
         }
+    }
+    if constexpr (COLLECT) {
+        // The split's collected scores (prefix positions only), written last:
+        // a workgroup barrier waits for the workgroup's outstanding stores, and
+        // none follows here.  16-byte stores from the first 16-byte boundary of
+        // the destination on; score_s was complete at the merge's first barrier.
+        float* dst = a.scores + (size_t)g * a.total_kv + seq0 + start;
+        const int nsc = min(end, L) - start;
+        const int peel = min((int)((4u - (uint32_t)(((uintptr_t)dst >> 2) & 3u)) & 3u), max(nsc, 0));
+        if ((int)threadIdx.x < peel) dst[threadIdx.x] = score_s[threadIdx.x];
+        const int nv = max(nsc - peel, 0) >> 2;
+        float4* dv = reinterpret_cast<float4*>(dst + peel);
+        for (int i = threadIdx.x; i < nv; i += blockDim.x) {
+            const float* sp = score_s + peel + 4 * i;
+            dv[i] = make_float4(sp[0], sp[1], sp[2], sp[3]);
+        }
+        for (int i = peel + 4 * nv + threadIdx.x; i < nsc; i += blockDim.x) dst[i] = score_s[i];
     }
 }
 

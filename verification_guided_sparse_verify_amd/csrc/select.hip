@@ -274,8 +274,8 @@ __global__ void __launch_bounds__(kSelThreads) sel_write_kernel(const SelectArgs
 #pragma unroll
     for (int e = 0; e < kCandPer; ++e) {
         const int i = e * kSelThreads + tid;
-        hk[e] = i < nc ? ck[i] : 0u;
-        hp[e] = i < nc ? cp[i] : 0;
+        hk[e] = ck[min(i, sg.L - 1)];        // issued with the count's load; slots >= nc unused
+        hp[e] = cp[min(i, sg.L - 1)];
     }
     // Visit every candidate (key, position) once: held ones first, then the rest
     // in batches of kCandPer loads per thread.
