@@ -222,6 +222,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2, help="0-based workload index (default: 128K Qwen3-8B step)")
     ap.add_argument("--layers", type=int, default=None, help="override the layer count (profiling runs only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="time verification and selection as two library calls instead of one")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--page-size", type=int, default=0,
                     help="keep every layer's KV cache as a randomly permuted page pool of this page size and "
@@ -287,11 +289,15 @@ def main():
 
     stream = torch.cuda.current_stream()
     bound = [st.bind(stream) for st in steps]     # ctypes arguments converted once
+    # Verification and selection as one library call where the path allows it.
+    fused = steps[0].fusable and not args.separate_calls
+    fused_calls = [st.bind_fused(stream) for st in steps] if fused else None
 
-    def one_step(verify_events=None, call_events=None):
+    def one_step(head_events=None, call_events=None):
         """One speculative iteration: verify + select on every layer, then gamma drafting
-        passes over every layer.  verify_events: list receiving an event pair around every
-        verify call; call_events: dict receiving event pairs around every call."""
+        passes over every layer.  head_events: list receiving an event pair around every
+        verify (separate calls) or verify+select (one call); call_events: dict receiving
+        event pairs around every call of the separate-call path."""
         def timed(kind, fn, sink):
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
@@ -300,21 +306,23 @@ def main():
             b.record(stream)
             sink[kind].append((a, b))
 
-        for verify, _, select, _ in bound:
+        for li, (verify, _, select, _) in enumerate(bound):
             if call_events is not None:
                 timed("verify", verify, call_events)
                 timed("select", select, call_events)
                 continue
-            if verify_events is not None:
+            head = fused_calls[li] if fused else verify
+            if head_events is not None:
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
                 a.record(stream)
-                verify()
+                head()
                 b.record(stream)
-                verify_events.append((a, b))
+                head_events.append((a, b))
             else:
-                verify()
-            select()
+                head()
+            if not fused:
+                select()
         for j in range(wl.n_drafts):
             for _, _, _, drafts in bound:
                 if call_events is not None:
@@ -325,10 +333,10 @@ def main():
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
-    verify_pairs = []
+    head_pairs = []
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        one_step(verify_events=verify_pairs)
+        one_step(head_events=head_pairs)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
@@ -340,7 +348,15 @@ def main():
     per = {k: [a.elapsed_time(b) * 1e3 for a, b in v] for k, v in call_pairs.items()}   # microseconds
     mean = {k: statistics.fmean(v) for k, v in per.items()}
     med = {k: statistics.median(v) for k, v in per.items()}
-    verify_us = [a.elapsed_time(b) * 1e3 for a, b in verify_pairs]
+    head_us = [a.elapsed_time(b) * 1e3 for a, b in head_pairs]
+    if fused:
+        # The timed region runs verification + selection as one call; the verification
+        # kernels' own duration comes from the separate-call steps of the breakdown.
+        verify_us = per["verify"]
+        mean["verify_select"] = statistics.fmean(head_us)
+        med["verify_select"] = statistics.median(head_us)
+    else:
+        verify_us = head_us
     verify_mean = statistics.fmean(verify_us)
 
     ms_per_step = elapsed * 1e3 / args.steps
@@ -391,8 +407,12 @@ def main():
             "algorithmic_bytes_per_launch": ab["verify"],
             "avg_launch_us": round(verify_mean, 2),
             "launches_timed": len(verify_us),
+            "timed_in": ("separate-call breakdown steps after the timed region (which runs verification "
+                         "and selection as one call)" if fused else "the timed region"),
         },
     }
+    result["config"]["calls"] = ("vegas_verify_select + gamma x vegas_sparse_decode_attn per layer" if fused else
+                                 "verify, select and gamma sparse-decode calls per layer")
 
     # Plain verification (collection off) on the same layers, for the collection + select overhead.
     plain = []
@@ -407,7 +427,10 @@ def main():
     torch.cuda.synchronize()
     plain_us = statistics.fmean(a.elapsed_time(b) * 1e3 for a, b in plain)
     result["plain_verify_us"] = round(plain_us, 2)
-    result["collect_select_overhead_vs_plain_verify"] = round((verify_mean + mean["select"]) / plain_us - 1, 4)
+    separate = (mean["verify"] + mean["select"]) / plain_us - 1
+    result["collect_select_overhead_vs_plain_verify"] = round(
+        (mean["verify_select"] if fused else verify_mean + mean["select"]) / plain_us - 1, 4)
+    result["collect_select_overhead_separate_calls"] = round(separate, 4)
 
     if cpu_leg:
         result["cpu_baseline"] = cpu_baseline(wl, layer_inputs, args.cpu_seconds)

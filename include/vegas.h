@@ -145,6 +145,36 @@ vegas_status_t vegas_select_topk(int32_t batch, int32_t num_kv_heads, int32_t ga
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Verification followed by selection, in one call.
+ * The two steps of "Vegas ..." sec. 3 (verification with Collect-2-Query,
+ * then the top-k of the summed logits, summary sec. 2A) as they follow each
+ * other in a decoding iteration.  Results are those of vegas_verify_attn and
+ * then vegas_select_topk with the same arguments, bit for bit: out, scores
+ * and indices are written as described there.  The difference is the launch
+ * sequence: the selection's histogram clearing rides on the verification's
+ * split kernel and its score summation on the verification's combine
+ * kernel, which saves two kernel launches per call.
+ *
+ *  collect_mask   must be non-zero (VEGAS_ERR_INVALID_ARGUMENT otherwise).
+ *  cu_k, indices  as for vegas_select_topk.
+ *  workspace      at least vegas_verify_select_workspace_size bytes (the
+ *                 verification workspace, rounded up to 256 bytes, then the
+ *                 selection workspace); contents undefined between calls.
+ * Errors: those of both calls; nothing is launched unless every argument of
+ * both steps is valid.
+ */
+vegas_status_t vegas_verify_select_workspace_size(const vegas_attn_shape_t* shape, int32_t gamma,
+                                                  int32_t max_seqlen_k, int32_t total_kv,
+                                                  size_t* bytes);
+vegas_status_t vegas_verify_select(const vegas_attn_shape_t* shape, int32_t gamma,
+                                   const void* q, const void* k, const void* v,
+                                   const int32_t* cu_seqlens_k, int32_t max_seqlen_k,
+                                   int32_t total_kv, uint32_t collect_mask,
+                                   const int32_t* cu_k, float* scores, int32_t* indices,
+                                   void* out, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/*
  * Sparse drafting attention over selected tokens.
  * Defined by "Vegas ..." sec. 4 "Serving framework integration" (paged
  * attention with a page size of one token whose page indices are the

@@ -191,3 +191,33 @@ def test_spec_accept_argument_errors(V):
     assert L.vegas_spec_accept(2, 3, 100, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == 1
     assert L.vegas_spec_accept(2, 3, 100, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, ws, None) == 1
     assert L.vegas_spec_accept(2, 3, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == 3
+
+
+def test_verify_select_sizes_and_argument_errors(V):
+    s = shape(V)
+    L = V.lib()
+    need = V.vegas_verify_select_workspace_size(s, 4, 1000, 4000)
+    vb = V.vegas_verify_workspace_size(s, 4, 1000)
+    sb = V.vegas_select_workspace_size(4, 8, 4, 1000, 4000)
+    assert need == (vb + 255) // 256 * 256 + sb
+
+    def call(**kw):
+        p = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, maxs=1000, total=4000, mask=1 | 16, cu_k=FAKE, scores=FAKE,
+                 idx=FAKE, out=FAKE, ws=FAKE, wsb=need)
+        p.update(kw)
+        return L.vegas_verify_select(ctypes.byref(s), 4, p["q"], p["k"], p["v"], p["cu"], p["maxs"], p["total"],
+                                     p["mask"], p["cu_k"], p["scores"], p["idx"], p["out"], p["ws"], p["wsb"],
+                                     None)
+
+    assert call(mask=0) == 1                 # nothing collected, nothing to select from
+    assert call(cu_k=None) == 1
+    assert call(idx=None) == 1
+    assert call(scores=None) == 1
+    assert call(q=None) == 1
+    assert call(mask=1 << 5) == 1
+    assert call(wsb=need - 1) == 3
+    assert call(ws=None) == 1
+    assert call(maxs=3) == 1
+    with pytest.raises(V.VegasError) as e:   # the selection's own limit on the prefix length
+        V.vegas_verify_select_workspace_size(s, 4, 2048 * 4096 + 1, 4 * (2048 * 4096 + 1))
+    assert e.value.status == 2

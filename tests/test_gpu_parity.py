@@ -373,3 +373,48 @@ def test_spec_accept_greedy_and_forced_rejections():
     torch.cuda.synchronize()
     n_ref, t_ref = oracle.spec_accept(p.numpy(), q.numpy(), draft.numpy(), ua.numpy(), us.numpy())
     assert np.array_equal(n.cpu().numpy(), n_ref) and np.array_equal(t.cpu().numpy(), t_ref)
+
+
+FUSED_CASES = [
+    # dtype, batch, Hq, Hkv, D, gamma, prefix lengths, ratio
+    ("bf16", 3, 16, 4, 128, 3, [1000, 4097, 129], Fraction(5, 100)),
+    ("f32", 2, 8, 2, 64, 2, [300, 77], Fraction(5, 100)),
+    ("bf16", 2, 16, 8, 64, 3, [777, 12000], Fraction(1)),
+    ("bf16", 2, 4, 2, 64, 2, [0, 10], Fraction(1, 2)),
+    ("bf16", 4, 32, 8, 128, 4, [3000, 1, 200, 9999], Fraction(5, 100)),
+    ("bf16", 1, 64, 8, 128, 6, [2000], Fraction(10, 100)),
+    "gpt-oss-ragged",
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES,
+                         ids=lambda c: c if isinstance(c, str) else f"{c[0]}-B{c[1]}-{c[2]}x{c[3]}-D{c[4]}-g{c[5]}-L{c[6]}")
+def test_verify_select_one_call_equals_two_calls(case):
+    """vegas_verify_select gives the outputs, scores and selection of vegas_verify_attn followed
+    by vegas_select_topk bit for bit, whatever its workspace held before (its histograms are
+    cleared inside the call), twice in a row."""
+    if isinstance(case, str):
+        wl = W.named_workload(4)
+    else:
+        dtype, B, hq, hkv, d, gamma, prefixes, ratio = case
+        wl = W.custom_workload(dtype, B, hq, hkv, d, gamma, prefixes, ratio=ratio)
+    log(f"case: one-call verify+select {wl.name}")
+    inp, st = run_layer(wl, seed=5)
+    cu, cuk = wl.cu_seqlens(), wl.cu_k()
+    ws = torch.full((V.vegas_verify_select_workspace_size(st.shape, wl.gamma, st.max_seqlen, st.total_kv),),
+                    0xA5, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        out = torch.empty_like(st.out)
+        scores = torch.full_like(st.scores, float("nan"))
+        idx = torch.full_like(st.indices, -7)
+        V.vegas_verify_select(st.shape, wl.gamma, inp["q"], inp["k"], inp["v"], inp["cu_seqlens_k"], st.max_seqlen,
+                              st.total_kv, st.collect_mask, inp["cu_k"], scores, idx, out, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.uint8), st.out.view(torch.uint8)), rep
+        for b in range(wl.batch):
+            s0, L = cu[b], wl.prefix_lens[b]
+            assert torch.equal(scores[:, s0:s0 + L], st.scores[:, s0:s0 + L]), (rep, b)
+        assert torch.equal(idx[: cuk[-1]], st.indices[: cuk[-1]]), rep
+        ws.fill_(0xFF if rep == 0 else 0x00)
+    if not isinstance(case, str):
+        check_layer(wl, inp, st)

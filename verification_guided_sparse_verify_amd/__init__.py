@@ -10,6 +10,7 @@ from .vegas import (  # noqa: F401
     AttnShape, VegasError, attn_shape, lib, status_string,
     vegas_abi_version, vegas_verify_workspace_size, vegas_verify_attn,
     vegas_select_workspace_size, vegas_select_topk,
+    vegas_verify_select_workspace_size, vegas_verify_select,
     vegas_sparse_decode_workspace_size, vegas_sparse_decode_attn,
     PagedKV, paged_kv, vegas_verify_paged_workspace_size, vegas_verify_attn_paged,
     vegas_sparse_decode_attn_paged, vegas_verify_local_workspace_size, vegas_verify_attn_local,

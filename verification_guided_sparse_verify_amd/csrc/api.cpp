@@ -217,7 +217,8 @@ int verify_span(int32_t max_seqlen_k, int32_t gamma, int32_t window) {
 vegas_status_t verify_impl(const vegas_attn_shape_t* shape, int32_t gamma, const void* q, const void* k,
                            const void* v, const vegas_paged_kv_t* pages, const int32_t* cu_seqlens_k,
                            int32_t max_seqlen_k, int32_t total_kv, uint32_t collect_mask, float* scores,
-                           void* out, void* workspace, size_t workspace_bytes, void* stream, int32_t window = 0) {
+                           void* out, void* workspace, size_t workspace_bytes, void* stream, int32_t window = 0,
+                           const vegas::SelectArgs* fused = nullptr) {
     vegas_status_t st = check_shape(shape);
     if (st != VEGAS_OK) return st;
     if ((st = check_gamma(gamma, shape)) != VEGAS_OK) return st;
@@ -283,9 +284,44 @@ vegas_status_t verify_impl(const vegas_attn_shape_t* shape, int32_t gamma, const
         a.max_pages = pages->max_pages_per_seq;
         a.num_pages = pages->num_pages;
     }
+    if (fused) {
+        a.sel_zero = fused->zeroed;
+        a.sel_zero_n = vegas::select_zeroed_words(fused->batch);
+    }
     return hip_status(vegas::launch_attn(a, shape->dtype == VEGAS_DTYPE_BF16, shape->head_dim, plan.mb,
-                                         false, collect_mask != 0u, static_cast<hipStream_t>(stream)),
+                                         false, collect_mask != 0u, static_cast<hipStream_t>(stream), fused),
                       "verify launch");
+}
+
+// Selection arguments over a workspace of at least plan.total() bytes.
+vegas::SelectArgs select_args(const SelectPlan& plan, int32_t batch, int32_t num_kv_heads, int32_t gamma,
+                              const float* scores, const int32_t* cu_seqlens_k, int32_t total_kv,
+                              const int32_t* cu_k, int32_t* indices, void* workspace) {
+    char* ws = static_cast<char*>(workspace);
+    auto take = [&ws](size_t n) {
+        char* p = ws;
+        ws += align_up(n);
+        return p;
+    };
+    vegas::SelectArgs a{};
+    a.scores = scores;
+    a.cu_seqlens_k = cu_seqlens_k;
+    a.cu_k = cu_k;
+    a.indices = indices;
+    a.keys = reinterpret_cast<uint32_t*>(take(plan.keys));
+    a.cand_key = reinterpret_cast<uint32_t*>(take(plan.cand_key));
+    a.cand_pos = reinterpret_cast<int32_t*>(take(plan.cand_pos));
+    a.zeroed = reinterpret_cast<uint32_t*>(take(plan.zeroed));
+    a.seq_info = reinterpret_cast<uint32_t*>(take(plan.seq_info));
+    a.chunk_above = reinterpret_cast<uint32_t*>(take(plan.chunk));
+    a.chunk_off = reinterpret_cast<uint32_t*>(take(plan.chunk));
+    a.chunk_ties = reinterpret_cast<uint32_t*>(take(plan.chunk));
+    a.batch = batch;
+    a.hkv = num_kv_heads;
+    a.W = gamma + 1;
+    a.total_kv = total_kv;
+    a.nchunks = plan.nchunks;
+    return a;
 }
 
 vegas_status_t decode_impl(const vegas_attn_shape_t* shape, const void* q, const void* k, const void* v,
@@ -469,32 +505,45 @@ vegas_status_t vegas_select_topk(int32_t batch, int32_t num_kv_heads, int32_t ga
     if (workspace_bytes < need)
         return fail(VEGAS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
     if (!workspace) return fail(VEGAS_ERR_INVALID_ARGUMENT, "workspace is NULL");
-    const SelectPlan plan = plan_select(batch, max_seqlen_k, total_kv);
-    char* ws = static_cast<char*>(workspace);
-    auto take = [&ws](size_t n) {
-        char* p = ws;
-        ws += align_up(n);
-        return p;
-    };
-    vegas::SelectArgs a{};
-    a.scores = scores;
-    a.cu_seqlens_k = cu_seqlens_k;
-    a.cu_k = cu_k;
-    a.indices = indices;
-    a.keys = reinterpret_cast<uint32_t*>(take(plan.keys));
-    a.cand_key = reinterpret_cast<uint32_t*>(take(plan.cand_key));
-    a.cand_pos = reinterpret_cast<int32_t*>(take(plan.cand_pos));
-    a.zeroed = reinterpret_cast<uint32_t*>(take(plan.zeroed));
-    a.seq_info = reinterpret_cast<uint32_t*>(take(plan.seq_info));
-    a.chunk_above = reinterpret_cast<uint32_t*>(take(plan.chunk));
-    a.chunk_off = reinterpret_cast<uint32_t*>(take(plan.chunk));
-    a.chunk_ties = reinterpret_cast<uint32_t*>(take(plan.chunk));
-    a.batch = batch;
-    a.hkv = num_kv_heads;
-    a.W = gamma + 1;
-    a.total_kv = total_kv;
-    a.nchunks = plan.nchunks;
+    const vegas::SelectArgs a = select_args(plan_select(batch, max_seqlen_k, total_kv), batch, num_kv_heads,
+                                            gamma, scores, cu_seqlens_k, total_kv, cu_k, indices, workspace);
     return hip_status(vegas::launch_select(a, static_cast<hipStream_t>(stream)), "select launch");
+}
+
+vegas_status_t vegas_verify_select_workspace_size(const vegas_attn_shape_t* shape, int32_t gamma,
+                                                  int32_t max_seqlen_k, int32_t total_kv, size_t* bytes) {
+    if (!bytes) return fail(VEGAS_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    size_t vb = 0, sb = 0;
+    vegas_status_t st = vegas_verify_workspace_size(shape, gamma, max_seqlen_k, &vb);
+    if (st != VEGAS_OK) return st;
+    st = vegas_select_workspace_size(shape->batch, shape->num_kv_heads, gamma, max_seqlen_k, total_kv, &sb);
+    if (st != VEGAS_OK) return st;
+    *bytes = align_up(vb) + sb;
+    return VEGAS_OK;
+}
+
+vegas_status_t vegas_verify_select(const vegas_attn_shape_t* shape, int32_t gamma, const void* q, const void* k,
+                                   const void* v, const int32_t* cu_seqlens_k, int32_t max_seqlen_k,
+                                   int32_t total_kv, uint32_t collect_mask, const int32_t* cu_k, float* scores,
+                                   int32_t* indices, void* out, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+    size_t need = 0, vb = 0;
+    vegas_status_t st = vegas_verify_select_workspace_size(shape, gamma, max_seqlen_k, total_kv, &need);
+    if (st != VEGAS_OK) return st;
+    if (collect_mask == 0u)
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "collect_mask is 0: there are no scores to select from");
+    if (!cu_k || !indices) return fail(VEGAS_ERR_INVALID_ARGUMENT, "cu_k and indices must be non-NULL");
+    if (workspace_bytes < need)
+        return fail(VEGAS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+    if (!workspace) return fail(VEGAS_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    vegas_verify_workspace_size(shape, gamma, max_seqlen_k, &vb);
+    const vegas::SelectArgs sa =
+        select_args(plan_select(shape->batch, max_seqlen_k, total_kv), shape->batch, shape->num_kv_heads, gamma,
+                    scores, cu_seqlens_k, total_kv, cu_k, indices, static_cast<char*>(workspace) + align_up(vb));
+    if ((st = verify_impl(shape, gamma, q, k, v, nullptr, cu_seqlens_k, max_seqlen_k, total_kv, collect_mask,
+                          scores, out, workspace, vb, stream, 0, &sa)) != VEGAS_OK)
+        return st;
+    return hip_status(vegas::launch_select_tail(sa, static_cast<hipStream_t>(stream)), "select launch");
 }
 
 vegas_status_t vegas_sparse_decode_workspace_size(const vegas_attn_shape_t* shape, int32_t max_idx,

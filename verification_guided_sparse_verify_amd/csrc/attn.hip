@@ -34,6 +34,7 @@
 // collected scores of the split are written with coalesced stores;
 // attn_combine merges the splits.
 #include "internal.h"
+#include "select_device.h"
 
 namespace vegas {
 namespace {
@@ -507,6 +508,11 @@ attn_split_kernel(const AttnArgs a) {
     const int lr = lane & 15;
     const int lg = lane >> 4;
 
+    // Fused selection: clear its histograms and counts (read after this launch).
+    if (a.sel_zero)
+        for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.sel_zero_n; i += gridDim.x * blockDim.x)
+            a.sel_zero[i] = 0u;
+
     // Workgroup -> (KV head g, sequence b, split): the units of all sequences'
     // split plans, in order; workgroups past the last unit have no work.
     // Workgroup 0 publishes every sequence's split count for the combine.
@@ -760,13 +766,18 @@ attn_split_kernel(const AttnArgs a) {
 constexpr int kCombineWaves = 4;
 static_assert(kCombineWaves == kAttnWaves, "batch_plan's workgroup reductions assume both kernels' width");
 
-template <bool BF16, int D, int MB, bool GATHER>
-__global__ void __launch_bounds__(kCombineWaves * 64) attn_combine_kernel(const AttnArgs a) {
+// KEYS (fused verification + selection): afterwards the workgroups run the
+// selection's first step (sel_keys_chunk) over the (sequence, chunk) units
+// of sa, the scores being complete once the split kernel has ended.
+template <bool BF16, int D, int MB, bool GATHER, bool KEYS>
+__global__ void __launch_bounds__(kCombineWaves * 64) attn_combine_kernel(const AttnArgs a, const SelectArgs sa) {
     constexpr int DB = D / 16;
     constexpr int NREG = DB * MB;
     constexpr int U = 4;
     __shared__ f32x4_t acc_s[kCombineWaves - 1][64];
     __shared__ float2 md_s[kCombineWaves - 1][64];
+    __shared__ uint32_t keys_h[KEYS ? kSelBins : 1];
+    static_assert(!KEYS || kCombineWaves * 64 == kSelThreads, "sel_keys_chunk takes kSelThreads threads");
     int wg = blockIdx.x;
     const int db = wg % DB;
     wg /= DB;
@@ -815,85 +826,98 @@ __global__ void __launch_bounds__(kCombineWaves * 64) attn_combine_kernel(const 
         md_s[wave - 1][lane] = make_float2(mr, den);
     }
     __syncthreads();
-    if (wave > 0) return;
+    if (wave == 0) {
 #pragma unroll
-    for (int w = 0; w < kCombineWaves - 1; ++w) {
-        const float2 md = md_s[w][lane];
-        if (md.x == kNegInf) continue;
-        const f32x4_t ob = acc_s[w][lane];
-        const float mm = fmaxf(mr, md.x);
-        const float ca = fast_exp2(mr - mm);
-        const float cb = fast_exp2(md.x - mm);
-        acc = ca * acc + cb * ob;
-        den = ca * den + cb * md.y;
-        mr = mm;
+        for (int w = 0; w < kCombineWaves - 1; ++w) {
+            const float2 md = md_s[w][lane];
+            if (md.x == kNegInf) continue;
+            const f32x4_t ob = acc_s[w][lane];
+            const float mm = fmaxf(mr, md.x);
+            const float ca = fast_exp2(mr - mm);
+            const float cb = fast_exp2(md.x - mm);
+            acc = ca * acc + cb * ob;
+            den = ca * den + cb * md.y;
+            mr = mm;
+        }
+        if (j < a.M) {
+            const float inv = den > 0.f ? 1.f / den : 0.f;
+            acc *= inv;
+            const int r = j / a.G;
+            const int hl = j % a.G;
+            const size_t orow = ((size_t)(b * a.W + r) * a.hq + (size_t)g * a.G + hl) * D + 16 * db + 4 * lg;
+            if constexpr (BF16) {
+                typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+                bf16x4_t h;
+                h[0] = static_cast<__bf16>(acc[0]);
+                h[1] = static_cast<__bf16>(acc[1]);
+                h[2] = static_cast<__bf16>(acc[2]);
+                h[3] = static_cast<__bf16>(acc[3]);
+                *reinterpret_cast<bf16x4_t*>(static_cast<uint16_t*>(a.out) + orow) = h;
+            } else {
+                *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + orow) = acc;
+            }
+        }
     }
-    if (j >= a.M) return;
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    acc *= inv;
-
-    const int r = j / a.G;
-    const int hl = j % a.G;
-    const size_t orow = ((size_t)(b * a.W + r) * a.hq + (size_t)g * a.G + hl) * D + 16 * db + 4 * lg;
-    if constexpr (BF16) {
-        typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-        bf16x4_t h;
-        h[0] = static_cast<__bf16>(acc[0]);
-        h[1] = static_cast<__bf16>(acc[1]);
-        h[2] = static_cast<__bf16>(acc[2]);
-        h[3] = static_cast<__bf16>(acc[3]);
-        *reinterpret_cast<bf16x4_t*>(static_cast<uint16_t*>(a.out) + orow) = h;
-    } else {
-        *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + orow) = acc;
+    if constexpr (KEYS) {
+        const int units = sa.batch * sa.nchunks;
+        for (int u = blockIdx.x; u < units; u += gridDim.x) sel_keys_chunk(sa, u / sa.nchunks, u % sa.nchunks, keys_h);
     }
 }
 
 template <bool BF16, int D, int MB, bool GATHER, bool COLLECT>
-hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_t(const AttnArgs& a, hipStream_t stream, const SelectArgs* sel) {
     const unsigned split_grid = (unsigned)(a.hkv * a.max_units);
     const unsigned comb_grid = (unsigned)(a.batch * a.hkv * MB * (D / 16));
     if (split_grid > 0)
         hipLaunchKernelGGL((attn_split_kernel<BF16, D, MB, GATHER, COLLECT>), dim3(split_grid),
                            dim3(kAttnWaves * 64), 0, stream, a);
-    if (comb_grid > 0)
-        hipLaunchKernelGGL((attn_combine_kernel<BF16, D, MB, GATHER>), dim3(comb_grid), dim3(kCombineWaves * 64), 0,
-                           stream, a);
+    if (comb_grid > 0) {
+        if constexpr (COLLECT && !GATHER) {
+            if (sel) {
+                hipLaunchKernelGGL((attn_combine_kernel<BF16, D, MB, GATHER, true>), dim3(comb_grid),
+                                   dim3(kCombineWaves * 64), 0, stream, a, *sel);
+                return hipGetLastError();
+            }
+        }
+        hipLaunchKernelGGL((attn_combine_kernel<BF16, D, MB, GATHER, false>), dim3(comb_grid),
+                           dim3(kCombineWaves * 64), 0, stream, a, SelectArgs{});
+    }
     return hipGetLastError();
 }
 
 template <bool BF16, int D, bool GATHER, bool COLLECT>
-hipError_t launch_mb(const AttnArgs& a, int mb, hipStream_t s) {
-    if (mb == 1) return launch_t<BF16, D, 1, GATHER, COLLECT>(a, s);
-    if (mb == 2) return launch_t<BF16, D, 2, GATHER, COLLECT>(a, s);
+hipError_t launch_mb(const AttnArgs& a, int mb, hipStream_t s, const SelectArgs* sel) {
+    if (mb == 1) return launch_t<BF16, D, 1, GATHER, COLLECT>(a, s, sel);
+    if (mb == 2) return launch_t<BF16, D, 2, GATHER, COLLECT>(a, s, sel);
     // fp32 at D = 128 stops at 32 rows per KV head (LDS budget)
     if constexpr (BF16 || D == 64) {
-        if (mb == 3) return launch_t<BF16, D, 3, GATHER, COLLECT>(a, s);
-        if (mb == 4) return launch_t<BF16, D, 4, GATHER, COLLECT>(a, s);
+        if (mb == 3) return launch_t<BF16, D, 3, GATHER, COLLECT>(a, s, sel);
+        if (mb == 4) return launch_t<BF16, D, 4, GATHER, COLLECT>(a, s, sel);
     }
     return hipErrorInvalidValue;
 }
 
 template <bool BF16, bool GATHER, bool COLLECT>
-hipError_t launch_d(const AttnArgs& a, int d, int mb, hipStream_t s) {
-    if (d == 64) return launch_mb<BF16, 64, GATHER, COLLECT>(a, mb, s);
-    if (d == 128) return launch_mb<BF16, 128, GATHER, COLLECT>(a, mb, s);
+hipError_t launch_d(const AttnArgs& a, int d, int mb, hipStream_t s, const SelectArgs* sel) {
+    if (d == 64) return launch_mb<BF16, 64, GATHER, COLLECT>(a, mb, s, sel);
+    if (d == 128) return launch_mb<BF16, 128, GATHER, COLLECT>(a, mb, s, sel);
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_attn(const AttnArgs& a, bool bf16, int head_dim, int mblocks, bool gather,
-                       bool collect, hipStream_t stream) {
+                       bool collect, hipStream_t stream, const SelectArgs* sel) {
     if (gather) {
-        return bf16 ? launch_d<true, true, false>(a, head_dim, mblocks, stream)
-                    : launch_d<false, true, false>(a, head_dim, mblocks, stream);
+        return bf16 ? launch_d<true, true, false>(a, head_dim, mblocks, stream, nullptr)
+                    : launch_d<false, true, false>(a, head_dim, mblocks, stream, nullptr);
     }
     if (collect) {
-        return bf16 ? launch_d<true, false, true>(a, head_dim, mblocks, stream)
-                    : launch_d<false, false, true>(a, head_dim, mblocks, stream);
+        return bf16 ? launch_d<true, false, true>(a, head_dim, mblocks, stream, sel)
+                    : launch_d<false, false, true>(a, head_dim, mblocks, stream, sel);
     }
-    return bf16 ? launch_d<true, false, false>(a, head_dim, mblocks, stream)
-                : launch_d<false, false, false>(a, head_dim, mblocks, stream);
+    return bf16 ? launch_d<true, false, false>(a, head_dim, mblocks, stream, nullptr)
+                : launch_d<false, false, false>(a, head_dim, mblocks, stream, nullptr);
 }
 
 }  // namespace vegas

@@ -69,6 +69,11 @@ struct AttnArgs {
     int32_t num_pages;
     int32_t page_shift;            // log2(page size); -1: contiguous varlen cache
     int32_t window;                // verification local mask: row r sees keys (L+r-window, L+r]; 0: none
+    // Fused selection (verification with collection only): the split kernel
+    // clears sel_zero[0 .. sel_zero_n) and the combine kernel runs the
+    // selection's first step on the finished scores.  NULL: not fused.
+    uint32_t* sel_zero;
+    int32_t sel_zero_n;
 };
 
 // Speculative-sampling acceptance: two launches over kAcceptChunk-token chunks.
@@ -92,9 +97,6 @@ hipError_t launch_spec_accept(const AcceptArgs& a, hipStream_t stream);
 hipError_t launch_streaming_indices(int batch, int W, int sinks, const int32_t* cu_seqlens_k, int32_t total_kv,
                                     const int32_t* cu_idx, int32_t total_idx, int32_t* indices,
                                     hipStream_t stream);
-
-hipError_t launch_attn(const AttnArgs& a, bool bf16, int head_dim, int mblocks, bool gather,
-                       bool collect, hipStream_t stream);
 
 struct SelectArgs {
     const float* scores;           // [hkv, total_kv]
@@ -121,6 +123,16 @@ constexpr int kSelChunk = kSelThreads * kSelPer;  // positions per chunk workgro
 constexpr int kSelChunkShift = 11;
 constexpr int kSelMaxChunks = 4096;               // longest prefix: kSelMaxChunks * kSelChunk
 
+// sel: non-NULL for the fused verification + selection path (collect only).
+hipError_t launch_attn(const AttnArgs& a, bool bf16, int head_dim, int mblocks, bool gather,
+                       bool collect, hipStream_t stream, const SelectArgs* sel = nullptr);
+
+// Words of a.zeroed: per-sequence histograms, then candidate counts.
+__host__ __device__ constexpr int select_zeroed_words(int batch) { return batch * kSelBins + batch; }
+
+// All four selection launches (zero, keys, cand, write) ...
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+// ... or the last two, after a fused verification pass did zero and keys.
+hipError_t launch_select_tail(const SelectArgs& a, hipStream_t stream);
 
 }  // namespace vegas

@@ -25,32 +25,10 @@
 //             the output offset and tie share of each chunk before it; then
 //             writes its selected positions in ascending order at its offset.
 #include "internal.h"
+#include "select_device.h"
 
 namespace vegas {
 namespace {
-
-__device__ __forceinline__ uint32_t order_key(float f) {
-    f = f + 0.0f;                             // -0 and +0 share one key
-    const uint32_t u = __float_as_uint(f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Clamped geometry of sequence b: first row, candidate count L (prefix), k
-// and the first output slot.
-struct SeqGeo {
-    int seq0, L, k, kout;
-};
-__device__ __forceinline__ SeqGeo seq_geo(const SelectArgs& a, int b) {
-    SeqGeo s;
-    s.seq0 = min(max(a.cu_seqlens_k[b], 0), a.total_kv);
-    const int end = min(max(a.cu_seqlens_k[b + 1], s.seq0), a.total_kv);
-    s.L = max(end - s.seq0 - a.W, 0);
-    s.L = min(s.L, a.nchunks * kSelChunk);
-    const int kend = max(a.cu_k[a.batch], 0);
-    s.kout = min(max(a.cu_k[b], 0), kend);
-    s.k = min(min(max(a.cu_k[b + 1] - s.kout, 0), s.L), kend - s.kout);
-    return s;
-}
 
 __global__ void sel_zero_kernel(uint32_t* __restrict__ p, int n) {
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
@@ -82,21 +60,19 @@ __device__ __forceinline__ int wg_exclusive_scan(int x, int* wsum, int* total) {
     return before + v - x;
 }
 
-// Ordered compaction offsets: items are ordered by (thread, e); off[e] is the
-// number of true predicates before item e.  Returns the total.
-template <int PER>
-__device__ __forceinline__ int ordered_offsets(const bool (&pred)[PER], int (&off)[PER], int* wsum) {
-    int mine = 0;
+// Sum of x over the workgroup's threads (any order: integers); all threads get it.
+__device__ __forceinline__ uint64_t wg_total(uint64_t x, uint64_t* wsum) {
+    constexpr int NW = kSelThreads / 64;
+    static_assert(kSelChunk < (1 << 16), "per-chunk counts are packed into 16 bits");
 #pragma unroll
-    for (int e = 0; e < PER; ++e) mine += pred[e] ? 1 : 0;
-    int total;
-    int base = wg_exclusive_scan(mine, wsum, &total);
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = x;
+    __syncthreads();
+    uint64_t all = 0;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-        off[e] = base;
-        base += pred[e] ? 1 : 0;
-    }
-    return total;
+    for (int i = 0; i < NW; ++i) all += wsum[i];
+    __syncthreads();
+    return all;
 }
 
 // Over NBINS LDS bins taken from the top, find the bin holding the
@@ -129,48 +105,7 @@ __device__ __forceinline__ void find_crossing(const uint32_t* bins, int need, in
 
 __global__ void __launch_bounds__(kSelThreads) sel_keys_kernel(const SelectArgs a) {
     __shared__ uint32_t h[kSelBins];
-    const int b = blockIdx.y;
-    const SeqGeo sg = seq_geo(a, b);
-    const int start = blockIdx.x * kSelChunk;
-    if (start >= sg.L) return;                         // uniform per workgroup
-    for (int i = threadIdx.x; i < kSelBins; i += kSelThreads) h[i] = 0u;
-
-    float s[kSelPer];
-    bool in[kSelPer];
-#pragma unroll
-    for (int e = 0; e < kSelPer; ++e) {
-        in[e] = start + e * kSelThreads + (int)threadIdx.x < sg.L;
-        s[e] = 0.f;
-    }
-    const float* col = a.scores + sg.seq0 + start + threadIdx.x;
-    // S = sum over KV heads 0, 1, ... in this order; eight heads' loads in flight.
-    for (int g0 = 0; g0 < a.hkv; g0 += 8) {
-        float x[8][kSelPer];
-#pragma unroll
-        for (int gi = 0; gi < 8; ++gi) {
-            const float* row = col + (size_t)(g0 + gi) * a.total_kv;
-#pragma unroll
-            for (int e = 0; e < kSelPer; ++e) x[gi][e] = (in[e] && g0 + gi < a.hkv) ? row[e * kSelThreads] : 0.f;
-        }
-#pragma unroll
-        for (int gi = 0; gi < 8; ++gi)
-#pragma unroll
-            for (int e = 0; e < kSelPer; ++e)
-                if (g0 + gi < a.hkv) s[e] += x[gi][e];
-    }
-    __syncthreads();                                   // histogram cleared
-    uint32_t* keys = a.keys + sg.seq0 + start + threadIdx.x;
-#pragma unroll
-    for (int e = 0; e < kSelPer; ++e) {
-        if (!in[e]) continue;
-        const uint32_t key = order_key(s[e]);
-        keys[e * kSelThreads] = key;
-        atomicAdd(&h[key >> (32 - kSelDigitBits)], 1u);
-    }
-    __syncthreads();
-    uint32_t* gh = a.zeroed + (size_t)b * kSelBins;
-    for (int i = threadIdx.x; i < kSelBins; i += kSelThreads)
-        if (h[i]) atomicAdd(&gh[i], h[i]);
+    sel_keys_chunk(a, blockIdx.y, blockIdx.x, h);
 }
 
 __global__ void __launch_bounds__(kSelThreads) sel_cand_kernel(const SelectArgs a) {
@@ -244,6 +179,7 @@ __global__ void __launch_bounds__(kSelThreads) sel_write_kernel(const SelectArgs
     __shared__ uint32_t gt[kSelMaxChunks];
     __shared__ uint32_t ties[kSelMaxChunks];
     __shared__ int wsum[kSelThreads / 64];
+    __shared__ uint64_t wsum64[kSelThreads / 64];
     __shared__ uint32_t cross[2];
     const int b = blockIdx.y;
     const int chunk = blockIdx.x;
@@ -277,6 +213,9 @@ __global__ void __launch_bounds__(kSelThreads) sel_write_kernel(const SelectArgs
         hk[e] = ck[min(i, sg.L - 1)];        // issued with the count's load; slots >= nc unused
         hp[e] = cp[min(i, sg.L - 1)];
     }
+    // Keys above the top digit in the chunks before this one (loaded up front).
+    int above_before = 0;
+    for (int c = tid; c < chunk; c += kSelThreads) above_before += (int)a.chunk_above[(size_t)b * a.nchunks + c];
     // Visit every candidate (key, position) once: held ones first, then the rest
     // in batches of kCandPer loads per thread.
     auto for_each_cand = [&](auto&& fn) {
@@ -333,14 +272,16 @@ __global__ void __launch_bounds__(kSelThreads) sel_write_kernel(const SelectArgs
     });
     __syncthreads();
     // Output offset of this chunk and its tie share, from the chunks before it.
-    int tl = 0, sl = 0;
+    // Both totals in one reduction: ties in the low word, keys above theta in
+    // the high word (each below 2^31).
+    uint32_t tl = 0, sl = (uint32_t)above_before;
     for (int c = tid; c < chunk; c += kSelThreads) {
-        tl += (int)ties[c];
-        sl += (int)a.chunk_above[(size_t)b * a.nchunks + c] + (int)gt[c];
+        tl += ties[c];
+        sl += gt[c];
     }
-    int ties_before, sel_before;
-    wg_exclusive_scan(tl, wsum, &ties_before);
-    wg_exclusive_scan(sl, wsum, &sel_before);
+    const uint64_t both = wg_total(((uint64_t)sl << 32) | tl, wsum64);
+    const int ties_before = (int)(uint32_t)both;
+    const int sel_before = (int)(both >> 32);
     const int off0 = sel_before + min(ties_before, take);
     const int tq = min(max(take - ties_before, 0), (int)ties[chunk]);
 
@@ -351,17 +292,24 @@ __global__ void __launch_bounds__(kSelThreads) sel_write_kernel(const SelectArgs
         gtp[e] = in && kk[e] > theta;
         tie[e] = in && kk[e] == theta;
     }
-    int trank[kSelPer];
-    ordered_offsets(tie, trank, wsum);
-    bool sel[kSelPer];
+    // One scan gives, for every item, the keys above theta and the ties before
+    // it (packed 16/16: a chunk holds at most kSelChunk of each).  The ties
+    // taken are the first tq in position order, so an item's output slot is
+    // (above theta before it) + min(ties before it, tq).
+    int mine = 0;
 #pragma unroll
-    for (int e = 0; e < kSelPer; ++e) sel[e] = gtp[e] || (tie[e] && trank[e] < tq);
-    int o[kSelPer];
-    ordered_offsets(sel, o, wsum);
+    for (int e = 0; e < kSelPer; ++e) mine += (gtp[e] ? 1 << 16 : 0) + (tie[e] ? 1 : 0);
+    int total;
+    int before = wg_exclusive_scan(mine, wsum, &total);
     int32_t* out = a.indices + sg.kout;
 #pragma unroll
-    for (int e = 0; e < kSelPer; ++e)
-        if (sel[e] && off0 + o[e] < sg.k) out[off0 + o[e]] = p0 + e;
+    for (int e = 0; e < kSelPer; ++e) {
+        const int gb = before >> 16, tb = before & 0xFFFF;
+        const bool sel = gtp[e] || (tie[e] && tb < tq);
+        const int slot = off0 + gb + min(tb, tq);
+        if (sel && slot >= 0 && slot < sg.k) out[slot] = p0 + e;
+        before += (gtp[e] ? 1 << 16 : 0) + (tie[e] ? 1 : 0);
+    }
 }
 
 // One thread per output slot: find the slot's sequence (binary search over
@@ -398,11 +346,17 @@ hipError_t launch_streaming_indices(int batch, int W, int sinks, const int32_t* 
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
-    const int nz = a.batch * kSelBins + a.batch;
+    const int nz = select_zeroed_words(a.batch);
     hipLaunchKernelGGL(sel_zero_kernel, dim3((nz + 1023) / 1024), dim3(256), 0, stream, a.zeroed, nz);
+    if (a.nchunks > 0)
+        hipLaunchKernelGGL(sel_keys_kernel, dim3(a.nchunks, a.batch), dim3(kSelThreads), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    return e != hipSuccess ? e : launch_select_tail(a, stream);
+}
+
+hipError_t launch_select_tail(const SelectArgs& a, hipStream_t stream) {
     if (a.nchunks > 0) {
         const dim3 grid(a.nchunks, a.batch);
-        hipLaunchKernelGGL(sel_keys_kernel, grid, dim3(kSelThreads), 0, stream, a);
         hipLaunchKernelGGL(sel_cand_kernel, grid, dim3(kSelThreads), 0, stream, a);
         hipLaunchKernelGGL(sel_write_kernel, grid, dim3(kSelThreads), 0, stream, a);
     }

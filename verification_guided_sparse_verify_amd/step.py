@@ -54,6 +54,8 @@ class LayerStep:
         ws = max(V.vegas_verify_paged_workspace_size(self.shape, gamma, self.max_seqlen, self.page_size),
                  V.vegas_select_workspace_size(batch, num_kv_heads, gamma, self.max_seqlen, self.total_kv),
                  V.vegas_sparse_decode_workspace_size(self.shape, self.max_k))
+        if self.fusable:
+            ws = max(ws, V.vegas_verify_select_workspace_size(self.shape, gamma, self.max_seqlen, self.total_kv))
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
 
     def rebind(self, inputs: dict):
@@ -70,6 +72,18 @@ class LayerStep:
             return
         V.vegas_verify_attn(self.shape, self.gamma, i["q"], i["k"], i["v"], i["cu_seqlens_k"], self.max_seqlen,
                             self.total_kv, mask, scores, self.out, self.workspace, stream)
+
+    @property
+    def fusable(self) -> bool:
+        """Verification and selection can run as one call (contiguous cache, Vegas selection)."""
+        return not self.paged and self.selection == "vegas"
+
+    def verify_select(self, stream=None):
+        """Verification with collection followed by selection, as one library call."""
+        i = self.inp
+        V.vegas_verify_select(self.shape, self.gamma, i["q"], i["k"], i["v"], i["cu_seqlens_k"], self.max_seqlen,
+                              self.total_kv, self.collect_mask, i["cu_k"], self.scores, self.indices, self.out,
+                              self.workspace, stream)
 
     def select(self, stream=None):
         i = self.inp
@@ -90,9 +104,12 @@ class LayerStep:
         V.vegas_sparse_decode_attn(self.shape, i["draft_q"][j], i["k"], i["v"], i["cu_seqlens_k"], self.total_kv,
                                    self.indices, i["cu_k"], self.max_k, self.draft_out[j], self.workspace, stream)
 
-    def run(self, stream=None):
-        self.verify(self.selection == "vegas", stream)
-        self.select(stream)
+    def run(self, stream=None, fused: bool = False):
+        if fused:
+            self.verify_select(stream)
+        else:
+            self.verify(self.selection == "vegas", stream)
+            self.select(stream)
         for j in range(self.n_drafts):
             self.draft(j, stream)
 
@@ -144,3 +161,20 @@ class LayerStep:
                         self.max_k, self.draft_out[j].data_ptr(), ws, wsb, st))
                   for j in range(self.n_drafts)]
         return verify, plain, select, drafts
+
+    def bind_fused(self, stream=None):
+        """Argument-free callable of the one-call verification + selection."""
+        if not self.fusable:
+            raise ValueError("the one-call verification + selection needs a contiguous cache and Vegas selection")
+        i = self.inp
+        args = (ctypes.byref(self.shape), self.gamma, i["q"].data_ptr(), i["k"].data_ptr(), i["v"].data_ptr(),
+                i["cu_seqlens_k"].data_ptr(), self.max_seqlen, self.total_kv, self.collect_mask,
+                i["cu_k"].data_ptr(), self.scores.data_ptr(), self.indices.data_ptr(), self.out.data_ptr(),
+                self.workspace.data_ptr(), self.workspace.numel(), V._stream(stream))
+        fn = V.lib().vegas_verify_select
+
+        def go():
+            rc = fn(*args)
+            if rc:
+                V._check(rc, "vegas_verify_select")
+        return go

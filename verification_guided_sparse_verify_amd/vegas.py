@@ -27,6 +27,7 @@ EXPORTED = (
     "vegas_abi_version", "vegas_status_string", "vegas_last_error_message",
     "vegas_verify_workspace_size", "vegas_verify_attn",
     "vegas_select_workspace_size", "vegas_select_topk",
+    "vegas_verify_select_workspace_size", "vegas_verify_select",
     "vegas_sparse_decode_workspace_size", "vegas_sparse_decode_attn",
     "vegas_verify_paged_workspace_size", "vegas_verify_attn_paged", "vegas_sparse_decode_attn_paged",
     "vegas_verify_local_workspace_size", "vegas_verify_attn_local", "vegas_streaming_indices",
@@ -74,6 +75,8 @@ def lib():
             "vegas_verify_attn": ([SP, I32, P, P, P, P, I32, I32, U32, P, P, P, SZ, P], ctypes.c_int),
             "vegas_select_workspace_size": ([I32, I32, I32, I32, I32, PSZ], ctypes.c_int),
             "vegas_select_topk": ([I32, I32, I32, P, P, I32, I32, P, P, P, SZ, P], ctypes.c_int),
+            "vegas_verify_select_workspace_size": ([SP, I32, I32, I32, PSZ], ctypes.c_int),
+            "vegas_verify_select": ([SP, I32, P, P, P, P, I32, I32, U32, P, P, P, P, P, SZ, P], ctypes.c_int),
             "vegas_sparse_decode_workspace_size": ([SP, I32, PSZ], ctypes.c_int),
             "vegas_sparse_decode_attn": ([SP, P, P, P, P, I32, P, P, I32, P, P, SZ, P], ctypes.c_int),
             "vegas_verify_paged_workspace_size": ([SP, I32, I32, I32, PSZ], ctypes.c_int),
@@ -163,6 +166,23 @@ def vegas_select_topk(batch: int, num_kv_heads: int, gamma: int, scores, cu_seql
                                    total_kv, _ptr(cu_k), _ptr(indices), _ptr(workspace), _nbytes(workspace),
                                    _stream(stream)),
            "vegas_select_topk")
+
+
+def vegas_verify_select_workspace_size(shape: AttnShape, gamma: int, max_seqlen_k: int, total_kv: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().vegas_verify_select_workspace_size(ctypes.byref(shape), gamma, max_seqlen_k, total_kv,
+                                                    ctypes.byref(n)),
+           "vegas_verify_select_workspace_size")
+    return n.value
+
+
+def vegas_verify_select(shape: AttnShape, gamma: int, q, k, v, cu_seqlens_k, max_seqlen_k: int, total_kv: int,
+                        collect_mask: int, cu_k, scores, indices, out, workspace, stream=None) -> None:
+    _check(lib().vegas_verify_select(ctypes.byref(shape), gamma, _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k),
+                                     max_seqlen_k, total_kv, collect_mask & 0xFFFFFFFF, _ptr(cu_k), _ptr(scores),
+                                     _ptr(indices), _ptr(out), _ptr(workspace), _nbytes(workspace),
+                                     _stream(stream)),
+           "vegas_verify_select")
 
 
 def vegas_sparse_decode_workspace_size(shape: AttnShape, max_idx: int) -> int:
