@@ -52,7 +52,7 @@ def algorithmic_bytes(wl):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("attn.hip", "internal.h"):
+    for f in ("attn.hip", "internal.h", "select_device.h"):
         with open(os.path.join(ROOT, "verification_guided_sparse_verify_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
