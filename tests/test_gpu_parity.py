@@ -45,6 +45,10 @@ SWEEP = [
     ("bf16", 1, 64, 8, 128, 6, [2000], Fraction(10, 100)),
     ("bf16", 4, 32, 8, 128, 4, [3000, 1, 200, 9999], Fraction(5, 100)),
     ("bf16", 2, 16, 8, 64, 3, [777, 12000], Fraction(1)),
+    # 40 and 56 query rows per KV head: the row-split verification (3 tiles padded to 4)
+    ("bf16", 2, 64, 8, 64, 4, [3000, 517], Fraction(5, 100)),
+    ("f32", 1, 64, 8, 64, 6, [900], Fraction(5, 100)),
+    ("bf16", 3, 64, 8, 128, 6, [5000, 64, 2047], Fraction(5, 100)),
 ]
 
 
@@ -211,6 +215,7 @@ MASK_CASES = [
     ("bf16", 2, 16, 8, 64, 7, [1500, 2049], 0b10110010),
     ("f32", 1, 8, 2, 64, 3, [900], "all"),
     ("bf16", 3, 8, 1, 128, 2, [130, 1, 4100], 0b010),
+    ("bf16", 1, 64, 8, 128, 6, [2500], "all"),
 ]
 
 
@@ -279,6 +284,7 @@ LOCAL_CASES = [
     ("bf16", 2, 64, 8, 64, 3, [20000, 50], 128),
     ("f32", 2, 8, 2, 64, 2, [300, 77], 64),
     ("bf16", 1, 32, 8, 128, 5, [700], 5000),
+    ("bf16", 2, 64, 8, 128, 6, [3000, 40], 256),
 ]
 
 

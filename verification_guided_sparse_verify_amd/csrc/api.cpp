@@ -53,6 +53,7 @@ AttnPlan plan_attn(bool bf16, int batch, int hkv, int M, int head_dim, int max_n
                    int page_size = 0) {
     AttnPlan p;
     p.mb = (M + 15) / 16;
+    if (!gather && p.mb == 3) p.mb = 4;   // verification runs 3-4 row tiles as two halves of 2
     const int unit = vegas::kAttnWaves * vegas::kAttnBlock;
     const int64_t n = max_n > 0 ? max_n : 1;
     // Both caps are multiples of `unit`.  Verification uses the same plan with

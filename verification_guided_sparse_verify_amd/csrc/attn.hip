@@ -217,24 +217,30 @@ __device__ __forceinline__ uint64_t row_offset(const SplitCtx& c, int p) {
 // lanes reading one chunk column of 16 rows hit distinct banks); V chunks are
 // XORed with the row's 4-row group (so the transposed reads, four lane groups
 // on rows 4 apart, hit distinct banks).
-template <class GEO, bool GATHER>
+// PART selects the tiles this wave copies: 3 both, 1 the K tile, 2 the V tile
+// (a row-split workgroup's two waves of a position group share the copies).
+template <class GEO, bool GATHER, int PART = 3>
 __device__ __forceinline__ void issue_block(const SplitCtx& c, int p0, int lane, unsigned char* stage) {
     // All row offsets first (in gather mode, LDS reads of the index list that
     // then complete together), then the copies back to back.
     uint64_t off[GEO::TLD];
 #pragma unroll
     for (int i = 0; i < GEO::TLD; ++i) off[i] = row_offset<GATHER>(c, p0 + i * GEO::RPI + lane / GEO::CPR);
+    if constexpr ((PART & 1) != 0) {
 #pragma unroll
-    for (int i = 0; i < GEO::TLD; ++i) {
-        const int row = i * GEO::RPI + lane / GEO::CPR;
-        const int cc = (lane % GEO::CPR) ^ (row & GEO::KSWZ);
-        copy16_to_lds(c.kbase + off[i] + cc * 16, stage + i * 1024);
+        for (int i = 0; i < GEO::TLD; ++i) {
+            const int row = i * GEO::RPI + lane / GEO::CPR;
+            const int cc = (lane % GEO::CPR) ^ (row & GEO::KSWZ);
+            copy16_to_lds(c.kbase + off[i] + cc * 16, stage + i * 1024);
+        }
     }
+    if constexpr ((PART & 2) != 0) {
 #pragma unroll
-    for (int i = 0; i < GEO::TLD; ++i) {
-        const int row = i * GEO::RPI + lane / GEO::CPR;
-        const int cc = (lane % GEO::CPR) ^ (GEO::SWZU * ((row >> 2) & 3));
-        copy16_to_lds(c.vbase + off[i] + cc * 16, stage + GEO::TILE + i * 1024);
+        for (int i = 0; i < GEO::TLD; ++i) {
+            const int row = i * GEO::RPI + lane / GEO::CPR;
+            const int cc = (lane % GEO::CPR) ^ (GEO::SWZU * ((row >> 2) & 3));
+            copy16_to_lds(c.vbase + off[i] + cc * 16, stage + GEO::TILE + i * 1024);
+        }
     }
 }
 
@@ -283,7 +289,8 @@ __device__ __forceinline__ void seq_plan(const AttnArgs& a, int len, float inv_t
     ns = min((len + chunk - 1) / chunk, a.nsplit);
 }
 
-// Sum of x over the workgroup (all threads get it).  red: kAttnWaves ints of LDS.
+// Sum of x over the NT threads of the workgroup (all get it).  red: NT/64 ints of LDS.
+template <int NT>
 __device__ __forceinline__ int wg_sum(int x, int* red) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
@@ -292,7 +299,7 @@ __device__ __forceinline__ int wg_sum(int x, int* red) {
     __syncthreads();
     int t = 0;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) t += red[w];
+    for (int w = 0; w < NT / 64; ++w) t += red[w];
     return t;
 }
 
@@ -301,20 +308,22 @@ __device__ __forceinline__ int wg_sum(int x, int* red) {
 // target is the largest one <= a.target whose units (rounded up per sequence)
 // fit in a.target, i.e. one round of workgroups when the LDS cap allows it;
 // ns/chunk receive this thread's sequences' plans.
-constexpr int kPlanPerThread = kMaxBatch / (kAttnWaves * 64);
+template <int NT>
+constexpr int plan_per_thread() { return kMaxBatch / NT; }
 
-template <bool GATHER>
-__device__ __forceinline__ void batch_plan(const AttnArgs& a, int* red, int (&ns)[kPlanPerThread],
-                                           int (&chunk)[kPlanPerThread]) {
+template <bool GATHER, int NT>
+__device__ __forceinline__ void batch_plan(const AttnArgs& a, int* red, int (&ns)[plan_per_thread<NT>()],
+                                           int (&chunk)[plan_per_thread<NT>()]) {
+    constexpr int kPlanPerThread = plan_per_thread<NT>();
     int len[kPlanPerThread];
     int mine = 0;
 #pragma unroll
     for (int k = 0; k < kPlanPerThread; ++k) {
-        const int b = k * kAttnWaves * 64 + threadIdx.x;
+        const int b = k * NT + threadIdx.x;
         len[k] = b < a.batch ? seq_span<GATHER>(a, b).len : 0;
         mine += len[k];
     }
-    const int total = wg_sum(mine, red);
+    const int total = wg_sum<NT>(mine, red);
     const float inv_total = total > 0 ? 1.f / (float)total : 0.f;
     auto plan = [&](int t) {
         int u = 0;
@@ -323,7 +332,7 @@ __device__ __forceinline__ void batch_plan(const AttnArgs& a, int* red, int (&ns
             seq_plan(a, len[k], inv_total, t, ns[k], chunk[k]);
             u += ns[k];
         }
-        return wg_sum(u, red);
+        return wg_sum<NT>(u, red);
     };
     if (total <= 0 || plan(a.target) <= a.target) return;
     int lo = 1, hi = a.target - 1, best = 1;   // the unit count does not decrease with t
@@ -348,6 +357,10 @@ struct WaveState {
     int rrow[MB];
     float m_run[MB], l_run[MB];
     f32x4_t o[D / 16][MB];
+    // Row split: this wave's partial collected score of its last block, added
+    // to the LDS buffer after the next workgroup barrier (idx -1: none).
+    float pend_val;
+    int pend_idx;
 };
 
 // PV step: acc += V^T(16 d x 16 pos) . P^T(16 pos x 16 rows).  Lane (lr, lg)
@@ -373,7 +386,7 @@ __device__ __forceinline__ f32x4_t mfma_pv(const uint32_t (&vt)[4], const float 
 }
 
 // One 16-position block: S^T, collection, mask, online softmax, O^T += V^T P^T.
-template <class GEO, bool BF16, int D, int MB, bool GATHER, bool COLLECT>
+template <class GEO, bool BF16, int D, int MB, bool GATHER, bool COLLECT, bool HOLD = false>
 __device__ __forceinline__ void compute_block(const AttnArgs& a, WaveState<BF16, D, MB>& ws, int p0, int L,
                                               int end, int start, int lane, const unsigned char* stage,
                                               float* score_s) {
@@ -419,7 +432,12 @@ __device__ __forceinline__ void compute_block(const AttnArgs& a, WaveState<BF16,
                 val = (lr == 1) ? red[1] : val;
                 val = (lr == 2) ? red[2] : val;
                 val = (lr == 3) ? red[3] : val;
-                score_s[p0 - start + 4 * lg + lr] = a.scale * val;
+                if constexpr (HOLD) {
+                    ws.pend_val = a.scale * val;
+                    ws.pend_idx = p0 - start + 4 * lg + lr;
+                } else {
+                    score_s[p0 - start + 4 * lg + lr] = a.scale * val;
+                }
             }
         }
     }
@@ -489,14 +507,27 @@ __device__ __forceinline__ void compute_block(const AttnArgs& a, WaveState<BF16,
     lds_fence();   // this stage's reads are done before it is refilled
 }
 
-template <bool BF16, int D, int MB, bool GATHER, bool COLLECT>
-__global__ void __launch_bounds__(kAttnWaves * 64)
+// RS = 2 (row split, verification with 3-4 row tiles): eight waves, two per
+// position group; wave (pw, rh) takes blocks pw, pw + kAttnWaves, ... and the
+// row tiles rh*MBW .. rh*MBW + MBW - 1.  The two waves of a position group
+// share one ring (one copies the K tile, the other the V tile) and every
+// block iteration ends its waits with a workgroup barrier.  Two waves per SIMD
+// then overlap one wave's MFMA with the other's softmax arithmetic.
+template <bool BF16, int D, int MB, bool GATHER, bool COLLECT, int RS>
+__global__ void __launch_bounds__(kAttnWaves * RS * 64)
 attn_split_kernel(const AttnArgs a) {
-    using GEO = Geo<BF16, D, MB>;
+    static_assert(MB % RS == 0 && (RS == 1 || (RS == 2 && !GATHER)), "row split: verification, even tile count");
+    constexpr int MBW = MB / RS;                  // row tiles per wave
+    constexpr int NT = kAttnWaves * RS * 64;      // threads
+    constexpr int NWV = NT / 64;                  // waves
+    using GEO = Geo<BF16, D, MBW>;
     using T = typename std::conditional<BF16, uint16_t, float>::type;
     constexpr int DC = GEO::DC, DB = GEO::DB, NREG = GEO::NREG, NST = GEO::NST;
+    constexpr int OPS = GEO::BLOCK_OPS / RS;      // copies one wave issues per block
+    constexpr int MERGE = RS * (kAttnWaves / 2) * GEO::MSLOT;
+    constexpr int MAIN = GEO::RING > MERGE ? GEO::RING : MERGE;
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[GEO::MAIN];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[MAIN];
     __shared__ int idx_s[GATHER ? kMaxGatherChunk : 1];
     __shared__ int page_s[GATHER ? 1 : kMaxPagesPerSplit];
     // Collected scores of this split, written to HBM once the split is done.
@@ -505,6 +536,8 @@ attn_split_kernel(const AttnArgs a) {
     const int lane = threadIdx.x & 63;
     // wave index as a scalar: every branch on it is uniform
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pw = wave % kAttnWaves;             // position group
+    const int rh = wave / kAttnWaves;             // row half (0 unless RS = 2)
     const int lr = lane & 15;
     const int lg = lane >> 4;
 
@@ -516,18 +549,19 @@ attn_split_kernel(const AttnArgs a) {
     // Workgroup -> (KV head g, sequence b, split): the units of all sequences'
     // split plans, in order; workgroups past the last unit have no work.
     // Workgroup 0 publishes every sequence's split count for the combine.
-    __shared__ int plan_red[kAttnWaves];
+    __shared__ int plan_red[NWV];
     __shared__ int plan_s[3];
     const int g = blockIdx.x % a.hkv;
     const int unit_id = blockIdx.x / a.hkv;
+    constexpr int kPlanPerThread = plan_per_thread<NT>();
     int pns[kPlanPerThread], pch[kPlanPerThread];
-    batch_plan<GATHER>(a, plan_red, pns, pch);
+    batch_plan<GATHER, NT>(a, plan_red, pns, pch);
     if (threadIdx.x == 0) plan_s[0] = -1;
     int before = 0;                                  // units of the sequences of earlier passes
 #pragma unroll
     for (int k = 0; k < kPlanPerThread; ++k) {
-        if (k * kAttnWaves * 64 >= a.batch) break;   // uniform
-        const int bb = k * kAttnWaves * 64 + threadIdx.x;
+        if (k * NT >= a.batch) break;                // uniform
+        const int bb = k * NT + threadIdx.x;
         const int ns = pns[k];
         if (blockIdx.x == 0 && bb < a.batch) a.seq_splits[bb] = ns;
         int v = ns;                                  // inclusive scan of ns over the threads
@@ -542,7 +576,7 @@ attn_split_kernel(const AttnArgs a) {
         __syncthreads();
         int wbefore = 0, all = 0;
 #pragma unroll
-        for (int w = 0; w < kAttnWaves; ++w) {
+        for (int w = 0; w < NWV; ++w) {
             wbefore += (w < (int)(threadIdx.x >> 6)) ? plan_red[w] : 0;
             all += plan_red[w];
         }
@@ -566,11 +600,13 @@ attn_split_kernel(const AttnArgs a) {
     if (n_b <= 0 || start >= count) return;                       // uniform per workgroup
     const int end = min(start + chunk, count);
 
-    WaveState<BF16, D, MB> ws;
+    WaveState<BF16, D, MBW> ws;
+    ws.pend_idx = -1;
+    ws.pend_val = 0.f;
 #pragma unroll
-    for (int qb = 0; qb < MB; ++qb) {
-        // B operand of S^T: query row 16*qb + lane%16, elements 32*ch + 8*(lane/16) .. +7
-        const int j = 16 * qb + lr;
+    for (int qb = 0; qb < MBW; ++qb) {
+        // B operand of S^T: query row 16*(rh*MBW + qb) + lane%16, elements 32*ch + 8*(lane/16) .. +7
+        const int j = 16 * (rh * MBW + qb) + lr;
         const bool valid = j < a.M;
         const int r = valid ? j / a.G : a.W - 1;
         const int hl = valid ? j % a.G : 0;
@@ -594,11 +630,11 @@ attn_split_kernel(const AttnArgs a) {
     const int pmask = paged ? (1 << a.page_shift) - 1 : 0;
     int page0 = 0;
     if constexpr (GATHER) {
-        constexpr int IPT = kMaxGatherChunk / (kAttnWaves * 64);   // indices per thread
+        constexpr int IPT = kMaxGatherChunk / NT;   // indices per thread
         int t[IPT];
 #pragma unroll
         for (int e = 0; e < IPT; ++e) {   // clamped, branch-free: all loads in flight together
-            const int i = min(e * kAttnWaves * 64 + (int)threadIdx.x, end - start - 1);
+            const int i = min(e * NT + (int)threadIdx.x, end - start - 1);
             t[e] = min(max(a.indices[ib0 + start + i], 0), n_b - 1);
         }
         if (paged) {                      // position -> row of the page pool
@@ -612,7 +648,7 @@ attn_split_kernel(const AttnArgs a) {
         }
 #pragma unroll
         for (int e = 0; e < IPT; ++e) {
-            const int i = e * kAttnWaves * 64 + threadIdx.x;
+            const int i = e * NT + threadIdx.x;
             if (i < end - start) idx_s[i] = t[e];
         }
         __syncthreads();
@@ -641,71 +677,97 @@ attn_split_kernel(const AttnArgs a) {
     c.start = start;
     c.end = end;
 
-    // This wave's blocks are wave, wave+NW, ...; a ring of NST stages keeps
-    // NST-1 of them in flight.  A block past the last one is replaced by the
-    // last one (re-fetched, served by the caches) so that every iteration
-    // issues the same number of copies and the wait count stays exact.
+    // This position group's blocks are pw, pw+kAttnWaves, ...; a ring of NST
+    // stages keeps NST-1 of them in flight.  A block past the last one is
+    // replaced by the last one (re-fetched, served by the caches) so that every
+    // iteration issues the same number of copies and the wait count stays exact.
+    // With the row split every wave runs the same number of iterations (its
+    // barriers must match); the extra ones compute nothing.
     const int nblk = (end - start + kAttnBlock - 1) / kAttnBlock;
-    const int nmine = wave < nblk ? (nblk - wave + kAttnWaves - 1) / kAttnWaves : 0;
-    unsigned char* ring = smem + wave * (NST * GEO::STAGE);
-    auto block_pos = [&](int jj) { return start + (wave + kAttnWaves * min(jj, nmine - 1)) * kAttnBlock; };
+    const int nmine = pw < nblk ? (nblk - pw + kAttnWaves - 1) / kAttnWaves : 0;
+    const int nloop = RS == 1 ? nmine : (nblk + kAttnWaves - 1) / kAttnWaves;
+    unsigned char* ring = smem + pw * (NST * GEO::STAGE);
+    auto block_pos = [&](int jj) { return start + (pw + kAttnWaves * min(jj, nmine - 1)) * kAttnBlock; };
+    auto issue = [&](int jj, unsigned char* stage) {
+        if constexpr (RS == 1) {
+            issue_block<GEO, GATHER, 3>(c, block_pos(jj), lane, stage);
+        } else {
+            if (rh == 0) issue_block<GEO, GATHER, 1>(c, block_pos(jj), lane, stage);
+            else issue_block<GEO, GATHER, 2>(c, block_pos(jj), lane, stage);
+        }
+    };
     if (nmine > 0) {
 #pragma unroll
-        for (int st = 0; st < NST - 1; ++st) issue_block<GEO, GATHER>(c, block_pos(st), lane, ring + st * GEO::STAGE);
+        for (int st = 0; st < NST - 1; ++st) issue(st, ring + st * GEO::STAGE);
     }
     // Retire the Q loads here, where the compiler can see it (its wait also
     // covers the first blocks' copies, issued after them), so that its own
     // wait for them is not placed inside the block loop.
 #pragma unroll
-    for (int qb = 0; qb < MB; ++qb)
+    for (int qb = 0; qb < MBW; ++qb)
 #pragma unroll
         for (int ch = 0; ch < DC; ++ch) {
             keep_live(ws.qf[qb][ch]);
             if (!ws.qvalid[qb]) ws.qf[qb][ch] = zero_frag<BF16>();
         }
-    if (nmine > 0) {
-        for (int jj = 0; jj < nmine; ++jj) {
-            wait_vmem<(NST - 2) * GEO::BLOCK_OPS>();      // block jj has landed
-            issue_block<GEO, GATHER>(c, block_pos(jj + NST - 1), lane, ring + ((jj + NST - 1) % NST) * GEO::STAGE);
-            compute_block<GEO, BF16, D, MB, GATHER, COLLECT>(a, ws, block_pos(jj), L, end, start, lane,
-                                                              ring + (jj % NST) * GEO::STAGE, score_s);
+    for (int jj = 0; jj < nloop; ++jj) {
+        wait_vmem<(NST - 2) * OPS>();                     // this wave's copies of block jj have landed
+        if constexpr (RS > 1) {
+            __syncthreads();                              // ... and its partner's; stage jj-1 is free
+            if constexpr (COLLECT) {                      // the second half's part of block jj-1
+                if (rh == 1 && ws.pend_idx >= 0) score_s[ws.pend_idx] += ws.pend_val;
+                ws.pend_idx = -1;
+            }
         }
-        wait_vmem<0>();
+        if (nmine > 0) issue(jj + NST - 1, ring + ((jj + NST - 1) % NST) * GEO::STAGE);
+        if (jj < nmine) {
+            if (RS > 1 && rh == 1)
+                compute_block<GEO, BF16, D, MBW, GATHER, COLLECT, true>(a, ws, block_pos(jj), L, end, start, lane,
+                                                                        ring + (jj % NST) * GEO::STAGE, score_s);
+            else
+                compute_block<GEO, BF16, D, MBW, GATHER, COLLECT, false>(a, ws, block_pos(jj), L, end, start, lane,
+                                                                         ring + (jj % NST) * GEO::STAGE, score_s);
+        }
     }
+    wait_vmem<0>();
 
     // Row sums: each lane summed its own positions.
 #pragma unroll
-    for (int qb = 0; qb < MB; ++qb) {
+    for (int qb = 0; qb < MBW; ++qb) {
         ws.l_run[qb] += __shfl_xor(ws.l_run[qb], 16);
         ws.l_run[qb] += __shfl_xor(ws.l_run[qb], 32);
     }
 
-    // Tree merge of the waves' (m, l, O) through LDS, in fragment order.
+    // Tree merge of the position groups' (m, l, O) through LDS, in fragment
+    // order, one tree per row half.
     __syncthreads();
-    float* fs = reinterpret_cast<float*>(smem);
+    if constexpr (RS > 1 && COLLECT) {                    // the second half's part of its last block
+        if (rh == 1 && ws.pend_idx >= 0) score_s[ws.pend_idx] += ws.pend_val;
+    }
+    float* fs = reinterpret_cast<float*>(smem) + rh * (kAttnWaves / 2) * (GEO::MSLOT / 4);
     constexpr int SLOTF = GEO::MSLOT / 4;
 #pragma unroll
     for (int half = kAttnWaves / 2; half >= 1; half >>= 1) {
-        if (wave >= half && wave < 2 * half) {
-            float* slot = fs + (wave - half) * SLOTF;
+        if (pw >= half && pw < 2 * half) {
+            float* slot = fs + (pw - half) * SLOTF;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int qb = 0; qb < MB; ++qb)
-                    *reinterpret_cast<f32x4_t*>(slot + ((db * MB + qb) * 64 + lane) * 4) = ws.o[db][qb];
+                for (int qb = 0; qb < MBW; ++qb)
+                    *reinterpret_cast<f32x4_t*>(slot + ((db * MBW + qb) * 64 + lane) * 4) = ws.o[db][qb];
 #pragma unroll
-            for (int qb = 0; qb < MB; ++qb) {
+            for (int qb = 0; qb < MBW; ++qb) {
                 slot[NREG * 256 + qb * 64 + lane] = ws.m_run[qb];
-                slot[NREG * 256 + (MB + qb) * 64 + lane] = ws.l_run[qb];
+                slot[NREG * 256 + (MBW + qb) * 64 + lane] = ws.l_run[qb];
             }
         }
         __syncthreads();
-        if (wave < half) {
-            const float* slot = fs + wave * SLOTF;
+        if (pw < half) {
+            const float* slot = fs + pw * SLOTF;
 #pragma unroll
-            for (int qb = 0; qb < MB; ++qb) {
+            for (int qb = 0; qb < MBW; ++qb) {
                 const float mb = slot[NREG * 256 + qb * 64 + lane];
-                const float lb = slot[NREG * 256 + (MB + qb) * 64 + lane];
+                const float lb = slot[NREG * 256 + (MBW + qb) * 64 + lane];
                 const float mm = fmaxf(ws.m_run[qb], mb);
                 if (mm != kNegInf) {
                     const float ca = fast_exp2(ws.m_run[qb] - mm);
@@ -715,7 +777,7 @@ attn_split_kernel(const AttnArgs a) {
 #pragma unroll
                     for (int db = 0; db < DB; ++db) {
                         const f32x4_t ob =
-                            *reinterpret_cast<const f32x4_t*>(slot + ((db * MB + qb) * 64 + lane) * 4);
+                            *reinterpret_cast<const f32x4_t*>(slot + ((db * MBW + qb) * 64 + lane) * 4);
                         ws.o[db][qb] = ca * ws.o[db][qb] + cb * ob;
                     }
                 }
@@ -724,17 +786,17 @@ attn_split_kernel(const AttnArgs a) {
         __syncthreads();
     }
 
-    if (wave == 0) {
+    if (pw == 0) {       // partials in the combine's layout: all MB row tiles of the workgroup
         const size_t slot = ((size_t)b * a.hkv + g) * a.nsplit + split;
-        f32x4_t* po = reinterpret_cast<f32x4_t*>(a.part_o) + slot * (NREG * 64);
+        f32x4_t* po = reinterpret_cast<f32x4_t*>(a.part_o) + slot * (DB * MB * 64);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int qb = 0; qb < MB; ++qb) po[(db * MB + qb) * 64 + lane] = ws.o[db][qb];
+            for (int qb = 0; qb < MBW; ++qb) po[(db * MB + rh * MBW + qb) * 64 + lane] = ws.o[db][qb];
         if (lg == 0) {
 #pragma unroll
-            for (int qb = 0; qb < MB; ++qb) {
-                float2* pml = reinterpret_cast<float2*>(a.part_ml) + slot * (MB * 16) + qb * 16 + lr;
+            for (int qb = 0; qb < MBW; ++qb) {
+                float2* pml = reinterpret_cast<float2*>(a.part_ml) + slot * (MB * 16) + (rh * MBW + qb) * 16 + lr;
                 *pml = make_float2(ws.m_run[qb], ws.l_run[qb]);
             }
         }
@@ -743,7 +805,7 @@ attn_split_kernel(const AttnArgs a) {
         // The split's collected scores (prefix positions only), written last:
         // a workgroup barrier waits for the workgroup's outstanding stores, and
         // none follows here.  16-byte stores from the first 16-byte boundary of
-        // the destination on; score_s was complete at the merge's first barrier.
+        // the destination on; score_s was complete at the merge's second barrier.
         float* dst = a.scores + (size_t)g * a.total_kv + seq0 + start;
         const int nsc = min(end, L) - start;
         const int peel = min((int)((4u - (uint32_t)(((uintptr_t)dst >> 2) & 3u)) & 3u), max(nsc, 0));
@@ -864,13 +926,13 @@ __global__ void __launch_bounds__(kCombineWaves * 64) attn_combine_kernel(const 
     }
 }
 
-template <bool BF16, int D, int MB, bool GATHER, bool COLLECT>
+template <bool BF16, int D, int MB, bool GATHER, bool COLLECT, int RS = 1>
 hipError_t launch_t(const AttnArgs& a, hipStream_t stream, const SelectArgs* sel) {
     const unsigned split_grid = (unsigned)(a.hkv * a.max_units);
     const unsigned comb_grid = (unsigned)(a.batch * a.hkv * MB * (D / 16));
     if (split_grid > 0)
-        hipLaunchKernelGGL((attn_split_kernel<BF16, D, MB, GATHER, COLLECT>), dim3(split_grid),
-                           dim3(kAttnWaves * 64), 0, stream, a);
+        hipLaunchKernelGGL((attn_split_kernel<BF16, D, MB, GATHER, COLLECT, RS>), dim3(split_grid),
+                           dim3(kAttnWaves * RS * 64), 0, stream, a);
     if (comb_grid > 0) {
         if constexpr (COLLECT && !GATHER) {
             if (sel) {
@@ -889,10 +951,17 @@ template <bool BF16, int D, bool GATHER, bool COLLECT>
 hipError_t launch_mb(const AttnArgs& a, int mb, hipStream_t s, const SelectArgs* sel) {
     if (mb == 1) return launch_t<BF16, D, 1, GATHER, COLLECT>(a, s, sel);
     if (mb == 2) return launch_t<BF16, D, 2, GATHER, COLLECT>(a, s, sel);
-    // fp32 at D = 128 stops at 32 rows per KV head (LDS budget)
+    // fp32 at D = 128 stops at 32 rows per KV head (LDS budget).  Verification
+    // with more than 32 rows runs 4 row tiles as two halves of 2 (the host
+    // rounds 3 tiles up to 4); gathering has one query row per head and keeps
+    // one wave per position group.
     if constexpr (BF16 || D == 64) {
-        if (mb == 3) return launch_t<BF16, D, 3, GATHER, COLLECT>(a, s, sel);
-        if (mb == 4) return launch_t<BF16, D, 4, GATHER, COLLECT>(a, s, sel);
+        if constexpr (GATHER) {
+            if (mb == 3) return launch_t<BF16, D, 3, GATHER, COLLECT>(a, s, sel);
+            if (mb == 4) return launch_t<BF16, D, 4, GATHER, COLLECT>(a, s, sel);
+        } else {
+            if (mb == 4) return launch_t<BF16, D, 4, GATHER, COLLECT, 2>(a, s, sel);
+        }
     }
     return hipErrorInvalidValue;
 }
