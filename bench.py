@@ -340,9 +340,9 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    # Per-call breakdown, outside the timed region: two more steps with events around every call.
+    # Per-call breakdown, outside the timed region: more steps with events around every call.
     call_pairs = {"verify": [], "select": [], "draft": []}
-    for _ in range(2):
+    for _ in range(max(2, 12 // layers)):          # at least a dozen calls of each kind
         one_step(call_events=call_pairs)
     torch.cuda.synchronize()
     per = {k: [a.elapsed_time(b) * 1e3 for a, b in v] for k, v in call_pairs.items()}   # microseconds
@@ -416,7 +416,7 @@ def main():
 
     # Plain verification (collection off) on the same layers, for the collection + select overhead.
     plain = []
-    for _ in range(3):
+    for _ in range(max(3, 12 // layers)):
         for _, verify_plain, _, _ in bound:
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)

@@ -154,6 +154,26 @@ def test_gpt_oss_ragged_sampled():
     log(f"  sequences {seqs} worst {worst}")
 
 
+def test_largest_batch_and_row_count():
+    """The largest batch the attention passes plan (1024 sequences, ragged, some empty) with the
+    largest query-row count per KV head (gamma 31 at GQA group 2: 64 rows, the row-split path)."""
+    rng = np.random.default_rng(11)
+    prefixes = [int(x) for x in rng.integers(0, 300, size=1024)]
+    prefixes[0], prefixes[1], prefixes[-1] = 0, 1, 299
+    wl = W.custom_workload("bf16", 1024, 16, 8, 64, 31, prefixes, draft_steps=2)
+    log(f"case: {wl.name} (1024 ragged sequences, 64 rows per KV head)")
+    inp, st = run_layer(wl, seed=4)
+    seqs = sorted({0, 1, 2, 511, 1022, 1023} | {int(x) for x in rng.integers(0, 1024, size=10)})
+    worst = check_layer(wl, inp, st, seqs=seqs)
+    log(f"  sequences {seqs} worst {worst}")
+    # every list is valid: k_b distinct ascending prefix positions
+    idx, cuk = st.indices.cpu().numpy(), wl.cu_k()
+    for b in range(1024):
+        t = idx[cuk[b]:cuk[b + 1]]
+        assert len(t) == wl.k_per_seq[b]
+        assert np.all(np.diff(t) > 0) and (len(t) == 0 or (t[0] >= 0 and t[-1] < prefixes[b])), b
+
+
 def test_qwen3_32b_clustered_sampled():
     wl = W.named_workload(3)
     log(f"case: {wl.name}")
