@@ -15,8 +15,9 @@
 // processed together, so every K/V byte is read from HBM exactly once for all
 // rows.  The four waves take 16-position blocks in turn; each wave streams its
 // blocks through a private two-stage LDS ring filled by the load-to-LDS path
-// (no VGPR round trip), computing one block while the next is in flight.  Per
-// block and wave:
+// (no VGPR round trip), computing one block while the next is in flight.
+// (With 3-4 row tiles, eight waves split the rows in two halves per position
+// group: see attn_split_kernel.)  Per block and wave:
 //   S^T[pos, row] = K[pos, :] . Q[row, :]          16x16x32 bf16 MFMA; K from
 //                                                   the ring, Q in registers
 //   collection (verification only)                 collected rows summed over
@@ -32,7 +33,8 @@
 // slots, and V^T is read in that order.  Partials (m, l, O) of the four waves
 // are merged in LDS and one partial per workgroup goes to the workspace; the
 // collected scores of the split are written with coalesced stores;
-// attn_combine merges the splits.
+// attn_combine merges the splits (and, in the one-call verification +
+// selection, also runs the selection's first step).
 #include "internal.h"
 #include "select_device.h"
 

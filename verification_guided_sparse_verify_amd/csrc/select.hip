@@ -24,6 +24,9 @@
 //             keys equal to theta are taken (lowest positions first), and
 //             the output offset and tie share of each chunk before it; then
 //             writes its selected positions in ascending order at its offset.
+// In the one-call verification + selection the verification kernels do zero
+// (split kernel) and keys (combine kernel), and only cand and write launch
+// here (launch_select_tail).
 #include "internal.h"
 #include "select_device.h"
 
