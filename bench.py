@@ -20,6 +20,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import statistics
@@ -51,10 +52,16 @@ def algorithmic_bytes(wl):
 
 
 def kernel_source_hash():
+    """Hash of the attention kernels' source with comments and blank lines removed (a change
+    of comments alone leaves the kernels, and so the counters, as they were)."""
     h = hashlib.sha256()
     for f in ("attn.hip", "internal.h", "select_device.h"):
-        with open(os.path.join(ROOT, "verification_guided_sparse_verify_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "verification_guided_sparse_verify_amd", "csrc", f)) as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        for ln in text.splitlines():
+            code = re.sub(r"//.*", "", ln).strip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
