@@ -118,11 +118,59 @@ def cpu_baseline(wl, layer_inputs, min_seconds=10.0):
         "value": round(spent * 1e6 / done, 1),
         "unit": "us/layer-step",
         "cores": min(threads, tasks),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"layers 0..{done - 1} of {len(layer_inputs)}, all {wl.batch} sequences "
                    f"(verify + select + {wl.n_drafts} drafts each), {spent:.2f} s in total, "
                    f"divided by {done} layer-steps"),
     }
+
+
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def stream_read_ceiling(nbytes: int = 4 << 30, reps: int = 5):
+    """Best HBM streaming-read rate of a plain read kernel (libvegas_probe.so) over a few
+    workgroup counts: a measured practical peak next to the published one."""
+    import ctypes
+    import torch
+    from verification_guided_sparse_verify_amd import build as B
+    if not os.path.exists(B.PROBE_LIB):
+        return None
+    probe = ctypes.CDLL(B.PROBE_LIB)
+    fn = probe.vegas_probe_stream_read
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(8192, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    best = (0.0, 0)
+    for wgs in (256, 512, 1024, 2048, 4096):
+        times = []
+        for r in range(reps + 1):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            rc = fn(buf.data_ptr(), nbytes, wgs, sink.data_ptr(), stream.cuda_stream)
+            b.record(stream)
+            if rc != 0:
+                raise RuntimeError(f"vegas_probe_stream_read returned {rc}")
+            times.append((a, b))
+        torch.cuda.synchronize()
+        us = min(x.elapsed_time(y) for x, y in times[1:]) * 1e3
+        gbps = nbytes / (us * 1e-6) / 1e9
+        if gbps > best[0]:
+            best = (gbps, wgs)
+    del buf, sink
+    return {"gbps": round(best[0], 1), "workgroups": best[1], "bytes": nbytes,
+            "kernel": "vegas_probe_stream_read (16-byte loads, 4 in flight per thread)"}
 
 
 def collect_sweep(base, gammas=(1, 3, 5, 7, 11, 15), reps=8):
@@ -229,6 +277,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2, help="0-based workload index (default: 128K Qwen3-8B step)")
     ap.add_argument("--layers", type=int, default=None, help="override the layer count (profiling runs only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stream-ceiling", action="store_true",
+                    help="skip the measured streaming-read ceiling (4 GiB read by a plain kernel)")
     ap.add_argument("--separate-calls", action="store_true",
                     help="time verification and selection as two library calls instead of one")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -355,6 +405,11 @@ def main():
     per = {k: [a.elapsed_time(b) * 1e3 for a, b in v] for k, v in call_pairs.items()}   # microseconds
     mean = {k: statistics.fmean(v) for k, v in per.items()}
     med = {k: statistics.median(v) for k, v in per.items()}
+
+    def p10_p90(xs):
+        q = statistics.quantiles(xs, n=10, method="inclusive") if len(xs) > 1 else [xs[0]] * 9
+        return q[0], q[-1]
+    pct = {k: p10_p90(v) for k, v in per.items()}
     head_us = [a.elapsed_time(b) * 1e3 for a, b in head_pairs]
     if fused:
         # The timed region runs verification + selection as one call; the verification
@@ -362,6 +417,7 @@ def main():
         verify_us = per["verify"]
         mean["verify_select"] = statistics.fmean(head_us)
         med["verify_select"] = statistics.median(head_us)
+        pct["verify_select"] = p10_p90(head_us)
     else:
         verify_us = head_us
     verify_mean = statistics.fmean(verify_us)
@@ -401,7 +457,8 @@ def main():
         },
         "layer_step_gbps": round(step_gbps, 1),
         "layer_step_frac_of_peak": round(step_gbps / PEAK_HBM_GBPS, 4),
-        "per_call_us": {k: {"mean": round(mean[k], 2), "median": round(med[k], 2)} for k in mean},
+        "per_call_us": {k: {"mean": round(mean[k], 2), "median": round(med[k], 2),
+                            "p10": round(pct[k][0], 2), "p90": round(pct[k][1], 2)} for k in mean},
         "collect_select_overhead_vs_plain_verify": None,
         "roofline": {
             "kernel": "verify: attn_split_kernel (+ attn_combine) per layer",
@@ -438,6 +495,13 @@ def main():
     result["collect_select_overhead_vs_plain_verify"] = round(
         (mean["verify_select"] if fused else verify_mean + mean["select"]) / plain_us - 1, 4)
     result["collect_select_overhead_separate_calls"] = round(separate, 4)
+
+    if not args.no_stream_ceiling:
+        ceiling = stream_read_ceiling()
+        result["stream_read_ceiling"] = ceiling
+        if ceiling:
+            result["roofline"]["frac_of_stream_ceiling"] = round(verify_gbps / ceiling["gbps"], 4)
+            result["layer_step_frac_of_stream_ceiling"] = round(step_gbps / ceiling["gbps"], 4)
 
     if cpu_leg:
         result["cpu_baseline"] = cpu_baseline(wl, layer_inputs, args.cpu_seconds)

@@ -1,0 +1,33 @@
+/*
+ * vegas_probe.h -- measurement helper of libvegas_probe.so (built next to
+ * libvegas.so).  Not part of the Vegas path: it gives the benchmark a measured
+ * "practical peak" of HBM reads on the device at hand, next to the published
+ * 8 TB/s, for the roofline fraction of the bandwidth-bound kernels.
+ */
+#ifndef VEGAS_PROBE_H
+#define VEGAS_PROBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * Streaming read of `bytes` bytes of device memory from `src` (16-byte
+ * aligned, bytes a multiple of 16 * workgroups * 256) by `workgroups`
+ * workgroups of 256 threads: workgroup w reads the w-th equal contiguous
+ * slice with 16-byte loads, four in flight per thread, and folds what it read
+ * into sink[w] (device uint32 [workgroups]; written only for an all-zero
+ * fold, so the loads cannot be dropped).  Asynchronous on `stream`.
+ * Returns 0, or -1 for invalid arguments (nothing launched), or the HIP error
+ * code of the launch.
+ */
+int vegas_probe_stream_read(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

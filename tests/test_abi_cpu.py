@@ -221,3 +221,22 @@ def test_verify_select_sizes_and_argument_errors(V):
     with pytest.raises(V.VegasError) as e:   # the selection's own limit on the prefix length
         V.vegas_verify_select_workspace_size(s, 4, 2048 * 4096 + 1, 4 * (2048 * 4096 + 1))
     assert e.value.status == 2
+
+
+def test_probe_library_exports_and_rejects_bad_arguments(V):
+    """libvegas_probe.so (measurement helper of the benchmark) exports what its header declares and
+    validates its arguments before launching anything."""
+    from verification_guided_sparse_verify_amd import build as B
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "vegas_probe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(vegas_[a-z_0-9]+)\s*\(", text)))
+    assert names == ["vegas_probe_stream_read"]
+    nm = subprocess.run(["nm", "-D", "--defined-only", B.PROBE_LIB], capture_output=True, text=True).stdout
+    assert "vegas_probe_stream_read" in nm
+    fn = ctypes.CDLL(B.PROBE_LIB).vegas_probe_stream_read
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    unit = 16 * 256 * 256
+    assert fn(None, unit, 256, FAKE, None) == -1            # no source
+    assert fn(FAKE + 4, unit, 256, FAKE, None) == -1        # misaligned
+    assert fn(FAKE, unit + 16, 256, FAKE, None) == -1       # not a whole number of slices
+    assert fn(FAKE, unit, 0, FAKE, None) == -1              # no workgroups
+    assert fn(FAKE, unit, 256, None, None) == -1            # no sink

@@ -11,8 +11,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libvegas.so")
+PROBE_LIB = os.path.join(PKG, "libvegas_probe.so")
 
 SOURCES = ["attn.hip", "select.hip", "accept.hip", "api.cpp"]
+PROBE_SOURCES = ["probe.hip"]      # measurement helper, its own library
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
@@ -24,10 +26,17 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
+    """Build libvegas.so and libvegas_probe.so; returns the path of libvegas.so."""
+    _build_lib(SOURCES, LIB, verbose)
+    _build_lib(PROBE_SOURCES, PROBE_LIB, verbose)
+    return LIB
+
+
+def _build_lib(sources, lib, verbose: bool) -> str:
     os.makedirs(BUILD, exist_ok=True)
     procs = []
     objs = []
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
@@ -45,10 +54,10 @@ def build(verbose: bool = False) -> str:
             failed.append(src)
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     subprocess.run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp, *objs], check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
