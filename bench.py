@@ -495,6 +495,11 @@ def main():
     result["collect_select_overhead_vs_plain_verify"] = round(
         (mean["verify_select"] if fused else verify_mean + mean["select"]) / plain_us - 1, 4)
     result["collect_select_overhead_separate_calls"] = round(separate, 4)
+    # Achieved algorithmic bandwidth of each of the three calls (per-call means of the breakdown).
+    result["per_call_gbps"] = {
+        kind: {"algorithmic_bytes": ab[kind], "gbps": round(ab[kind] / (mean[kind] * 1e-6) / 1e9, 1),
+               "frac_of_peak": round(ab[kind] / (mean[kind] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+        for kind in ("verify", "select", "draft")}
 
     if not args.no_stream_ceiling:
         ceiling = stream_read_ceiling()
