@@ -197,6 +197,11 @@ SELECT_CASES = [
     (8, 5, [131072, 40000], [6553, 40000], 2),
     (1, 0, [2049, 2047, 4096], [1, 2047, 0], 1),
     (4, 1, [300000], [15000], 0),
+    # more ragged and tie-heavy lists: a partial last chunk, k = L, k = 1, all scores equal
+    (2, 3, [32768, 100, 0], [1638, 100, 0], 2),
+    (2, 3, [32769, 5], [3000, 5], 2),
+    (4, 1, [20000, 7], [1000, 7], 0),
+    (3, 2, [4000, 31, 1], [3999, 1, 1], 1),
 ]
 
 
