@@ -22,7 +22,7 @@
 //                                                   the ring, Q in registers
 //   collection (verification only)                 collected rows summed over
 //                                                   the query heads of g: a
-//                                                   16-lane DPP reduction,
+//                                                   16-lane DPP butterfly,
 //                                                   buffered in LDS
 //   online softmax over positions (exp2 domain)    rows are MFMA columns, so a
 //                                                   row max is in-lane + 2 shuffles
@@ -115,13 +115,20 @@ __device__ __forceinline__ float dpp(float x) {
     return __builtin_amdgcn_update_dpp(0.0f, x, CTRL, 0xf, 0xf, false);
 }
 
-// Sum over the 16 lanes of a DPP row; every lane of the row gets the sum.
-__device__ __forceinline__ float row16_sum(float x) {
-    x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]
-    x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]
-    x += dpp<0x124>(x);   // row_ror 4
-    x += dpp<0x128>(x);   // row_ror 8
-    return x;
+// Four sums over the 16 lanes of a DPP row at once, scattered: lane r of the
+// row returns the sum of x[r / 4] over the row.  Each step halves the values a
+// lane carries: lanes r and r^8 (row_ror 8) swap halves of their four, lanes r
+// and 7-r within each half row (row_half_mirror; they differ in bit 2 and
+// share bit 3) swap halves of the remaining two, then the pairs r^1 and r^2
+// (quad permutations) finish the single value: 5 DPP adds instead of 16.
+__device__ __forceinline__ float row16_sum4(const float (&x)[4], int lr) {
+    const bool b3 = (lr & 8) != 0, b2 = (lr & 4) != 0;
+    const float y0 = (b3 ? x[2] : x[0]) + dpp<0x128>(b3 ? x[0] : x[2]);
+    const float y1 = (b3 ? x[3] : x[1]) + dpp<0x128>(b3 ? x[1] : x[3]);
+    float z = (b2 ? y1 : y0) + dpp<0x141>(b2 ? y0 : y1);
+    z += dpp<0xB1>(z);   // quad_perm [1,0,3,2]
+    z += dpp<0x4E>(z);   // quad_perm [2,3,0,1]
+    return z;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -172,7 +179,7 @@ struct Geo {
     static constexpr int TLD = kAttnBlock / RPI;  // copies per lane per K (or V) tile
     static constexpr int TILE = kAttnBlock * ROWB;
     static constexpr int STAGE = 2 * TILE;        // K tile then V tile
-    static constexpr int NST = kAttnStages;       // ring depth
+    static constexpr int NST = attn_stages(BF16, D);   // ring depth
     static constexpr int RING = kAttnWaves * NST * STAGE;
     static constexpr int BLOCK_OPS = 2 * TLD;     // copies one block issues
     static constexpr int SWZU = 16 / EPC;         // chunks per 16-element d tile
@@ -421,24 +428,21 @@ __device__ __forceinline__ void compute_block(const AttnArgs& a, WaveState<BF16,
     // holding the query rows), times s.
     if constexpr (COLLECT) {
         if (p0 < L) {
-            float red[4];
+            float x[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                float x = 0.f;
+                x[v] = 0.f;
 #pragma unroll
-                for (int qb = 0; qb < MB; ++qb) x += ws.cmask[qb] * s[qb][v];
-                red[v] = row16_sum(x);
+                for (int qb = 0; qb < MB; ++qb) x[v] += ws.cmask[qb] * s[qb][v];
             }
-            if (lr < 4) {
-                float val = red[0];
-                val = (lr == 1) ? red[1] : val;
-                val = (lr == 2) ? red[2] : val;
-                val = (lr == 3) ? red[3] : val;
+            const float sum = row16_sum4(x, lr);      // position 4*lg + lr/4 of the block
+            if ((lr & 3) == 0) {
+                const int idx = p0 - start + 4 * lg + (lr >> 2);
                 if constexpr (HOLD) {
-                    ws.pend_val = a.scale * val;
-                    ws.pend_idx = p0 - start + 4 * lg + lr;
+                    ws.pend_val = a.scale * sum;
+                    ws.pend_idx = idx;
                 } else {
-                    score_s[p0 - start + 4 * lg + lr] = a.scale * val;
+                    score_s[idx] = a.scale * sum;
                 }
             }
         }

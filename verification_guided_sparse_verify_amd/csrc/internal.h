@@ -8,12 +8,16 @@
 
 namespace vegas {
 
-// Waves per attention workgroup, positions per wave iteration, and depth of
-// each wave's LDS ring of K/V blocks (one block computed while the next one
-// is in flight; deeper rings measured slower).
+// Waves per attention workgroup and positions per wave iteration.
 constexpr int kAttnWaves = 4;
 constexpr int kAttnBlock = 16;
-constexpr int kAttnStages = 2;
+// Depth of each wave's LDS ring of K/V blocks: enough stages that the blocks
+// in flight (all but the one being computed) hold at least 8 KB per wave,
+// 32 KB per CU, where streaming reads saturate; deeper rings measured slower.
+// 2 stages (one 8 KB block in flight) except bf16 at D = 64 (4 KB blocks): 3.
+__host__ __device__ constexpr int attn_stages(bool bf16, int head_dim) {
+    return (bf16 && head_dim == 64) ? 3 : 2;
+}
 // Longest position range one workgroup takes in gather mode: its index list
 // is staged in LDS.
 constexpr int kMaxGatherChunk = 2048;
@@ -26,7 +30,7 @@ constexpr int kMaxBatch = 1024;
 
 // Bytes of one workgroup's K/V ring.
 __host__ __device__ constexpr int attn_ring_bytes(bool bf16, int head_dim) {
-    return kAttnWaves * kAttnStages * 2 * kAttnBlock * head_dim * (bf16 ? 2 : 4);
+    return kAttnWaves * attn_stages(bf16, head_dim) * 2 * kAttnBlock * head_dim * (bf16 ? 2 : 4);
 }
 // Longest position range one workgroup takes in verification: the collected
 // scores of its range are buffered in LDS next to the ring (144 KB in all of
