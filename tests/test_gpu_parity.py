@@ -449,3 +449,45 @@ def test_verify_select_one_call_equals_two_calls(case):
         ws.fill_(0xFF if rep == 0 else 0x00)
     if not isinstance(case, str):
         check_layer(wl, inp, st)
+
+
+def test_out_of_range_device_indices_are_clamped():
+    """Index values read from device memory are clamped to the owning sequence (the header's
+    promise): a draft list holding negative and too-large positions attends to the clamped
+    rows, as the oracle does on the clamped list; a selection budget above L_b writes the
+    L_b prefix positions and leaves the extra slots alone."""
+    from parity_util import _seq_host
+    wl = W.custom_workload("bf16", 2, 16, 4, 64, 2, [300, 41])
+    inp, st = run_layer(wl, seed=12)
+    Wr = wl.gamma + 1
+    lens = wl.seqlens
+    raw = [np.array([-3, 5, 7, lens[0] + 50, 2 ** 30, 0], np.int32), np.array([lens[1], -1, 40, 9], np.int32)]
+    clamped = [np.clip(x, 0, n - 1).astype(np.int32) for x, n in zip(raw, lens)]
+    cui = np.array([0, len(raw[0]), len(raw[0]) + len(raw[1])], np.int32)
+    q = inp["draft_q"][0].contiguous()
+    out = torch.empty_like(q)
+    mx = max(len(x) for x in raw)
+    ws = torch.empty(V.vegas_sparse_decode_workspace_size(st.shape, mx), dtype=torch.uint8, device="cuda")
+    V.vegas_sparse_decode_attn(st.shape, q, inp["k"], inp["v"], inp["cu_seqlens_k"], wl.total_kv,
+                               torch.from_numpy(np.concatenate(raw)).cuda(), torch.from_numpy(cui).cuda(), mx, out, ws)
+    torch.cuda.synchronize()
+    for b in range(wl.batch):
+        _, k, v, cu1 = _seq_host(inp, wl, b)
+        ref = oracle.sparse_decode_attn(W.host_bits(q[b:b + 1]), k, v, cu1, clamped[b],
+                                        np.array([0, len(clamped[b])], np.int32), wl.scale)
+        err = float(np.abs(out[b:b + 1].float().cpu().numpy() - ref).max())
+        assert err <= ATOL["bf16"], (b, err)
+
+    # selection budget above the prefix: k_0 = L_0 + 5
+    L0, L1 = wl.prefix_lens
+    cuk = np.array([0, L0 + 5, L0 + 5 + 3], np.int32)
+    idx = torch.full((int(cuk[-1]),), -9, dtype=torch.int32, device="cuda")
+    sws = torch.empty(V.vegas_select_workspace_size(wl.batch, wl.num_kv_heads, wl.gamma, max(lens), wl.total_kv),
+                      dtype=torch.uint8, device="cuda")
+    V.vegas_select_topk(wl.batch, wl.num_kv_heads, wl.gamma, st.scores, inp["cu_seqlens_k"], max(lens), wl.total_kv,
+                        torch.from_numpy(cuk).cuda(), idx, sws)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    assert np.array_equal(got[:L0], np.arange(L0))          # every prefix position, ascending
+    assert np.all(got[L0:L0 + 5] == -9)                       # the extra slots untouched
+    assert len(set(got[L0 + 5:].tolist())) == 3 and np.all(np.diff(got[L0 + 5:]) > 0)
