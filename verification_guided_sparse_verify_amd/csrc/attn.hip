@@ -131,6 +131,26 @@ __device__ __forceinline__ float row16_sum4(const float (&x)[4], int lr) {
     return z;
 }
 
+// Max and sum over the lane pairs (l, l^16) and (l, l^32): gfx950's permlane
+// swaps leave the pair's two values in the two outputs (checked on the device
+// with a probe), a VALU exchange where a shuffle would go through LDS.
+__device__ __forceinline__ float pair16_max(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair16_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Compiler barrier that also drains outstanding LDS operations of this wave.
@@ -470,8 +490,7 @@ __device__ __forceinline__ void compute_block(const AttnArgs& a, WaveState<BF16,
 #pragma unroll
     for (int qb = 0; qb < MB; ++qb) {
         float mx = fmaxf(fmaxf(s[qb][0], s[qb][1]), fmaxf(s[qb][2], s[qb][3]));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = pair32_max(pair16_max(mx));
         mx *= a.scale_log2;
         const float m_new = fmaxf(ws.m_run[qb], mx);
         const float m_use = (m_new == kNegInf) ? 0.f : m_new;
@@ -740,8 +759,7 @@ attn_split_kernel(const AttnArgs a) {
     // Row sums: each lane summed its own positions.
 #pragma unroll
     for (int qb = 0; qb < MBW; ++qb) {
-        ws.l_run[qb] += __shfl_xor(ws.l_run[qb], 16);
-        ws.l_run[qb] += __shfl_xor(ws.l_run[qb], 32);
+        ws.l_run[qb] = pair32_sum(pair16_sum(ws.l_run[qb]));
     }
 
     // Tree merge of the position groups' (m, l, O) through LDS, in fragment
