@@ -392,23 +392,10 @@ struct WaveState {
     int pend_idx;
 };
 
-// PV step: acc += V^T(16 d x 16 pos) . P^T(16 pos x 16 rows).  Lane (lr, lg)
-// supplies d (resp. row) lr and the k slots = positions 4*lg .. 4*lg+3, which
-// is where the S^T accumulator left its probabilities.
-__device__ __forceinline__ f32x4_t mfma_pv(const uint32_t (&vt)[4], const float (&p)[4], f32x4_t acc,
-                                           std::true_type) {
-    typedef short s16x4_t __attribute__((ext_vector_type(4)));
-    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-    bf16x4_t pb;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pb[i] = static_cast<__bf16>(p[i]);
-    s16x4_t va;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) va[i] = (short)vt[i];
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, __builtin_bit_cast(s16x4_t, pb), acc, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4_t mfma_pv(const uint32_t (&vt)[4], const float (&p)[4], f32x4_t acc,
-                                           std::false_type) {
+// PV step (fp32): acc += V^T(16 d x 16 pos) . P^T(16 pos x 16 rows).  Lane
+// (lr, lg) supplies d (resp. row) lr and the k slots = positions 4*lg ..
+// 4*lg+3, which is where the S^T accumulator left its probabilities.
+__device__ __forceinline__ f32x4_t mfma_pv(const uint32_t (&vt)[4], const float (&p)[4], f32x4_t acc) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vt[m]), p[m], acc, 0, 0, 0);
     return acc;
@@ -514,20 +501,47 @@ __device__ __forceinline__ void compute_block(const AttnArgs& a, WaveState<BF16,
     }
 
     // O^T += V^T P^T over the 16 positions of the block.
+    if constexpr (BF16) {
+        // The V^T operand by transposed LDS reads (gfx950 ds_read_b64_tr_b16;
+        // its lane mapping was checked on the device with a probe).  Within the
+        // 16-lane group lg, lane (m, q) = (lr / 4, lr % 4) points at the four d
+        // values 16*db + 4q .. +3 of position 4*lg + m; the read then hands
+        // lane lr the values V[4*lg + e][16*db + lr], e = 0..3: its A-operand
+        // k slots, the positions where the S^T accumulator left its P values.
+        typedef short s16x4_t __attribute__((ext_vector_type(4)));
+        typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+        s16x4_t pb[MB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-        const int d = 16 * db + lr;
-        const unsigned char* base = vtile + (4 * lg) * GEO::ROWB +
-                                    (((d / EPC) ^ (GEO::SWZU * lg)) << 4) + (d % EPC) * GEO::ES;
-        uint32_t vt[4];
+        for (int qb = 0; qb < MB; ++qb) {
+            bf16x4_t t;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            if constexpr (BF16) vt[m] = *reinterpret_cast<const uint16_t*>(base + m * GEO::ROWB);
-            else vt[m] = *reinterpret_cast<const uint32_t*>(base + m * GEO::ROWB);
+            for (int i = 0; i < 4; ++i) t[i] = static_cast<__bf16>(pr[qb][i]);
+            pb[qb] = __builtin_bit_cast(s16x4_t, t);
         }
+        const int q = lr & 3;
+        const unsigned char* vrow = vtile + (4 * lg + (lr >> 2)) * GEO::ROWB + 8 * (q & 1);
 #pragma unroll
-        for (int qb = 0; qb < MB; ++qb)
-            ws.o[db][qb] = mfma_pv(vt, pr[qb], ws.o[db][qb], std::integral_constant<bool, BF16>());
+        for (int db = 0; db < DB; ++db) {
+            const unsigned char* src = vrow + (((2 * db + (q >> 1)) ^ (GEO::SWZU * lg)) << 4);
+            const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(src));
+            const s16x4_t va = __builtin_bit_cast(s16x4_t, v);
+#pragma unroll
+            for (int qb = 0; qb < MB; ++qb)
+                ws.o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[qb], ws.o[db][qb], 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const int d = 16 * db + lr;
+            const unsigned char* base = vtile + (4 * lg) * GEO::ROWB +
+                                        (((d / EPC) ^ (GEO::SWZU * lg)) << 4) + (d % EPC) * GEO::ES;
+            uint32_t vt[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) vt[m] = *reinterpret_cast<const uint32_t*>(base + m * GEO::ROWB);
+#pragma unroll
+            for (int qb = 0; qb < MB; ++qb) ws.o[db][qb] = mfma_pv(vt, pr[qb], ws.o[db][qb]);
+        }
     }
     lds_fence();   // this stage's reads are done before it is refilled
 }
