@@ -138,7 +138,9 @@ def cpu_model() -> str:
 
 def stream_read_ceiling(nbytes: int = 4 << 30, reps: int = 5):
     """Best HBM streaming-read rate of a plain read kernel (libvegas_probe.so) over a few
-    workgroup counts: a measured practical peak next to the published one."""
+    workgroup counts: a measured practical peak next to the published one.  The probe reads
+    with the attention kernels' own load path (direct-to-LDS, non-temporal policy), the
+    fastest of the read paths tried on MI355X."""
     import ctypes
     import torch
     from verification_guided_sparse_verify_amd import build as B
@@ -170,7 +172,7 @@ def stream_read_ceiling(nbytes: int = 4 << 30, reps: int = 5):
             best = (gbps, wgs)
     del buf, sink
     return {"gbps": round(best[0], 1), "workgroups": best[1], "bytes": nbytes,
-            "kernel": "vegas_probe_stream_read (16-byte loads, 4 in flight per thread)"}
+            "kernel": "vegas_probe_stream_read (16-byte non-temporal direct-to-LDS copies, 8 KB in flight per wave)"}
 
 
 def collect_sweep(base, gammas=(1, 3, 5, 7, 11, 15), reps=8):

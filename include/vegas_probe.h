@@ -16,13 +16,14 @@ extern "C" {
 
 /*
  * Streaming read of `bytes` bytes of device memory from `src` (16-byte
- * aligned, bytes a multiple of 16 * workgroups * 256) by `workgroups`
+ * aligned, bytes a multiple of 32768 * workgroups) by `workgroups`
  * workgroups of 256 threads: workgroup w reads the w-th equal contiguous
- * slice with 16-byte loads, four in flight per thread, and folds what it read
- * into sink[w] (device uint32 [workgroups]; written only for an all-zero
- * fold, so the loads cannot be dropped).  Asynchronous on `stream`.
- * Returns 0, or -1 for invalid arguments (nothing launched), or the HIP error
- * code of the launch.
+ * slice in rounds of 32 KB, each of its four waves copying 8 KB into its own
+ * LDS with eight 16-byte-per-lane direct-to-LDS loads in flight under the
+ * non-temporal cache policy (the load path of the attention kernels).  The
+ * last round is folded into sink[w] (device uint32 [workgroups]; written only
+ * for an all-zero fold).  Asynchronous on `stream`.  Returns 0, or -1 for
+ * invalid arguments (nothing launched), or the HIP error code of the launch.
  */
 int vegas_probe_stream_read(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink, void* stream);
 

@@ -234,7 +234,7 @@ def test_probe_library_exports_and_rejects_bad_arguments(V):
     assert "vegas_probe_stream_read" in nm
     fn = ctypes.CDLL(B.PROBE_LIB).vegas_probe_stream_read
     fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
-    unit = 16 * 256 * 256
+    unit = 32768 * 256
     assert fn(None, unit, 256, FAKE, None) == -1            # no source
     assert fn(FAKE + 4, unit, 256, FAKE, None) == -1        # misaligned
     assert fn(FAKE, unit + 16, 256, FAKE, None) == -1       # not a whole number of slices

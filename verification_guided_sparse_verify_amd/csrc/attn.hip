@@ -161,9 +161,12 @@ __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)
 // analysis would otherwise make every later LDS read wait for all copies in
 // flight, including the next block's.  Completion is ordered by vmcnt like
 // any load, and the block loop waits for it explicitly (wait_vmem).
+// The copy carries the non-temporal cache policy (nt): every K/V row is read
+// once per call, and streaming reads with that policy run at ~7.2 TB/s on
+// MI355X against ~6.3 TB/s with the default one (same kernel otherwise).
 __device__ __forceinline__ void copy16_to_lds(const void* src, unsigned char* lds) {
     const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds_addr) : "memory");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(src), "{m0}"(lds_addr) : "memory");
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding

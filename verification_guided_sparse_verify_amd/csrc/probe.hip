@@ -7,24 +7,38 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kInFlight = 4;     // 16-byte loads per thread per round
+constexpr int kInFlight = 8;     // 1 KB wave-wide copies per wave per round
+constexpr size_t kRoundBytes = (size_t)16 * kThreads * kInFlight;
 
-__global__ void __launch_bounds__(kThreads) stream_read_kernel(const uint4* __restrict__ src, size_t per_wg16,
-                                                               uint32_t* __restrict__ sink) {
-    const uint4* base = src + (size_t)blockIdx.x * per_wg16;
-    uint32_t acc = 0;
-    for (size_t i = threadIdx.x; i < per_wg16; i += (size_t)kThreads * kInFlight) {
-        uint4 v[kInFlight];
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Each wave streams its part of the workgroup's slice into its own 8 KB of
+// LDS with 16-byte direct-to-LDS copies (non-temporal policy), eight in
+// flight, then waits for all of them before the next round.
+__global__ void __launch_bounds__(kThreads) stream_read_kernel(const unsigned char* __restrict__ src,
+                                                               size_t per_wg, uint32_t* __restrict__ sink) {
+    __shared__ __attribute__((aligned(16))) uint4 buf[kThreads * kInFlight];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const unsigned char* base = src + (size_t)blockIdx.x * per_wg + (size_t)wave * 1024 * kInFlight + 16 * lane;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)(buf + wave * 64 * kInFlight);
+    for (size_t off = 0; off < per_wg; off += kRoundBytes) {
 #pragma unroll
         for (int u = 0; u < kInFlight; ++u) {
-            const size_t j = i + (size_t)u * kThreads;
-            v[u] = j < per_wg16 ? base[j] : make_uint4(0, 0, 0, 0);
+            const unsigned char* p = base + off + (size_t)u * 1024;
+            asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(p), "{m0}"(lds0 + 1024u * u)
+                         : "memory");
         }
-#pragma unroll
-        for (int u = 0; u < kInFlight; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    // one lane per workgroup reports only a zero fold (never, for data of any
-    // interest), which keeps the loads live without a store per thread
+    __syncthreads();
+    // Fold the last round; one lane per workgroup reports only a zero fold
+    // (never, for data of any interest).
+    uint32_t acc = 0;
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) {
+        const uint4 v = buf[u * kThreads + threadIdx.x];
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
     if (acc == 0u && threadIdx.x == 0) sink[blockIdx.x] = 1u;
 }
 
@@ -33,10 +47,9 @@ __global__ void __launch_bounds__(kThreads) stream_read_kernel(const uint4* __re
 extern "C" int vegas_probe_stream_read(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink,
                                        void* stream) {
     if (!src || !sink || workgroups < 1 || (reinterpret_cast<uintptr_t>(src) & 15u) != 0) return -1;
-    const size_t unit = (size_t)16 * workgroups * kThreads;
+    const size_t unit = kRoundBytes * (size_t)workgroups;
     if (bytes == 0 || bytes % unit != 0) return -1;
-    const size_t per_wg16 = bytes / 16 / (size_t)workgroups;
     hipLaunchKernelGGL(stream_read_kernel, dim3(workgroups), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
-                       static_cast<const uint4*>(src), per_wg16, sink);
+                       static_cast<const unsigned char*>(src), bytes / (size_t)workgroups, sink);
     return (int)hipGetLastError();
 }
