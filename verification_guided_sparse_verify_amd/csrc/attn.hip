@@ -380,6 +380,10 @@ __device__ __forceinline__ void batch_plan(const AttnArgs& a, int* red, int (&ns
     plan(best);
 }
 
+// Headroom of the lazily moved softmax reference (log2 units): block
+// probabilities are at most 2^8, far inside bf16/fp32 range.
+constexpr float kRescaleSlack = 8.f;
+
 // Per-wave running state of the online softmax.
 template <bool BF16, int D, int MB>
 struct WaveState {
@@ -482,10 +486,18 @@ __device__ __forceinline__ void compute_block(const AttnArgs& a, WaveState<BF16,
         float mx = fmaxf(fmaxf(s[qb][0], s[qb][1]), fmaxf(s[qb][2], s[qb][3]));
         mx = pair32_max(pair16_max(mx));
         mx *= a.scale_log2;
-        const float m_new = fmaxf(ws.m_run[qb], mx);
+        // Lazy rescaling: the running reference m moves (and O, l are
+        // rescaled) only when a block's max exceeds it by more than
+        // kRescaleSlack (log2 units), so the probabilities stay below
+        // 2^kRescaleSlack and the O rescale runs a handful of times per
+        // split instead of whenever any row's max creeps up.  The result is
+        // the same softmax in real arithmetic ((m, l, O) stay consistent).
+        const float m_old = ws.m_run[qb];
+        const bool grow = mx > m_old + kRescaleSlack;     // also the first finite block
+        const float m_new = grow ? mx : m_old;
         const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-        alpha[qb] = fast_exp2(ws.m_run[qb] - m_use);
-        rescale |= (alpha[qb] != 1.f);
+        alpha[qb] = grow ? fast_exp2(m_old - m_use) : 1.f;
+        rescale |= grow;
         ws.m_run[qb] = m_new;
         float ls = 0.f;
 #pragma unroll
