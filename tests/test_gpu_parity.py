@@ -118,6 +118,51 @@ def test_all_zero_queries_select_lowest_positions():
         assert got == list(range(wl.k_per_seq[b]))
 
 
+LOGIT_CASES = [
+    ("bf16", 128, "drift"), ("bf16", 64, "drift"), ("bf16", 128, "wide"), ("f32", 64, "drift"),
+]
+
+
+@pytest.mark.parametrize("case", LOGIT_CASES, ids=lambda c: f"{c[0]}-D{c[1]}-{c[2]}")
+def test_logit_patterns_that_move_the_softmax_reference(case):
+    """Logits with a designed course along the positions, so the kernels' running softmax
+    reference moves often: 'drift' oscillates by +-7 (log2 units) around a rise of 12 over the
+    prefix, so many blocks carry weight and the reference moves a few times; 'wide' draws
+    every position's logit with a spread of 40 (log2 units), so it moves many times early.
+    Built as K = f(pos)/D * u_g + small noise and q = a * u_g (u_g a +-1 vector per KV head,
+    a per row and head in [0.8, 1.2])."""
+    dt, d, pattern = case
+    wl = W.custom_workload(dt, 2, 8, 2, d, 3, [3000, 1200], plants=False)
+    inp = W.make_inputs(wl, seed=21, device="cuda")
+    g = torch.Generator().manual_seed(77)
+    tdt = inp["k"].dtype
+    log2e = 1.4426950408889634
+    u = torch.randint(0, 2, (wl.num_kv_heads, d), generator=g).double() * 2 - 1
+    cu = wl.cu_seqlens()
+    k = torch.empty(wl.total_kv, wl.num_kv_heads, d, dtype=torch.float64)
+    for b in range(wl.batch):
+        n = cu[b + 1] - cu[b]
+        pos = torch.arange(n, dtype=torch.float64)
+        for h in range(wl.num_kv_heads):
+            if pattern == "drift":
+                t = 7.0 * torch.sin(2 * np.pi * pos / 200.0 + h) + 12.0 * pos / n
+            else:
+                t = 40.0 * torch.randn(n, generator=g, dtype=torch.float64)
+            f = t / (wl.scale * log2e)
+            k[cu[b]:cu[b + 1], h] = f[:, None] / d * u[h][None, :] + 0.02 * torch.randn(n, d, generator=g,
+                                                                                        dtype=torch.float64)
+    inp["k"].copy_(k.to(tdt))
+    G = wl.num_q_heads // wl.num_kv_heads
+    heads = torch.arange(wl.num_q_heads) // G
+    qa = 0.8 + 0.4 * torch.rand(wl.batch * (wl.gamma + 1), wl.num_q_heads, 1, generator=g, dtype=torch.float64)
+    inp["q"].copy_((qa * u[heads][None]).to(tdt))
+    da = 0.8 + 0.4 * torch.rand(wl.n_drafts, wl.batch, wl.num_q_heads, 1, generator=g, dtype=torch.float64)
+    inp["draft_q"].copy_((da * u[heads][None, None]).to(tdt))
+    inp, st = run_layer(wl, inputs=inp)
+    worst = check_layer(wl, inp, st)
+    log(f"{dt} D{d} {pattern}: {worst}")
+
+
 def test_empty_draft_list_gives_zero_rows():
     wl = W.custom_workload("bf16", 2, 8, 2, 128, 1, [100, 100])
     inp = W.make_inputs(wl, seed=6, device="cuda")
