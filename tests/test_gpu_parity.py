@@ -181,6 +181,76 @@ def test_empty_draft_list_gives_zero_rows():
     assert np.abs(out.float().cpu().numpy() - ref).max() <= 2e-2
 
 
+def test_all_draft_lists_empty():
+    """Every list empty (nothing to gather anywhere): all rows are zero."""
+    wl = W.custom_workload("bf16", 3, 8, 2, 128, 1, [100, 40, 7])
+    inp = W.make_inputs(wl, seed=7, device="cuda")
+    st = LayerStep(inp, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.gamma, wl.seqlens,
+                   wl.k_per_seq, wl.scale)
+    cui = torch.zeros(4, dtype=torch.int32, device="cuda")
+    idx = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for max_idx in (0, 5):
+        out = torch.full_like(inp["draft_q"][0], 7.0)
+        V.vegas_sparse_decode_attn(st.shape, inp["draft_q"][0], inp["k"], inp["v"], inp["cu_seqlens_k"],
+                                   wl.total_kv, idx, cui, max_idx, out, st.workspace)
+        torch.cuda.synchronize()
+        assert torch.all(out == 0)
+
+
+def _draft_case():
+    """Two sequences whose lists take many splits per KV head (many partials to merge)."""
+    wl = W.custom_workload("bf16", 2, 16, 4, 128, 2, [20000, 9000], ratio=Fraction(20, 100))
+    inp, st = run_layer(wl, seed=8)
+    return wl, inp, st
+
+
+def test_draft_merge_takes_any_workspace_contents():
+    """The drafting call needs nothing from the workspace's previous contents: zeros, all ones,
+    random bytes and another call's leftovers give the same bits."""
+    wl, inp, st = _draft_case()
+    ref = st.draft_out[0].clone()
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    fills = [lambda w: w.zero_(), lambda w: w.fill_(255),
+             lambda w: w.copy_(torch.randint(0, 256, w.shape, generator=gen, device="cuda", dtype=torch.uint8)),
+             lambda w: st.verify()]
+    for fill in fills:
+        fill(st.workspace)
+        out = torch.full_like(ref, 3.0)
+        V.vegas_sparse_decode_attn(st.shape, inp["draft_q"][0], inp["k"], inp["v"], inp["cu_seqlens_k"],
+                                   wl.total_kv, st.indices, inp["cu_k"], st.max_k, out, st.workspace)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    check_layer(wl, inp, st)
+
+
+def test_draft_graph_replays():
+    """A drafting call captured in a HIP graph gives the eager result on every replay, also after
+    eager calls on the same workspace in between."""
+    wl, inp, st = _draft_case()
+    ref = st.draft_out[1].clone()
+    out = torch.empty_like(ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):       # warm-up outside the capture
+        V.vegas_sparse_decode_attn(st.shape, inp["draft_q"][1], inp["k"], inp["v"], inp["cu_seqlens_k"],
+                                   wl.total_kv, st.indices, inp["cu_k"], st.max_k, out, st.workspace)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        V.vegas_sparse_decode_attn(st.shape, inp["draft_q"][1], inp["k"], inp["v"], inp["cu_seqlens_k"],
+                                   wl.total_kv, st.indices, inp["cu_k"], st.max_k, out, st.workspace)
+    for rep in range(4):
+        out.fill_(5.0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
+        if rep == 1:                    # eager calls on the same workspace in between
+            st.draft(0)
+            st.draft(1)
+            torch.cuda.synchronize()
+
+
 def test_qwen3_8b_layer_full():
     wl = W.named_workload(1)
     log(f"case: {wl.name}")

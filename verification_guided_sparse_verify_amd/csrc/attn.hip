@@ -366,7 +366,8 @@ __device__ __forceinline__ void batch_plan(const AttnArgs& a, int* red, int (&ns
         }
         return wg_sum<NT>(u, red);
     };
-    if (total <= 0 || plan(a.target) <= a.target) return;
+    // (plan runs first also when every list is empty: it sets ns = 0 for all)
+    if (plan(a.target) <= a.target || total <= 0) return;
     int lo = 1, hi = a.target - 1, best = 1;   // the unit count does not decrease with t
     while (lo <= hi) {
         const int mid = (lo + hi) >> 1;
