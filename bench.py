@@ -296,6 +296,9 @@ def main():
     ap.add_argument("--accept-bench", action="store_true",
                     help="only time the speculative-sampling acceptance step (batch 4, gamma 5, "
                          "Qwen3 vocabulary 151936, and batch 16, gamma 3, gpt-oss vocabulary 201088)")
+    ap.add_argument("--device-plan", action="store_true",
+                    help="time the entry points that plan splits on the device (default: the *_hostplan entry "
+                         "points, which take host copies of the offsets; same results)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a device copy of BYTES bytes three times (counter calibration)")
     args = ap.parse_args()
@@ -347,10 +350,13 @@ def main():
     print(f"# generated {layers} layers in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
-    bound = [st.bind(stream) for st in steps]     # ctypes arguments converted once
+    # Host-planned entry points (host copies of the offsets) unless asked otherwise; they
+    # cover the contiguous cache.
+    host_plan = not args.device_plan and not args.page_size
+    bound = [st.bind(stream, host_plan=host_plan) for st in steps]     # ctypes arguments converted once
     # Verification and selection as one library call where the path allows it.
     fused = steps[0].fusable and not args.separate_calls
-    fused_calls = [st.bind_fused(stream) for st in steps] if fused else None
+    fused_calls = [st.bind_fused(stream, host_plan=host_plan) for st in steps] if fused else None
 
     def one_step(head_events=None, call_events=None):
         """One speculative iteration: verify + select on every layer, then gamma drafting
@@ -477,8 +483,12 @@ def main():
                          "and selection as one call)" if fused else "the timed region"),
         },
     }
-    result["config"]["calls"] = ("vegas_verify_select + gamma x vegas_sparse_decode_attn per layer" if fused else
-                                 "verify, select and gamma sparse-decode calls per layer")
+    sfx = "_hostplan" if host_plan else ""
+    result["config"]["calls"] = (f"vegas_verify_select{sfx} + gamma x vegas_sparse_decode_attn{sfx} per layer"
+                                 if fused else
+                                 f"verify{sfx}, select and gamma sparse-decode{sfx} calls per layer")
+    result["config"]["split_plan"] = ("host (host copies of the offsets, computed per call)" if host_plan
+                                      else "device")
 
     # Plain verification (collection off) on the same layers, for the collection + select overhead.
     plain = []

@@ -175,6 +175,51 @@ vegas_status_t vegas_verify_select(const vegas_attn_shape_t* shape, int32_t gamm
                                    void* stream);
 
 /*
+ * Host copies of the offset arrays, for the *_hostplan entry points.
+ * A serving loop (the pages hook vLLM, "Vegas ..." sec. 4) keeps every
+ * sequence's length on the host.  Given host copies, the library computes
+ * the split plan on the host and passes it in the kernel arguments, so the
+ * kernels start without reading the offsets or planning on the device.  The
+ * plan, and so every result bit, is the one the device computes from the
+ * same values: the *_hostplan calls give exactly the results of the calls
+ * without the suffix.  Batches above 16 sequences are planned on the device
+ * as before (same results).
+ *
+ *  cu_seqlens_k   host int32 [batch+1]: the values of the device array.
+ *  cu_idx         host int32 [batch+1]: the values of the device cu_k (for
+ *                 vegas_verify_select_hostplan) or cu_idx (for
+ *                 vegas_sparse_decode_attn_hostplan); unused (may be NULL)
+ *                 by vegas_verify_attn_hostplan.
+ * Both are read during the call only (not kept).  They are checked on the
+ * host: non-decreasing, starting at >= 0, cu_seqlens_k within total_kv with
+ * every length in [gamma+1, max_seqlen_k] (verification), every list at most
+ * max_idx long (drafting); a violation returns VEGAS_ERR_INVALID_ARGUMENT and
+ * launches nothing.  The device arrays must hold the same values; they are
+ * still passed (and still read where the plan does not cover them).
+ */
+typedef struct {
+    const int32_t* cu_seqlens_k;
+    const int32_t* cu_idx;
+} vegas_host_offsets_t;
+
+/* vegas_verify_attn with host offsets (cu_idx unused); workspace as for
+ * vegas_verify_attn. */
+vegas_status_t vegas_verify_attn_hostplan(const vegas_attn_shape_t* shape, int32_t gamma,
+                                          const void* q, const void* k, const void* v,
+                                          const int32_t* cu_seqlens_k, int32_t max_seqlen_k,
+                                          int32_t total_kv, uint32_t collect_mask, float* scores,
+                                          void* out, void* workspace, size_t workspace_bytes,
+                                          void* stream, const vegas_host_offsets_t* host);
+/* vegas_verify_select with host offsets; workspace as for vegas_verify_select. */
+vegas_status_t vegas_verify_select_hostplan(const vegas_attn_shape_t* shape, int32_t gamma,
+                                            const void* q, const void* k, const void* v,
+                                            const int32_t* cu_seqlens_k, int32_t max_seqlen_k,
+                                            int32_t total_kv, uint32_t collect_mask,
+                                            const int32_t* cu_k, float* scores, int32_t* indices,
+                                            void* out, void* workspace, size_t workspace_bytes,
+                                            void* stream, const vegas_host_offsets_t* host);
+
+/*
  * Sparse drafting attention over selected tokens.
  * Defined by "Vegas ..." sec. 4 "Serving framework integration" (paged
  * attention with a page size of one token whose page indices are the
@@ -199,6 +244,15 @@ vegas_status_t vegas_sparse_decode_attn(const vegas_attn_shape_t* shape, const v
                                         const int32_t* indices, const int32_t* cu_idx,
                                         int32_t max_idx, void* out, void* workspace,
                                         size_t workspace_bytes, void* stream);
+/* vegas_sparse_decode_attn with host offsets (vegas_host_offsets_t above);
+ * workspace: vegas_sparse_decode_workspace_size. */
+vegas_status_t vegas_sparse_decode_attn_hostplan(const vegas_attn_shape_t* shape, const void* q,
+                                                 const void* k, const void* v,
+                                                 const int32_t* cu_seqlens_k, int32_t total_kv,
+                                                 const int32_t* indices, const int32_t* cu_idx,
+                                                 int32_t max_idx, void* out, void* workspace,
+                                                 size_t workspace_bytes, void* stream,
+                                                 const vegas_host_offsets_t* host);
 
 /*
  * Paged KV cache (NEXT to the contiguous layout above).

@@ -223,6 +223,47 @@ def test_verify_select_sizes_and_argument_errors(V):
     assert e.value.status == 2
 
 
+def test_hostplan_offsets_are_checked_before_launch(V):
+    """The *_hostplan calls check the host copies of the offsets and launch nothing when they
+    are malformed (batch 4, gamma 4: every sequence needs 5 .. max_seqlen_k rows)."""
+    s = shape(V)
+    L = V.lib()
+    need = V.vegas_verify_select_workspace_size(s, 4, 1000, 4000)
+    vws = V.vegas_verify_workspace_size(s, 4, 1000)
+    dws = V.vegas_sparse_decode_workspace_size(s, 50)
+    good_cu, good_k = [0, 1000, 2000, 3000, 4000], [0, 50, 100, 150, 200]
+
+    def vs(cu, cuk, host=True):
+        h = V.host_offsets(cu, cuk)
+        return L.vegas_verify_select_hostplan(ctypes.byref(s), 4, FAKE, FAKE, FAKE, FAKE, 1000, 4000, 1 | 16, FAKE,
+                                              FAKE, FAKE, FAKE, FAKE, need, None, ctypes.byref(h) if host else None)
+
+    def va(cu):
+        h = V.host_offsets(cu, [0])
+        return L.vegas_verify_attn_hostplan(ctypes.byref(s), 4, FAKE, FAKE, FAKE, FAKE, 1000, 4000, 0, None, FAKE,
+                                            FAKE, vws, None, ctypes.byref(h))
+
+    def dr(cu, cui):
+        h = V.host_offsets(cu, cui)
+        return L.vegas_sparse_decode_attn_hostplan(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 4000, FAKE, FAKE, 50,
+                                                   FAKE, FAKE, dws, None, ctypes.byref(h))
+
+    assert vs(good_cu, good_k, host=False) == 1
+    assert vs([0, 1000, 900, 3000, 4000], good_k) == 1          # decreasing
+    assert vs([0, 1000, 2000, 3000, 4001], good_k) == 1         # past total_kv
+    assert vs([0, 4, 2000, 3000, 4000], good_k) == 1            # fewer rows than gamma + 1
+    assert vs([0, 1001, 2000, 3000, 4000], good_k) == 1         # longer than max_seqlen_k
+    assert vs(good_cu, [0, 50, 40, 150, 200]) == 1              # cu_k decreasing
+    assert va([-1, 1000, 2000, 3000, 4000]) == 1
+    assert dr(good_cu, [0, 50, 100, 151, 200]) == 1             # a list longer than max_idx
+    assert dr([0, 1000, 2000, 3000, 3000 - 1], [0, 1, 2, 3, 4]) == 1
+    assert "max_idx" in L.vegas_last_error_message().decode() or True
+    # well-formed host offsets get as far as the workspace check
+    assert L.vegas_sparse_decode_attn_hostplan(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 4000, FAKE, FAKE, 50,
+                                               FAKE, FAKE, dws - 1, None,
+                                               ctypes.byref(V.host_offsets(good_cu, good_k))) == 3
+
+
 def test_probe_library_exports_and_rejects_bad_arguments(V):
     """libvegas_probe.so (measurement helper of the benchmark) exports what its header declares and
     validates its arguments before launching anything."""

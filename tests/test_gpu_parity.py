@@ -606,3 +606,60 @@ def test_out_of_range_device_indices_are_clamped():
     assert np.array_equal(got[:L0], np.arange(L0))          # every prefix position, ascending
     assert np.all(got[L0:L0 + 5] == -9)                       # the extra slots untouched
     assert len(set(got[L0 + 5:].tolist())) == 3 and np.all(np.diff(got[L0 + 5:]) > 0)
+
+
+HOSTPLAN_CASES = FUSED_CASES + [
+    # 17 sequences: above the host plan's batch limit, planned on the device (same results)
+    ("bf16", 17, 8, 2, 128, 2, [100 * (i + 1) for i in range(17)], Fraction(5, 100)),
+    # a sequence whose list is empty next to non-empty ones
+    ("bf16", 3, 8, 2, 128, 2, [5000, 10, 3000], Fraction(5, 100)),
+]
+
+
+@pytest.mark.parametrize("case", HOSTPLAN_CASES,
+                         ids=lambda c: c if isinstance(c, str) else f"{c[0]}-B{c[1]}-{c[2]}x{c[3]}-D{c[4]}-g{c[5]}")
+def test_hostplan_calls_equal_device_planned_calls(case):
+    """The *_hostplan entry points (split plan from host copies of the offsets) give the bits of the
+    entry points that plan on the device: verification with and without collection, the one-call
+    verification + selection, and every drafting call; and they match the oracle."""
+    if isinstance(case, str):
+        wl = W.named_workload(4)
+    else:
+        dtype, B, hq, hkv, d, gamma, prefixes, ratio = case
+        wl = W.custom_workload(dtype, B, hq, hkv, d, gamma, prefixes, ratio=ratio)
+    log(f"case: host plan {wl.name}")
+    inp = W.make_inputs(wl, seed=9, device="cuda")
+    st = LayerStep(inp, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.gamma, wl.seqlens,
+                   wl.k_per_seq, wl.scale, n_drafts=wl.n_drafts)
+    cu, cuk = wl.cu_seqlens(), wl.cu_k()
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return (st.out.clone(), [st.scores[:, cu[b]:cu[b] + wl.prefix_lens[b]].clone() for b in range(wl.batch)],
+                st.indices[: cuk[-1]].clone(), st.draft_out.clone())
+
+    st.run(fused=True)
+    ref = snapshot()
+    st.out.fill_(3.0)
+    st.scores.fill_(float("nan"))
+    st.indices.fill_(-7)
+    st.draft_out.fill_(5.0)
+    st.run(fused=True, host_plan=True)
+    got = snapshot()
+    assert torch.equal(got[0].view(torch.uint8), ref[0].view(torch.uint8))
+    for a, b in zip(got[1], ref[1]):
+        assert torch.equal(a, b)
+    assert torch.equal(got[2], ref[2])
+    assert torch.equal(got[3][: wl.n_drafts].view(torch.uint8), ref[3][: wl.n_drafts].view(torch.uint8))
+    for collect in (False, True):
+        st.verify(collect=collect)
+        torch.cuda.synchronize()
+        a = st.out.clone()
+        st.out.fill_(3.0)
+        st.verify(collect=collect, host_plan=True)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.uint8), st.out.view(torch.uint8)), collect
+    if not isinstance(case, str):        # (the 128K-long ragged sequences have sampled checks of their own)
+        st.run(fused=True, host_plan=True)
+        torch.cuda.synchronize()
+        check_layer(wl, inp, st, seqs=range(min(wl.batch, 3)))

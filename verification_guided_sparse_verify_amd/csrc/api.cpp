@@ -78,6 +78,85 @@ AttnPlan plan_attn(bool bf16, int batch, int hkv, int M, int head_dim, int max_n
     return p;
 }
 
+// Host-side split plan: the same plan the kernels derive on the device
+// (seq_span, seq_plan and batch_plan in attn.hip), evaluated on host copies of
+// the offsets, for batches of at most kHostPlanMax sequences.  The caller
+// guarantees the host arrays hold the device arrays' values; lengths are
+// clamped exactly as on the device.
+void host_plan(const AttnPlan& plan, int batch, int W, int window, int32_t total_kv, const int32_t* cu_host,
+               const int32_t* cu_idx_host, bool gather, vegas::HostPlan* hp) {
+    constexpr int unit = vegas::kAttnWaves * vegas::kAttnBlock;
+    int len[vegas::kHostPlanMax];
+    int64_t total = 0;
+    for (int b = 0; b < batch; ++b) {
+        const int seq0 = std::min(std::max(cu_host[b], 0), total_kv);
+        const int n_b = std::min(std::max(cu_host[b + 1], seq0), total_kv) - seq0;
+        hp->seq0[b] = seq0;
+        hp->n_b[b] = n_b;
+        if (gather) {
+            hp->ib0[b] = cu_idx_host[b];
+            hp->L[b] = 0;
+            hp->lo[b] = 0;
+            hp->len[b] = n_b > 0 ? std::max(cu_idx_host[b + 1] - cu_idx_host[b], 0) : 0;
+        } else {
+            hp->ib0[b] = 0;
+            hp->L[b] = n_b - W;
+            hp->lo[b] = window > 0 ? std::max(0, hp->L[b] - window + 1) : 0;
+            hp->len[b] = std::max(n_b - hp->lo[b], 0);
+        }
+        len[b] = hp->len[b];
+        total += len[b];
+    }
+    int ns[vegas::kHostPlanMax];
+    auto eval = [&](int t) {
+        int units = 0;
+        for (int b = 0; b < batch; ++b) {
+            if (len[b] <= 0) {
+                ns[b] = 0;
+                hp->chunk[b] = unit;
+                continue;
+            }
+            int want = (int)(((int64_t)len[b] * t + total - 1) / total);
+            want = std::max(std::max(want, 1), (len[b] + plan.cap - 1) / plan.cap);
+            int chunk = (len[b] + want - 1) / want;
+            chunk = (chunk + unit - 1) / unit * unit;
+            hp->chunk[b] = chunk;
+            ns[b] = std::min((len[b] + chunk - 1) / chunk, plan.nsplit);
+            units += ns[b];
+        }
+        return units;
+    };
+    if (!(eval(plan.target) <= plan.target || total <= 0)) {
+        int lo = 1, hi = plan.target - 1, best = 1;   // the unit count does not decrease with t
+        while (lo <= hi) {
+            const int mid = (lo + hi) >> 1;
+            if (eval(mid) <= plan.target) {
+                best = mid;
+                lo = mid + 1;
+            } else {
+                hi = mid - 1;
+            }
+        }
+        eval(best);
+    }
+    hp->first[0] = 0;
+    for (int b = 0; b < batch; ++b) hp->first[b + 1] = hp->first[b] + ns[b];
+    hp->n = batch;
+}
+
+// Host offsets: non-decreasing, within [0, total] (total < 0: no bound).
+vegas_status_t check_host_offsets(const int32_t* cu, int batch, int64_t total, const char* name) {
+    if (!cu) return fail(VEGAS_ERR_INVALID_ARGUMENT, "host %s is NULL", name);
+    if (cu[0] < 0) return fail(VEGAS_ERR_INVALID_ARGUMENT, "host %s[0] = %d < 0", name, cu[0]);
+    for (int b = 0; b < batch; ++b)
+        if (cu[b + 1] < cu[b])
+            return fail(VEGAS_ERR_INVALID_ARGUMENT, "host %s decreases at %d (%d -> %d)", name, b, cu[b], cu[b + 1]);
+    if (total >= 0 && cu[batch] > total)
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "host %s[batch] = %d exceeds %lld", name, cu[batch],
+                    (long long)total);
+    return VEGAS_OK;
+}
+
 vegas_status_t check_shape(const vegas_attn_shape_t* s) {
     if (!s) return fail(VEGAS_ERR_INVALID_ARGUMENT, "shape is NULL");
     if (s->dtype != VEGAS_DTYPE_F32 && s->dtype != VEGAS_DTYPE_BF16)
@@ -219,7 +298,7 @@ vegas_status_t verify_impl(const vegas_attn_shape_t* shape, int32_t gamma, const
                            const void* v, const vegas_paged_kv_t* pages, const int32_t* cu_seqlens_k,
                            int32_t max_seqlen_k, int32_t total_kv, uint32_t collect_mask, float* scores,
                            void* out, void* workspace, size_t workspace_bytes, void* stream, int32_t window = 0,
-                           const vegas::SelectArgs* fused = nullptr) {
+                           const vegas::SelectArgs* fused = nullptr, const int32_t* cu_host = nullptr) {
     vegas_status_t st = check_shape(shape);
     if (st != VEGAS_OK) return st;
     if ((st = check_gamma(gamma, shape)) != VEGAS_OK) return st;
@@ -289,6 +368,17 @@ vegas_status_t verify_impl(const vegas_attn_shape_t* shape, int32_t gamma, const
         a.sel_zero = fused->zeroed;
         a.sel_zero_n = vegas::select_zeroed_words(fused->batch);
     }
+    if (cu_host) {
+        if ((st = check_host_offsets(cu_host, shape->batch, total_kv, "cu_seqlens_k")) != VEGAS_OK) return st;
+        for (int b = 0; b < shape->batch; ++b) {
+            const int len = cu_host[b + 1] - cu_host[b];
+            if (len < W || len > max_seqlen_k)
+                return fail(VEGAS_ERR_INVALID_ARGUMENT, "sequence %d has %d rows, outside [gamma+1, max_seqlen_k] = "
+                            "[%d, %d]", b, len, W, max_seqlen_k);
+        }
+        if (shape->batch <= vegas::kHostPlanMax)
+            host_plan(plan, shape->batch, W, window, total_kv, cu_host, nullptr, false, &a.hp);
+    }
     return hip_status(vegas::launch_attn(a, shape->dtype == VEGAS_DTYPE_BF16, shape->head_dim, plan.mb,
                                          false, collect_mask != 0u, static_cast<hipStream_t>(stream), fused),
                       "verify launch");
@@ -328,7 +418,8 @@ vegas::SelectArgs select_args(const SelectPlan& plan, int32_t batch, int32_t num
 vegas_status_t decode_impl(const vegas_attn_shape_t* shape, const void* q, const void* k, const void* v,
                            const vegas_paged_kv_t* pages, const int32_t* cu_seqlens_k, int32_t total_kv,
                            const int32_t* indices, const int32_t* cu_idx, int32_t max_idx, void* out,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+                           void* workspace, size_t workspace_bytes, void* stream,
+                           const vegas_host_offsets_t* host = nullptr) {
     size_t need = 0;
     vegas_status_t st = vegas_sparse_decode_workspace_size(shape, max_idx, &need);
     if (st != VEGAS_OK) return st;
@@ -378,6 +469,17 @@ vegas_status_t decode_impl(const vegas_attn_shape_t* shape, const void* q, const
         a.block_table = pages->block_table;
         a.max_pages = pages->max_pages_per_seq;
         a.num_pages = pages->num_pages;
+    }
+    if (host) {
+        if ((st = check_host_offsets(host->cu_seqlens_k, shape->batch, total_kv, "cu_seqlens_k")) != VEGAS_OK ||
+            (st = check_host_offsets(host->cu_idx, shape->batch, -1, "cu_idx")) != VEGAS_OK)
+            return st;
+        for (int b = 0; b < shape->batch; ++b)
+            if (host->cu_idx[b + 1] - host->cu_idx[b] > max_idx)
+                return fail(VEGAS_ERR_INVALID_ARGUMENT, "list %d holds %d indices, more than max_idx %d", b,
+                            host->cu_idx[b + 1] - host->cu_idx[b], max_idx);
+        if (shape->batch <= vegas::kHostPlanMax)
+            host_plan(plan, shape->batch, 1, 0, total_kv, host->cu_seqlens_k, host->cu_idx, true, &a.hp);
     }
     return hip_status(vegas::launch_attn(a, shape->dtype == VEGAS_DTYPE_BF16, shape->head_dim, plan.mb,
                                          true, false, static_cast<hipStream_t>(stream)),
@@ -523,11 +625,15 @@ vegas_status_t vegas_verify_select_workspace_size(const vegas_attn_shape_t* shap
     return VEGAS_OK;
 }
 
-vegas_status_t vegas_verify_select(const vegas_attn_shape_t* shape, int32_t gamma, const void* q, const void* k,
-                                   const void* v, const int32_t* cu_seqlens_k, int32_t max_seqlen_k,
-                                   int32_t total_kv, uint32_t collect_mask, const int32_t* cu_k, float* scores,
-                                   int32_t* indices, void* out, void* workspace, size_t workspace_bytes,
-                                   void* stream) {
+}  // extern "C"
+
+namespace {
+
+vegas_status_t verify_select_impl(const vegas_attn_shape_t* shape, int32_t gamma, const void* q, const void* k,
+                                  const void* v, const int32_t* cu_seqlens_k, int32_t max_seqlen_k,
+                                  int32_t total_kv, uint32_t collect_mask, const int32_t* cu_k, float* scores,
+                                  int32_t* indices, void* out, void* workspace, size_t workspace_bytes,
+                                  void* stream, const vegas_host_offsets_t* host) {
     size_t need = 0, vb = 0;
     vegas_status_t st = vegas_verify_select_workspace_size(shape, gamma, max_seqlen_k, total_kv, &need);
     if (st != VEGAS_OK) return st;
@@ -538,13 +644,67 @@ vegas_status_t vegas_verify_select(const vegas_attn_shape_t* shape, int32_t gamm
         return fail(VEGAS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
     if (!workspace) return fail(VEGAS_ERR_INVALID_ARGUMENT, "workspace is NULL");
     vegas_verify_workspace_size(shape, gamma, max_seqlen_k, &vb);
-    const vegas::SelectArgs sa =
+    vegas::SelectArgs sa =
         select_args(plan_select(shape->batch, max_seqlen_k, total_kv), shape->batch, shape->num_kv_heads, gamma,
                     scores, cu_seqlens_k, total_kv, cu_k, indices, static_cast<char*>(workspace) + align_up(vb));
+    if (host) {
+        if ((st = check_host_offsets(host->cu_idx, shape->batch, -1, "cu_k")) != VEGAS_OK) return st;
+        if (shape->batch <= vegas::kHostPlanMax && host->cu_seqlens_k) {
+            // each sequence's clamped selection geometry, as seq_geo derives it on the device
+            const int kend = std::max(host->cu_idx[shape->batch], 0);
+            for (int b = 0; b < shape->batch; ++b) {
+                const int seq0 = std::min(std::max(host->cu_seqlens_k[b], 0), total_kv);
+                const int end = std::min(std::max(host->cu_seqlens_k[b + 1], seq0), total_kv);
+                const int L = std::min(std::max(end - seq0 - (gamma + 1), 0), sa.nchunks * vegas::kSelChunk);
+                const int kout = std::min(std::max(host->cu_idx[b], 0), kend);
+                sa.hg_seq0[b] = seq0;
+                sa.hg_L[b] = L;
+                sa.hg_kout[b] = kout;
+                sa.hg_k[b] = std::min(std::min(std::max(host->cu_idx[b + 1] - kout, 0), L), kend - kout);
+            }
+            sa.hg_n = shape->batch;
+        }
+    }
     if ((st = verify_impl(shape, gamma, q, k, v, nullptr, cu_seqlens_k, max_seqlen_k, total_kv, collect_mask,
-                          scores, out, workspace, vb, stream, 0, &sa)) != VEGAS_OK)
+                          scores, out, workspace, vb, stream, 0, &sa, host ? host->cu_seqlens_k : nullptr)) !=
+        VEGAS_OK)
         return st;
     return hip_status(vegas::launch_select_tail(sa, static_cast<hipStream_t>(stream)), "select launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+vegas_status_t vegas_verify_select(const vegas_attn_shape_t* shape, int32_t gamma, const void* q, const void* k,
+                                   const void* v, const int32_t* cu_seqlens_k, int32_t max_seqlen_k,
+                                   int32_t total_kv, uint32_t collect_mask, const int32_t* cu_k, float* scores,
+                                   int32_t* indices, void* out, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+    return verify_select_impl(shape, gamma, q, k, v, cu_seqlens_k, max_seqlen_k, total_kv, collect_mask, cu_k,
+                              scores, indices, out, workspace, workspace_bytes, stream, nullptr);
+}
+
+vegas_status_t vegas_verify_attn_hostplan(const vegas_attn_shape_t* shape, int32_t gamma, const void* q,
+                                          const void* k, const void* v, const int32_t* cu_seqlens_k,
+                                          int32_t max_seqlen_k, int32_t total_kv, uint32_t collect_mask,
+                                          float* scores, void* out, void* workspace, size_t workspace_bytes,
+                                          void* stream, const vegas_host_offsets_t* host) {
+    if (!host || !host->cu_seqlens_k) return fail(VEGAS_ERR_INVALID_ARGUMENT, "host cu_seqlens_k must be non-NULL");
+    return verify_impl(shape, gamma, q, k, v, nullptr, cu_seqlens_k, max_seqlen_k, total_kv, collect_mask, scores,
+                       out, workspace, workspace_bytes, stream, 0, nullptr, host->cu_seqlens_k);
+}
+
+vegas_status_t vegas_verify_select_hostplan(const vegas_attn_shape_t* shape, int32_t gamma, const void* q,
+                                            const void* k, const void* v, const int32_t* cu_seqlens_k,
+                                            int32_t max_seqlen_k, int32_t total_kv, uint32_t collect_mask,
+                                            const int32_t* cu_k, float* scores, int32_t* indices, void* out,
+                                            void* workspace, size_t workspace_bytes, void* stream,
+                                            const vegas_host_offsets_t* host) {
+    if (!host || !host->cu_seqlens_k || !host->cu_idx)
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "host offsets (cu_seqlens_k and cu_idx = cu_k) must be non-NULL");
+    return verify_select_impl(shape, gamma, q, k, v, cu_seqlens_k, max_seqlen_k, total_kv, collect_mask, cu_k,
+                              scores, indices, out, workspace, workspace_bytes, stream, host);
 }
 
 vegas_status_t vegas_sparse_decode_workspace_size(const vegas_attn_shape_t* shape, int32_t max_idx,
@@ -568,6 +728,17 @@ vegas_status_t vegas_sparse_decode_attn(const vegas_attn_shape_t* shape, const v
                                         void* stream) {
     return decode_impl(shape, q, k, v, nullptr, cu_seqlens_k, total_kv, indices, cu_idx, max_idx, out,
                        workspace, workspace_bytes, stream);
+}
+
+vegas_status_t vegas_sparse_decode_attn_hostplan(const vegas_attn_shape_t* shape, const void* q, const void* k,
+                                                 const void* v, const int32_t* cu_seqlens_k, int32_t total_kv,
+                                                 const int32_t* indices, const int32_t* cu_idx, int32_t max_idx,
+                                                 void* out, void* workspace, size_t workspace_bytes, void* stream,
+                                                 const vegas_host_offsets_t* host) {
+    if (!host || !host->cu_seqlens_k || !host->cu_idx)
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "host offsets (cu_seqlens_k and cu_idx) must be non-NULL");
+    return decode_impl(shape, q, k, v, nullptr, cu_seqlens_k, total_kv, indices, cu_idx, max_idx, out,
+                       workspace, workspace_bytes, stream, host);
 }
 
 vegas_status_t vegas_sparse_decode_attn_paged(const vegas_attn_shape_t* shape, const void* q, const void* k,

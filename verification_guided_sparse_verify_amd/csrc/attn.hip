@@ -303,18 +303,18 @@ __device__ __forceinline__ SeqSpan seq_span(const AttnArgs& a, int b) {
 // Split plan of one sequence: a share of `target` splits (per KV head, for the
 // whole batch) proportional to its positions, but no split longer than
 // a.chunk_cap; split length a multiple of kAttnWaves*kAttnBlock.  Ragged
-// batches so get about equal work per workgroup.  Float arithmetic for the
-// share: every workgroup of a pass evaluates it identically.
-__device__ __forceinline__ void seq_plan(const AttnArgs& a, int len, float inv_total, int target, int& ns,
-                                         int& chunk) {
+// batches so get about equal work per workgroup.  Integer arithmetic: every
+// workgroup of a pass, and the host plan, evaluate it identically.
+__device__ __forceinline__ void seq_plan(const AttnArgs& a, int len, int total, int target, int& ns, int& chunk) {
     constexpr int unit = kAttnWaves * kAttnBlock;
     if (len <= 0) {
         ns = 0;
         chunk = unit;
         return;
     }
-    // (an exact multiple of the share must not round up to the next split count)
-    int want = (int)ceilf((float)len * (float)target * inv_total - 1e-3f);
+    // ceil(len * target / total) in exact integer arithmetic (the host plan
+    // evaluates the same expression)
+    int want = (int)(((long long)len * target + total - 1) / total);
     want = max(max(want, 1), (len + a.chunk_cap - 1) / a.chunk_cap);
     chunk = (len + want - 1) / want;
     chunk = (chunk + unit - 1) / unit * unit;
@@ -356,12 +356,11 @@ __device__ __forceinline__ void batch_plan(const AttnArgs& a, int* red, int (&ns
         mine += len[k];
     }
     const int total = wg_sum<NT>(mine, red);
-    const float inv_total = total > 0 ? 1.f / (float)total : 0.f;
     auto plan = [&](int t) {
         int u = 0;
 #pragma unroll
         for (int k = 0; k < kPlanPerThread; ++k) {
-            seq_plan(a, len[k], inv_total, t, ns[k], chunk[k]);
+            seq_plan(a, len[k], total, t, ns[k], chunk[k]);
             u += ns[k];
         }
         return wg_sum<NT>(u, red);
@@ -608,46 +607,65 @@ attn_split_kernel(const AttnArgs a) {
     __shared__ int plan_s[3];
     const int g = blockIdx.x % a.hkv;
     const int unit_id = blockIdx.x / a.hkv;
-    constexpr int kPlanPerThread = plan_per_thread<NT>();
-    int pns[kPlanPerThread], pch[kPlanPerThread];
-    batch_plan<GATHER, NT>(a, plan_red, pns, pch);
-    if (threadIdx.x == 0) plan_s[0] = -1;
-    int before = 0;                                  // units of the sequences of earlier passes
+    int b, split, chunk;
+    SeqSpan sp;
+    if (a.hp.n > 0) {
+        // Host plan: the unit's sequence, split and span are in the arguments.
+        b = -1;
+        for (int t = 0; t < a.hp.n; ++t)
+            if (unit_id >= a.hp.first[t] && unit_id < a.hp.first[t + 1]) b = t;
+        if (b < 0) return;                                        // uniform per workgroup
+        split = unit_id - a.hp.first[b];
+        chunk = a.hp.chunk[b];
+        sp.seq0 = a.hp.seq0[b];
+        sp.n_b = a.hp.n_b[b];
+        sp.L = a.hp.L[b];
+        sp.lo = a.hp.lo[b];
+        sp.len = a.hp.len[b];
+        sp.ib0 = a.hp.ib0[b];
+    } else {
+        constexpr int kPlanPerThread = plan_per_thread<NT>();
+        int pns[kPlanPerThread], pch[kPlanPerThread];
+        batch_plan<GATHER, NT>(a, plan_red, pns, pch);
+        if (threadIdx.x == 0) plan_s[0] = -1;
+        int before = 0;                                  // units of the sequences of earlier passes
 #pragma unroll
-    for (int k = 0; k < kPlanPerThread; ++k) {
-        if (k * NT >= a.batch) break;                // uniform
-        const int bb = k * NT + threadIdx.x;
-        const int ns = pns[k];
-        if (blockIdx.x == 0 && bb < a.batch) a.seq_splits[bb] = ns;
-        int v = ns;                                  // inclusive scan of ns over the threads
-        const int ln = threadIdx.x & 63;
+        for (int k = 0; k < kPlanPerThread; ++k) {
+            if (k * NT >= a.batch) break;                // uniform
+            const int bb = k * NT + threadIdx.x;
+            const int ns = pns[k];
+            if (blockIdx.x == 0 && bb < a.batch) a.seq_splits[bb] = ns;
+            int v = ns;                                  // inclusive scan of ns over the threads
+            const int ln = threadIdx.x & 63;
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(v, off);
-            if (ln >= off) v += y;
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(v, off);
+                if (ln >= off) v += y;
+            }
+            __syncthreads();
+            if (ln == 63) plan_red[threadIdx.x >> 6] = v;
+            __syncthreads();
+            int wbefore = 0, all = 0;
+#pragma unroll
+            for (int w = 0; w < NWV; ++w) {
+                wbefore += (w < (int)(threadIdx.x >> 6)) ? plan_red[w] : 0;
+                all += plan_red[w];
+            }
+            const int first_unit = before + wbefore + v - ns;
+            if (ns > 0 && unit_id >= first_unit && unit_id < first_unit + ns) {
+                plan_s[0] = bb;
+                plan_s[1] = unit_id - first_unit;
+                plan_s[2] = pch[k];
+            }
+            before += all;
         }
         __syncthreads();
-        if (ln == 63) plan_red[threadIdx.x >> 6] = v;
-        __syncthreads();
-        int wbefore = 0, all = 0;
-#pragma unroll
-        for (int w = 0; w < NWV; ++w) {
-            wbefore += (w < (int)(threadIdx.x >> 6)) ? plan_red[w] : 0;
-            all += plan_red[w];
-        }
-        const int first_unit = before + wbefore + v - ns;
-        if (ns > 0 && unit_id >= first_unit && unit_id < first_unit + ns) {
-            plan_s[0] = bb;
-            plan_s[1] = unit_id - first_unit;
-            plan_s[2] = pch[k];
-        }
-        before += all;
+        b = plan_s[0];
+        if (b < 0) return;                                        // uniform per workgroup
+        split = plan_s[1];
+        chunk = plan_s[2];
+        sp = seq_span<GATHER>(a, b);
     }
-    __syncthreads();
-    const int b = plan_s[0];
-    if (b < 0) return;                                            // uniform per workgroup
-    const int split = plan_s[1], chunk = plan_s[2];
-    const SeqSpan sp = seq_span<GATHER>(a, b);
     const int seq0 = sp.seq0, n_b = sp.n_b, L = sp.L, ib0 = sp.ib0;
     // Under a local mask no row sees a key before row 0's band (sp.lo).
     const int count = sp.lo + sp.len;
@@ -907,7 +925,8 @@ __global__ void __launch_bounds__(kCombineWaves * 64) attn_combine_kernel(const 
     const int lg = lane >> 4;
     const int j = 16 * qb + lr;
 
-    const int nsv = min(max(a.seq_splits[b], 0), a.nsplit);    // published by the split kernel
+    // published by the split kernel, or known from the host plan
+    const int nsv = a.hp.n > 0 ? a.hp.first[b + 1] - a.hp.first[b] : min(max(a.seq_splits[b], 0), a.nsplit);
 
     float mr = kNegInf, den = 0.f;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -982,7 +1001,8 @@ __global__ void __launch_bounds__(kCombineWaves * 64) attn_combine_kernel(const 
 
 template <bool BF16, int D, int MB, bool GATHER, bool COLLECT, int RS = 1>
 hipError_t launch_t(const AttnArgs& a, hipStream_t stream, const SelectArgs* sel) {
-    const unsigned split_grid = (unsigned)(a.hkv * a.max_units);
+    // (a host plan knows the exact unit count; the device plan's grid is its bound)
+    const unsigned split_grid = (unsigned)(a.hkv * (a.hp.n > 0 ? a.hp.first[a.hp.n] : a.max_units));
     const unsigned comb_grid = (unsigned)(a.batch * a.hkv * MB * (D / 16));
     if (split_grid > 0)
         hipLaunchKernelGGL((attn_split_kernel<BF16, D, MB, GATHER, COLLECT, RS>), dim3(split_grid),

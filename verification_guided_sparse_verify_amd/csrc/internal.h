@@ -40,6 +40,21 @@ __host__ __device__ constexpr int collect_chunk_cap(bool bf16, int head_dim) {
     return (144 * 1024 - attn_ring_bytes(bf16, head_dim)) / 4 / 64 * 64;
 }
 
+// Split plan computed on the host from host copies of the sequence offsets,
+// passed in the kernel arguments (batches of at most kHostPlanMax sequences):
+// the kernels then start without reading offsets or planning on the device.
+// It is the plan the device computes from the same offsets (same splits, so
+// the same output bits).
+constexpr int kHostPlanMax = 16;
+struct HostPlan {
+    int32_t n;                          // sequences; 0: the kernels plan on the device
+    int32_t first[kHostPlanMax + 1];    // first (sequence, split) unit of each sequence, per KV head
+    int32_t chunk[kHostPlanMax];        // positions per split
+    // the sequence's span, as the device derives it (clamped offsets)
+    int32_t seq0[kHostPlanMax], n_b[kHostPlanMax], L[kHostPlanMax];
+    int32_t lo[kHostPlanMax], len[kHostPlanMax], ib0[kHostPlanMax];
+};
+
 // Arguments of the split attention kernel and of its combine kernel.
 struct AttnArgs {
     const void* q;
@@ -78,6 +93,7 @@ struct AttnArgs {
     // selection's first step on the finished scores.  NULL: not fused.
     uint32_t* sel_zero;
     int32_t sel_zero_n;
+    HostPlan hp;
 };
 
 // Speculative-sampling acceptance: two launches over kAcceptChunk-token chunks.
@@ -117,6 +133,10 @@ struct SelectArgs {
     uint32_t* chunk_ties;          // [batch][nchunks]: keys equal to theta the chunk contributes
     int32_t batch, hkv, W, total_kv;
     int32_t nchunks;               // chunks per sequence
+    // Host copies of each sequence's clamped geometry (hg_n sequences, at most
+    // kHostPlanMax; 0: read from cu_seqlens_k and cu_k on the device).
+    int32_t hg_n;
+    int32_t hg_seq0[kHostPlanMax], hg_L[kHostPlanMax], hg_k[kHostPlanMax], hg_kout[kHostPlanMax];
 };
 
 constexpr int kSelDigitBits = 12;

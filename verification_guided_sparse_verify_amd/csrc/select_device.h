@@ -21,6 +21,13 @@ struct SeqGeo {
 };
 __device__ __forceinline__ SeqGeo seq_geo(const SelectArgs& a, int b) {
     SeqGeo s;
+    if (a.hg_n > 0) {                         // computed on the host from host copies of the offsets
+        s.seq0 = a.hg_seq0[b];
+        s.L = a.hg_L[b];
+        s.k = a.hg_k[b];
+        s.kout = a.hg_kout[b];
+        return s;
+    }
     s.seq0 = min(max(a.cu_seqlens_k[b], 0), a.total_kv);
     const int end = min(max(a.cu_seqlens_k[b + 1], s.seq0), a.total_kv);
     s.L = max(end - s.seq0 - a.W, 0);

@@ -46,6 +46,12 @@ class LayerStep:
         self.max_k = int(max(k_per_seq)) if len(k_per_seq) else 0
         self.total_k = int(sum(k_per_seq))
         self.collect_mask = (1 | (1 << gamma)) if collect_mask is None else collect_mask
+        # host copies of cu_seqlens_k and cu_k, for the host-planned entry points
+        cu, cuk = [0], [0]
+        for n, kk in zip(seqlens, k_per_seq):
+            cu.append(cu[-1] + int(n))
+            cuk.append(cuk[-1] + int(kk))
+        self.host = V.host_offsets(cu, cuk)
         self.n_drafts = gamma if n_drafts is None else n_drafts
         self.out = torch.empty_like(q)
         self.scores = torch.empty(num_kv_heads, self.total_kv, dtype=torch.float32, device=dev)
@@ -62,9 +68,14 @@ class LayerStep:
         """Point at another layer's inputs of the same shapes."""
         self.inp = inputs
 
-    def verify(self, collect: bool = True, stream=None):
+    def verify(self, collect: bool = True, stream=None, host_plan: bool = False):
         i = self.inp
         mask, scores = (self.collect_mask, self.scores) if collect else (0, None)
+        if host_plan and not self.paged:
+            V.vegas_verify_attn_hostplan(self.shape, self.gamma, i["q"], i["k"], i["v"], i["cu_seqlens_k"],
+                                         self.max_seqlen, self.total_kv, mask, scores, self.out, self.workspace,
+                                         self.host, stream)
+            return
         if self.paged:
             V.vegas_verify_attn_paged(self.shape, self.gamma, i["q"], self.paged["k_pool"], self.paged["v_pool"],
                                       self.pages, i["cu_seqlens_k"], self.max_seqlen, self.total_kv, mask, scores,
@@ -78,9 +89,15 @@ class LayerStep:
         """Verification and selection can run as one call (contiguous cache, Vegas selection)."""
         return not self.paged and self.selection == "vegas"
 
-    def verify_select(self, stream=None):
-        """Verification with collection followed by selection, as one library call."""
+    def verify_select(self, stream=None, host_plan: bool = False):
+        """Verification with collection followed by selection, as one library call (host_plan: the
+        call that also takes host copies of the offsets)."""
         i = self.inp
+        if host_plan:
+            V.vegas_verify_select_hostplan(self.shape, self.gamma, i["q"], i["k"], i["v"], i["cu_seqlens_k"],
+                                           self.max_seqlen, self.total_kv, self.collect_mask, i["cu_k"], self.scores,
+                                           self.indices, self.out, self.workspace, self.host, stream)
+            return
         V.vegas_verify_select(self.shape, self.gamma, i["q"], i["k"], i["v"], i["cu_seqlens_k"], self.max_seqlen,
                               self.total_kv, self.collect_mask, i["cu_k"], self.scores, self.indices, self.out,
                               self.workspace, stream)
@@ -94,8 +111,13 @@ class LayerStep:
         V.vegas_select_topk(self.batch, self.hkv, self.gamma, self.scores, i["cu_seqlens_k"], self.max_seqlen,
                             self.total_kv, i["cu_k"], self.indices, self.workspace, stream)
 
-    def draft(self, j: int, stream=None):
+    def draft(self, j: int, stream=None, host_plan: bool = False):
         i = self.inp
+        if host_plan and not self.paged:
+            V.vegas_sparse_decode_attn_hostplan(self.shape, i["draft_q"][j], i["k"], i["v"], i["cu_seqlens_k"],
+                                                self.total_kv, self.indices, i["cu_k"], self.max_k, self.draft_out[j],
+                                                self.workspace, self.host, stream)
+            return
         if self.paged:
             V.vegas_sparse_decode_attn_paged(self.shape, i["draft_q"][j], self.paged["k_pool"], self.paged["v_pool"],
                                              self.pages, i["cu_seqlens_k"], self.total_kv, self.indices, i["cu_k"],
@@ -104,18 +126,19 @@ class LayerStep:
         V.vegas_sparse_decode_attn(self.shape, i["draft_q"][j], i["k"], i["v"], i["cu_seqlens_k"], self.total_kv,
                                    self.indices, i["cu_k"], self.max_k, self.draft_out[j], self.workspace, stream)
 
-    def run(self, stream=None, fused: bool = False):
+    def run(self, stream=None, fused: bool = False, host_plan: bool = False):
         if fused:
-            self.verify_select(stream)
+            self.verify_select(stream, host_plan)
         else:
             self.verify(self.selection == "vegas", stream)
             self.select(stream)
         for j in range(self.n_drafts):
-            self.draft(j, stream)
+            self.draft(j, stream, host_plan)
 
-    def bind(self, stream=None):
+    def bind(self, stream=None, host_plan: bool = False):
         """Return argument-free callables (verify, verify_plain, select, [draft_j]) with every
-        ctypes argument converted once, for launch loops where host time matters."""
+        ctypes argument converted once, for launch loops where host time matters (host_plan:
+        verification and drafting go through the host-planned entry points)."""
         i = self.inp
         st = V._stream(stream)
         shape = ctypes.byref(self.shape)
@@ -143,8 +166,13 @@ class LayerStep:
                       i["cu_seqlens_k"].data_ptr(), self.max_seqlen, self.total_kv)
             dfn, dname = L.vegas_sparse_decode_attn, "vegas_sparse_decode_attn"
             kv = (i["k"].data_ptr(), i["v"].data_ptr())
-        verify = call(vfn, vname, common + (self.collect_mask, self.scores.data_ptr(), self.out.data_ptr(), ws, wsb, st))
-        plain = call(vfn, vname, common + (0, None, self.out.data_ptr(), ws, wsb, st))
+        vtail = ()
+        if host_plan and not self.paged:
+            vfn, vname = L.vegas_verify_attn_hostplan, "vegas_verify_attn_hostplan"
+            vtail = (ctypes.byref(self.host),)
+        verify = call(vfn, vname,
+                      common + (self.collect_mask, self.scores.data_ptr(), self.out.data_ptr(), ws, wsb, st) + vtail)
+        plain = call(vfn, vname, common + (0, None, self.out.data_ptr(), ws, wsb, st) + vtail)
         if self.selection == "streaming":
             select = call(L.vegas_streaming_indices, "vegas_streaming_indices",
                           (self.batch, self.gamma, self.sinks, i["cu_seqlens_k"].data_ptr(), self.total_kv,
@@ -155,15 +183,20 @@ class LayerStep:
                           (self.batch, self.hkv, self.gamma, self.scores.data_ptr(), i["cu_seqlens_k"].data_ptr(),
                            self.max_seqlen, self.total_kv, i["cu_k"].data_ptr(), self.indices.data_ptr(), ws, wsb,
                            st))
+        tail = ()
+        if host_plan and not self.paged:
+            dfn, dname = L.vegas_sparse_decode_attn_hostplan, "vegas_sparse_decode_attn_hostplan"
+            tail = (ctypes.byref(self.host),)
         drafts = [call(dfn, dname,
                        (shape, i["draft_q"][j].data_ptr()) + kv +
                        (i["cu_seqlens_k"].data_ptr(), self.total_kv, self.indices.data_ptr(), i["cu_k"].data_ptr(),
-                        self.max_k, self.draft_out[j].data_ptr(), ws, wsb, st))
+                        self.max_k, self.draft_out[j].data_ptr(), ws, wsb, st) + tail)
                   for j in range(self.n_drafts)]
         return verify, plain, select, drafts
 
-    def bind_fused(self, stream=None):
-        """Argument-free callable of the one-call verification + selection."""
+    def bind_fused(self, stream=None, host_plan: bool = False):
+        """Argument-free callable of the one-call verification + selection (host_plan: the
+        host-planned entry point)."""
         if not self.fusable:
             raise ValueError("the one-call verification + selection needs a contiguous cache and Vegas selection")
         i = self.inp
@@ -171,10 +204,14 @@ class LayerStep:
                 i["cu_seqlens_k"].data_ptr(), self.max_seqlen, self.total_kv, self.collect_mask,
                 i["cu_k"].data_ptr(), self.scores.data_ptr(), self.indices.data_ptr(), self.out.data_ptr(),
                 self.workspace.data_ptr(), self.workspace.numel(), V._stream(stream))
-        fn = V.lib().vegas_verify_select
+        name = "vegas_verify_select"
+        if host_plan:
+            args += (ctypes.byref(self.host),)
+            name = "vegas_verify_select_hostplan"
+        fn = getattr(V.lib(), name)
 
         def go():
             rc = fn(*args)
             if rc:
-                V._check(rc, "vegas_verify_select")
+                V._check(rc, name)
         return go

@@ -32,6 +32,7 @@ EXPORTED = (
     "vegas_verify_paged_workspace_size", "vegas_verify_attn_paged", "vegas_sparse_decode_attn_paged",
     "vegas_verify_local_workspace_size", "vegas_verify_attn_local", "vegas_streaming_indices",
     "vegas_spec_accept_workspace_size", "vegas_spec_accept",
+    "vegas_verify_attn_hostplan", "vegas_verify_select_hostplan", "vegas_sparse_decode_attn_hostplan",
 )
 
 
@@ -54,6 +55,21 @@ class PagedKV(ctypes.Structure):
                 ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
 
 
+class HostOffsets(ctypes.Structure):
+    """vegas_host_offsets_t: host copies of cu_seqlens_k and of cu_k / cu_idx."""
+    _fields_ = [("cu_seqlens_k", ctypes.POINTER(ctypes.c_int32)), ("cu_idx", ctypes.POINTER(ctypes.c_int32))]
+
+
+def host_offsets(cu_seqlens_k, cu_idx) -> HostOffsets:
+    """Host offsets from two integer sequences (lists, numpy arrays or CPU tensors); the
+    returned structure owns copies of both."""
+    a = (ctypes.c_int32 * len(cu_seqlens_k))(*[int(x) for x in cu_seqlens_k])
+    b = (ctypes.c_int32 * len(cu_idx))(*[int(x) for x in cu_idx])
+    h = HostOffsets(ctypes.cast(a, ctypes.POINTER(ctypes.c_int32)), ctypes.cast(b, ctypes.POINTER(ctypes.c_int32)))
+    h._keep = (a, b)
+    return h
+
+
 _lib = None
 
 
@@ -67,6 +83,7 @@ def lib():
         SP = ctypes.POINTER(AttnShape)
         PP = ctypes.POINTER(PagedKV)
         PSZ = ctypes.POINTER(ctypes.c_size_t)
+        HP = ctypes.POINTER(HostOffsets)
         sig = {
             "vegas_abi_version": ([], I32),
             "vegas_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -87,6 +104,10 @@ def lib():
             "vegas_streaming_indices": ([I32, I32, I32, P, I32, P, I32, P, P], ctypes.c_int),
             "vegas_spec_accept_workspace_size": ([I32, I32, PSZ], ctypes.c_int),
             "vegas_spec_accept": ([I32, I32, I32, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
+            "vegas_verify_attn_hostplan": ([SP, I32, P, P, P, P, I32, I32, U32, P, P, P, SZ, P, HP], ctypes.c_int),
+            "vegas_verify_select_hostplan": ([SP, I32, P, P, P, P, I32, I32, U32, P, P, P, P, P, SZ, P, HP],
+                                             ctypes.c_int),
+            "vegas_sparse_decode_attn_hostplan": ([SP, P, P, P, P, I32, P, P, I32, P, P, SZ, P, HP], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -185,6 +206,26 @@ def vegas_verify_select(shape: AttnShape, gamma: int, q, k, v, cu_seqlens_k, max
            "vegas_verify_select")
 
 
+def vegas_verify_attn_hostplan(shape: AttnShape, gamma: int, q, k, v, cu_seqlens_k, max_seqlen_k: int,
+                               total_kv: int, collect_mask: int, scores, out, workspace, host: HostOffsets,
+                               stream=None) -> None:
+    _check(lib().vegas_verify_attn_hostplan(ctypes.byref(shape), gamma, _ptr(q), _ptr(k), _ptr(v),
+                                            _ptr(cu_seqlens_k), max_seqlen_k, total_kv, collect_mask & 0xFFFFFFFF,
+                                            _ptr(scores), _ptr(out), _ptr(workspace), _nbytes(workspace),
+                                            _stream(stream), ctypes.byref(host)),
+           "vegas_verify_attn_hostplan")
+
+
+def vegas_verify_select_hostplan(shape: AttnShape, gamma: int, q, k, v, cu_seqlens_k, max_seqlen_k: int,
+                                 total_kv: int, collect_mask: int, cu_k, scores, indices, out, workspace,
+                                 host: HostOffsets, stream=None) -> None:
+    _check(lib().vegas_verify_select_hostplan(ctypes.byref(shape), gamma, _ptr(q), _ptr(k), _ptr(v),
+                                              _ptr(cu_seqlens_k), max_seqlen_k, total_kv, collect_mask & 0xFFFFFFFF,
+                                              _ptr(cu_k), _ptr(scores), _ptr(indices), _ptr(out), _ptr(workspace),
+                                              _nbytes(workspace), _stream(stream), ctypes.byref(host)),
+           "vegas_verify_select_hostplan")
+
+
 def vegas_sparse_decode_workspace_size(shape: AttnShape, max_idx: int) -> int:
     n = ctypes.c_size_t(0)
     _check(lib().vegas_sparse_decode_workspace_size(ctypes.byref(shape), max_idx, ctypes.byref(n)),
@@ -198,6 +239,15 @@ def vegas_sparse_decode_attn(shape: AttnShape, q, k, v, cu_seqlens_k, total_kv: 
                                           total_kv, _ptr(indices), _ptr(cu_idx), max_idx, _ptr(out),
                                           _ptr(workspace), _nbytes(workspace), _stream(stream)),
            "vegas_sparse_decode_attn")
+
+
+def vegas_sparse_decode_attn_hostplan(shape: AttnShape, q, k, v, cu_seqlens_k, total_kv: int, indices, cu_idx,
+                                      max_idx: int, out, workspace, host: HostOffsets, stream=None) -> None:
+    _check(lib().vegas_sparse_decode_attn_hostplan(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                                   _ptr(cu_seqlens_k), total_kv, _ptr(indices), _ptr(cu_idx),
+                                                   max_idx, _ptr(out), _ptr(workspace), _nbytes(workspace),
+                                                   _stream(stream), ctypes.byref(host)),
+           "vegas_sparse_decode_attn_hostplan")
 
 
 def paged_kv(block_table, page_size: int, num_pages: int) -> PagedKV:
