@@ -180,10 +180,15 @@ vegas_status_t vegas_verify_select(const vegas_attn_shape_t* shape, int32_t gamm
  * sequence's length on the host.  Given host copies, the library computes
  * the split plan on the host and passes it in the kernel arguments, so the
  * kernels start without reading the offsets or planning on the device.  The
- * plan, and so every result bit, is the one the device computes from the
- * same values: the *_hostplan calls give exactly the results of the calls
- * without the suffix.  Batches above 16 sequences are planned on the device
- * as before (same results).
+ * plan is the one the device computes from the same values, so the
+ * *_hostplan calls give exactly the results of the calls without the suffix,
+ * with one exception: when the sequence lengths are unequal enough that the
+ * per-sequence splits leave some workgroups with clearly more than an equal
+ * share, verification splits the batch's positions, laid end to end, into
+ * equal slices instead (the scores, the selection and the drafting outputs
+ * stay bit-identical; the verification output then differs only in the
+ * rounding of the split merge, and is deterministic).  Batches above 16
+ * sequences are planned on the device as before.
  *
  *  cu_seqlens_k   host int32 [batch+1]: the values of the device array.
  *  cu_idx         host int32 [batch+1]: the values of the device cu_k (for

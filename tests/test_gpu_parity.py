@@ -613,15 +613,20 @@ HOSTPLAN_CASES = FUSED_CASES + [
     ("bf16", 17, 8, 2, 128, 2, [100 * (i + 1) for i in range(17)], Fraction(5, 100)),
     # a sequence whose list is empty next to non-empty ones
     ("bf16", 3, 8, 2, 128, 2, [5000, 10, 3000], Fraction(5, 100)),
+    # ragged lengths for which the host balances the verification splits over the batch
+    ("bf16", 12, 64, 8, 64, 3, [1705, 6093, 6444, 35657, 19991, 18445, 12287, 1781, 29032, 4948, 8582, 1443],
+     Fraction(5, 100)),
 ]
 
 
 @pytest.mark.parametrize("case", HOSTPLAN_CASES,
                          ids=lambda c: c if isinstance(c, str) else f"{c[0]}-B{c[1]}-{c[2]}x{c[3]}-D{c[4]}-g{c[5]}")
 def test_hostplan_calls_equal_device_planned_calls(case):
-    """The *_hostplan entry points (split plan from host copies of the offsets) give the bits of the
-    entry points that plan on the device: verification with and without collection, the one-call
-    verification + selection, and every drafting call; and they match the oracle."""
+    """The *_hostplan entry points (split plan from host copies of the offsets) against the entry
+    points that plan on the device: collected scores, selections and drafting outputs bit for bit;
+    verification outputs bit for bit when the lengths are equal, and otherwise (the host may balance
+    a ragged batch's splits, which changes only the merge's rounding) within the output tolerance;
+    and everything matches the oracle."""
     if isinstance(case, str):
         wl = W.named_workload(4)
     else:
@@ -646,7 +651,13 @@ def test_hostplan_calls_equal_device_planned_calls(case):
     st.draft_out.fill_(5.0)
     st.run(fused=True, host_plan=True)
     got = snapshot()
-    assert torch.equal(got[0].view(torch.uint8), ref[0].view(torch.uint8))
+    equal_lengths = len(set(wl.seqlens)) == 1
+
+    def same_out(x, y):
+        if equal_lengths:
+            return torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+        return (x.float() - y.float()).abs().max().item() <= ATOL[wl.dtype]
+    assert same_out(got[0], ref[0])
     for a, b in zip(got[1], ref[1]):
         assert torch.equal(a, b)
     assert torch.equal(got[2], ref[2])
@@ -658,8 +669,12 @@ def test_hostplan_calls_equal_device_planned_calls(case):
         st.out.fill_(3.0)
         st.verify(collect=collect, host_plan=True)
         torch.cuda.synchronize()
-        assert torch.equal(a.view(torch.uint8), st.out.view(torch.uint8)), collect
+        assert same_out(a, st.out), collect
+        b = st.out.clone()
+        st.verify(collect=collect, host_plan=True)     # host-planned calls are deterministic
+        torch.cuda.synchronize()
+        assert torch.equal(b.view(torch.uint8), st.out.view(torch.uint8)), collect
     if not isinstance(case, str):        # (the 128K-long ragged sequences have sampled checks of their own)
         st.run(fused=True, host_plan=True)
         torch.cuda.synchronize()
-        check_layer(wl, inp, st, seqs=range(min(wl.batch, 3)))
+        check_layer(wl, inp, st)

@@ -78,6 +78,59 @@ AttnPlan plan_attn(bool bf16, int batch, int hkv, int M, int head_dim, int max_n
     return p;
 }
 
+// Balanced verification plan for ragged batches.  The per-sequence plan gives
+// every split to one sequence, so a batch of unequal lengths leaves some
+// workgroups with much more than an equal share (1.23x for 16 lengths drawn
+// log-uniform from 4K to 128K).  Here plan.target workgroups per KV head
+// each take an equal slice of the sequences' positions laid end to end, one
+// unit per sequence the slice touches.  It replaces the per-sequence plan
+// when its largest workgroup load, counting kUnitCost positions for each
+// unit's fixed work (query loads, ring fill, merge, stores), is at least 3%
+// smaller.  The merge then groups positions differently, so results differ
+// from the per-sequence plan's in rounding only.
+void balance_plan(const AttnPlan& plan, int batch, const int* len, const int* ns, int64_t total,
+                  vegas::HostPlan* hp) {
+    constexpr int unit = vegas::kAttnWaves * vegas::kAttnBlock;
+    constexpr int64_t kUnitCost = 512;
+    int64_t prop_max = 0;
+    for (int b = 0; b < batch; ++b)
+        for (int i = 0; i < ns[b]; ++i)
+            prop_max = std::max<int64_t>(prop_max, std::min<int64_t>(hp->chunk[b], len[b] - (int64_t)i * hp->chunk[b]));
+    int64_t C = (total + plan.target - 1) / plan.target;
+    C = std::min<int64_t>((C + unit - 1) / unit * unit, plan.cap);
+    const int64_t nwg = (total + C - 1) / C;
+    if (nwg > vegas::kHostWgMax) return;
+    int64_t cum[vegas::kHostPlanMax + 1];
+    cum[0] = 0;
+    for (int b = 0; b < batch; ++b) cum[b + 1] = cum[b] + len[b];
+    int pieces[vegas::kHostPlanMax] = {};
+    int nu = 0;
+    int64_t worst = 0;
+    vegas::HostPlan t = *hp;
+    for (int64_t w = 0; w < nwg; ++w) {
+        const int64_t lo = w * C, hi = std::min(total, lo + C);
+        t.wg_first[w] = nu;
+        int64_t load = 0;
+        for (int b = 0; b < batch; ++b) {
+            const int64_t s = std::max(lo, cum[b]), e = std::min(hi, cum[b + 1]);
+            if (s >= e) continue;
+            if (nu == vegas::kHostUnitsMax || pieces[b] >= plan.nsplit) return;
+            t.u_bs[nu] = b | (pieces[b]++ << 5);
+            t.u_start[nu] = (int)(hp->lo[b] + (s - cum[b]));
+            t.u_end[nu] = (int)(hp->lo[b] + (e - cum[b]));
+            ++nu;
+            load += (e - s) + kUnitCost;
+        }
+        worst = std::max(worst, load);
+    }
+    if (worst * 100 >= (prop_max + kUnitCost) * 97) return;
+    t.wg_first[nwg] = nu;
+    t.nwg = (int)nwg;
+    t.first[0] = 0;
+    for (int b = 0; b < batch; ++b) t.first[b + 1] = t.first[b] + pieces[b];
+    *hp = t;
+}
+
 // Host-side split plan: the same plan the kernels derive on the device
 // (seq_span, seq_plan and batch_plan in attn.hip), evaluated on host copies of
 // the offsets, for batches of at most kHostPlanMax sequences.  The caller
@@ -142,6 +195,8 @@ void host_plan(const AttnPlan& plan, int batch, int W, int window, int32_t total
     hp->first[0] = 0;
     for (int b = 0; b < batch; ++b) hp->first[b + 1] = hp->first[b] + ns[b];
     hp->n = batch;
+    hp->nwg = 0;
+    if (!gather && total > 0) balance_plan(plan, batch, len, ns, total, hp);
 }
 
 // Host offsets: non-decreasing, within [0, total] (total < 0: no bound).

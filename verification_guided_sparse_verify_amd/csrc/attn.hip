@@ -567,111 +567,30 @@ __device__ __forceinline__ void compute_block(const AttnArgs& a, WaveState<BF16,
 // share one ring (one copies the K tile, the other the V tile) and every
 // block iteration ends its waits with a workgroup barrier.  Two waves per SIMD
 // then overlap one wave's MFMA with the other's softmax arithmetic.
+// One unit of the split kernel: positions [start, end) of sequence b (span
+// sp; under a local mask no row sees a key before row 0's band, sp.lo) for KV
+// head g and all query rows of the KV head.  The unit's partial goes to slot
+// `slot` of (b, g).  Called by whole workgroups (every branch on its
+// arguments is uniform); the LDS arrays are the kernel's.
 template <bool BF16, int D, int MB, bool GATHER, bool COLLECT, int RS>
-__global__ void __launch_bounds__(kAttnWaves * RS * 64)
-attn_split_kernel(const AttnArgs a) {
-    static_assert(MB % RS == 0 && (RS == 1 || (RS == 2 && !GATHER)), "row split: verification, even tile count");
+__device__ __forceinline__ void split_unit(const AttnArgs& a, int g, int b, int slot, int start, int end,
+                                           const SeqSpan& sp, unsigned char* smem, int* idx_s, int* page_s,
+                                           float* score_s) {
     constexpr int MBW = MB / RS;                  // row tiles per wave
     constexpr int NT = kAttnWaves * RS * 64;      // threads
-    constexpr int NWV = NT / 64;                  // waves
     using GEO = Geo<BF16, D, MBW>;
     using T = typename std::conditional<BF16, uint16_t, float>::type;
     constexpr int DC = GEO::DC, DB = GEO::DB, NREG = GEO::NREG, NST = GEO::NST;
     constexpr int OPS = GEO::BLOCK_OPS / RS;      // copies one wave issues per block
-    constexpr int MERGE = RS * (kAttnWaves / 2) * GEO::MSLOT;
-    constexpr int MAIN = GEO::RING > MERGE ? GEO::RING : MERGE;
-
-    __shared__ __attribute__((aligned(16))) unsigned char smem[MAIN];
-    __shared__ int idx_s[GATHER ? kMaxGatherChunk : 1];
-    __shared__ int page_s[GATHER ? 1 : kMaxPagesPerSplit];
-    // Collected scores of this split, written to HBM once the split is done.
-    __shared__ float score_s[COLLECT ? collect_chunk_cap(BF16, D) : 1];
-
     const int lane = threadIdx.x & 63;
-    // wave index as a scalar: every branch on it is uniform
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int pw = wave % kAttnWaves;             // position group
     const int rh = wave / kAttnWaves;             // row half (0 unless RS = 2)
     const int lr = lane & 15;
     const int lg = lane >> 4;
-
-    // Fused selection: clear its histograms and counts (read after this launch).
-    if (a.sel_zero)
-        for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.sel_zero_n; i += gridDim.x * blockDim.x)
-            a.sel_zero[i] = 0u;
-
-    // Workgroup -> (KV head g, sequence b, split): the units of all sequences'
-    // split plans, in order; workgroups past the last unit have no work.
-    // Workgroup 0 publishes every sequence's split count for the combine.
-    __shared__ int plan_red[NWV];
-    __shared__ int plan_s[3];
-    const int g = blockIdx.x % a.hkv;
-    const int unit_id = blockIdx.x / a.hkv;
-    int b, split, chunk;
-    SeqSpan sp;
-    if (a.hp.n > 0) {
-        // Host plan: the unit's sequence, split and span are in the arguments.
-        b = -1;
-        for (int t = 0; t < a.hp.n; ++t)
-            if (unit_id >= a.hp.first[t] && unit_id < a.hp.first[t + 1]) b = t;
-        if (b < 0) return;                                        // uniform per workgroup
-        split = unit_id - a.hp.first[b];
-        chunk = a.hp.chunk[b];
-        sp.seq0 = a.hp.seq0[b];
-        sp.n_b = a.hp.n_b[b];
-        sp.L = a.hp.L[b];
-        sp.lo = a.hp.lo[b];
-        sp.len = a.hp.len[b];
-        sp.ib0 = a.hp.ib0[b];
-    } else {
-        constexpr int kPlanPerThread = plan_per_thread<NT>();
-        int pns[kPlanPerThread], pch[kPlanPerThread];
-        batch_plan<GATHER, NT>(a, plan_red, pns, pch);
-        if (threadIdx.x == 0) plan_s[0] = -1;
-        int before = 0;                                  // units of the sequences of earlier passes
-#pragma unroll
-        for (int k = 0; k < kPlanPerThread; ++k) {
-            if (k * NT >= a.batch) break;                // uniform
-            const int bb = k * NT + threadIdx.x;
-            const int ns = pns[k];
-            if (blockIdx.x == 0 && bb < a.batch) a.seq_splits[bb] = ns;
-            int v = ns;                                  // inclusive scan of ns over the threads
-            const int ln = threadIdx.x & 63;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int y = __shfl_up(v, off);
-                if (ln >= off) v += y;
-            }
-            __syncthreads();
-            if (ln == 63) plan_red[threadIdx.x >> 6] = v;
-            __syncthreads();
-            int wbefore = 0, all = 0;
-#pragma unroll
-            for (int w = 0; w < NWV; ++w) {
-                wbefore += (w < (int)(threadIdx.x >> 6)) ? plan_red[w] : 0;
-                all += plan_red[w];
-            }
-            const int first_unit = before + wbefore + v - ns;
-            if (ns > 0 && unit_id >= first_unit && unit_id < first_unit + ns) {
-                plan_s[0] = bb;
-                plan_s[1] = unit_id - first_unit;
-                plan_s[2] = pch[k];
-            }
-            before += all;
-        }
-        __syncthreads();
-        b = plan_s[0];
-        if (b < 0) return;                                        // uniform per workgroup
-        split = plan_s[1];
-        chunk = plan_s[2];
-        sp = seq_span<GATHER>(a, b);
-    }
     const int seq0 = sp.seq0, n_b = sp.n_b, L = sp.L, ib0 = sp.ib0;
-    // Under a local mask no row sees a key before row 0's band (sp.lo).
-    const int count = sp.lo + sp.len;
-    const int start = sp.lo + split * chunk;
-    if (n_b <= 0 || start >= count) return;                       // uniform per workgroup
-    const int end = min(start + chunk, count);
+    if (n_b <= 0 || start >= end) return;                         // uniform per workgroup
+
 
     WaveState<BF16, D, MBW> ws;
     ws.pend_idx = -1;
@@ -859,8 +778,8 @@ attn_split_kernel(const AttnArgs a) {
     }
 
     if (pw == 0) {       // partials in the combine's layout: all MB row tiles of the workgroup
-        const size_t slot = ((size_t)b * a.hkv + g) * a.nsplit + split;
-        f32x4_t* po = reinterpret_cast<f32x4_t*>(a.part_o) + slot * (DB * MB * 64);
+        const size_t slot_i = ((size_t)b * a.hkv + g) * a.nsplit + slot;
+        f32x4_t* po = reinterpret_cast<f32x4_t*>(a.part_o) + slot_i * (DB * MB * 64);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -868,7 +787,7 @@ attn_split_kernel(const AttnArgs a) {
         if (lg == 0) {
 #pragma unroll
             for (int qb = 0; qb < MBW; ++qb) {
-                float2* pml = reinterpret_cast<float2*>(a.part_ml) + slot * (MB * 16) + (rh * MBW + qb) * 16 + lr;
+                float2* pml = reinterpret_cast<float2*>(a.part_ml) + slot_i * (MB * 16) + (rh * MBW + qb) * 16 + lr;
                 *pml = make_float2(ws.m_run[qb], ws.l_run[qb]);
             }
         }
@@ -890,6 +809,119 @@ attn_split_kernel(const AttnArgs a) {
         }
         for (int i = peel + 4 * nv + threadIdx.x; i < nsc; i += blockDim.x) dst[i] = score_s[i];
     }
+}
+
+template <bool BF16, int D, int MB, bool GATHER, bool COLLECT, int RS>
+__global__ void __launch_bounds__(kAttnWaves * RS * 64)
+attn_split_kernel(const AttnArgs a) {
+    static_assert(MB % RS == 0 && (RS == 1 || (RS == 2 && !GATHER)), "row split: verification, even tile count");
+    constexpr int NT = kAttnWaves * RS * 64;      // threads
+    constexpr int NWV = NT / 64;                  // waves
+    using GEO = Geo<BF16, D, MB / RS>;
+    constexpr int MERGE = RS * (kAttnWaves / 2) * GEO::MSLOT;
+    constexpr int MAIN = GEO::RING > MERGE ? GEO::RING : MERGE;
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[MAIN];
+    __shared__ int idx_s[GATHER ? kMaxGatherChunk : 1];
+    __shared__ int page_s[GATHER ? 1 : kMaxPagesPerSplit];
+    // Collected scores of this split, written to HBM once the split is done.
+    __shared__ float score_s[COLLECT ? collect_chunk_cap(BF16, D) : 1];
+
+    // Fused selection: clear its histograms and counts (read after this launch).
+    if (a.sel_zero)
+        for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.sel_zero_n; i += gridDim.x * blockDim.x)
+            a.sel_zero[i] = 0u;
+
+    // Workgroup -> (KV head g, its units).  Without a unit table a workgroup
+    // runs one unit (sequence b, split): the units of all sequences' split
+    // plans, in order; workgroups past the last unit have no work.  With the
+    // device plan, workgroup 0 publishes every sequence's split count for the
+    // combine.
+    __shared__ int plan_red[NWV];
+    __shared__ int plan_s[3];
+    const int g = blockIdx.x % a.hkv;
+    const int unit_id = blockIdx.x / a.hkv;
+    if (a.hp.nwg > 0) {
+        // Host plan with a unit table: this workgroup runs units
+        // wg_first[w] .. wg_first[w+1]-1 (w = unit_id < nwg: the grid).
+        const int k0 = a.hp.wg_first[unit_id], k1 = a.hp.wg_first[unit_id + 1];
+        for (int k = k0; k < k1; ++k) {
+            if (k > k0) __syncthreads();              // the previous unit's LDS reads are done
+            const int ub = a.hp.u_bs[k] & 31, us = a.hp.u_bs[k] >> 5;
+            SeqSpan usp;
+            usp.seq0 = a.hp.seq0[ub];
+            usp.n_b = a.hp.n_b[ub];
+            usp.L = a.hp.L[ub];
+            usp.lo = a.hp.lo[ub];
+            usp.len = a.hp.len[ub];
+            usp.ib0 = a.hp.ib0[ub];
+            split_unit<BF16, D, MB, GATHER, COLLECT, RS>(a, g, ub, us, a.hp.u_start[k], a.hp.u_end[k], usp, smem,
+                                                         idx_s, page_s, score_s);
+        }
+        return;
+    }
+    int b, split, chunk;
+    SeqSpan sp;
+    if (a.hp.n > 0) {
+        // Host plan: the unit's sequence, split and span are in the arguments.
+        b = -1;
+        for (int t = 0; t < a.hp.n; ++t)
+            if (unit_id >= a.hp.first[t] && unit_id < a.hp.first[t + 1]) b = t;
+        if (b < 0) return;                                        // uniform per workgroup
+        split = unit_id - a.hp.first[b];
+        chunk = a.hp.chunk[b];
+        sp.seq0 = a.hp.seq0[b];
+        sp.n_b = a.hp.n_b[b];
+        sp.L = a.hp.L[b];
+        sp.lo = a.hp.lo[b];
+        sp.len = a.hp.len[b];
+        sp.ib0 = a.hp.ib0[b];
+    } else {
+        constexpr int kPlanPerThread = plan_per_thread<NT>();
+        int pns[kPlanPerThread], pch[kPlanPerThread];
+        batch_plan<GATHER, NT>(a, plan_red, pns, pch);
+        if (threadIdx.x == 0) plan_s[0] = -1;
+        int before = 0;                                  // units of the sequences of earlier passes
+#pragma unroll
+        for (int k = 0; k < kPlanPerThread; ++k) {
+            if (k * NT >= a.batch) break;                // uniform
+            const int bb = k * NT + threadIdx.x;
+            const int ns = pns[k];
+            if (blockIdx.x == 0 && bb < a.batch) a.seq_splits[bb] = ns;
+            int v = ns;                                  // inclusive scan of ns over the threads
+            const int ln = threadIdx.x & 63;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(v, off);
+                if (ln >= off) v += y;
+            }
+            __syncthreads();
+            if (ln == 63) plan_red[threadIdx.x >> 6] = v;
+            __syncthreads();
+            int wbefore = 0, all = 0;
+#pragma unroll
+            for (int w = 0; w < NWV; ++w) {
+                wbefore += (w < (int)(threadIdx.x >> 6)) ? plan_red[w] : 0;
+                all += plan_red[w];
+            }
+            const int first_unit = before + wbefore + v - ns;
+            if (ns > 0 && unit_id >= first_unit && unit_id < first_unit + ns) {
+                plan_s[0] = bb;
+                plan_s[1] = unit_id - first_unit;
+                plan_s[2] = pch[k];
+            }
+            before += all;
+        }
+        __syncthreads();
+        b = plan_s[0];
+        if (b < 0) return;                                        // uniform per workgroup
+        split = plan_s[1];
+        chunk = plan_s[2];
+        sp = seq_span<GATHER>(a, b);
+    }
+    const int start = sp.lo + split * chunk;
+    split_unit<BF16, D, MB, GATHER, COLLECT, RS>(a, g, b, split, start, min(start + chunk, sp.lo + sp.len), sp,
+                                                 smem, idx_s, page_s, score_s);
 }
 
 // Merge the split partials of one (sequence, KV head, 16-row tile, 16-wide d
@@ -1001,8 +1033,9 @@ __global__ void __launch_bounds__(kCombineWaves * 64) attn_combine_kernel(const 
 
 template <bool BF16, int D, int MB, bool GATHER, bool COLLECT, int RS = 1>
 hipError_t launch_t(const AttnArgs& a, hipStream_t stream, const SelectArgs* sel) {
-    // (a host plan knows the exact unit count; the device plan's grid is its bound)
-    const unsigned split_grid = (unsigned)(a.hkv * (a.hp.n > 0 ? a.hp.first[a.hp.n] : a.max_units));
+    // (a host plan knows the exact workgroup count; the device plan's grid is its bound)
+    const int per_head = a.hp.nwg > 0 ? a.hp.nwg : (a.hp.n > 0 ? a.hp.first[a.hp.n] : a.max_units);
+    const unsigned split_grid = (unsigned)(a.hkv * per_head);
     const unsigned comb_grid = (unsigned)(a.batch * a.hkv * MB * (D / 16));
     if (split_grid > 0)
         hipLaunchKernelGGL((attn_split_kernel<BF16, D, MB, GATHER, COLLECT, RS>), dim3(split_grid),

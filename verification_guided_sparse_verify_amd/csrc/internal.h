@@ -46,6 +46,9 @@ __host__ __device__ constexpr int collect_chunk_cap(bool bf16, int head_dim) {
 // It is the plan the device computes from the same offsets (same splits, so
 // the same output bits).
 constexpr int kHostPlanMax = 16;
+// Unit table of a balanced host plan (see HostPlan::nwg).
+constexpr int kHostUnitsMax = 96;
+constexpr int kHostWgMax = 64;
 struct HostPlan {
     int32_t n;                          // sequences; 0: the kernels plan on the device
     int32_t first[kHostPlanMax + 1];    // first (sequence, split) unit of each sequence, per KV head
@@ -53,6 +56,15 @@ struct HostPlan {
     // the sequence's span, as the device derives it (clamped offsets)
     int32_t seq0[kHostPlanMax], n_b[kHostPlanMax], L[kHostPlanMax];
     int32_t lo[kHostPlanMax], len[kHostPlanMax], ib0[kHostPlanMax];
+    // Balanced plan (nwg > 0): per KV head, nwg workgroups each take an equal
+    // slice of the sequences' positions laid end to end, one unit per sequence
+    // the slice touches.  Workgroup w runs units wg_first[w] .. wg_first[w+1]-1;
+    // unit u covers positions [u_start[u], u_end[u]) of sequence u_bs[u] & 31
+    // and writes partial slot u_bs[u] >> 5 of that sequence (slots numbered
+    // in position order; first[] then counts each sequence's units).
+    int32_t nwg;
+    int32_t wg_first[kHostWgMax + 1];
+    int32_t u_bs[kHostUnitsMax], u_start[kHostUnitsMax], u_end[kHostUnitsMax];
 };
 
 // Arguments of the split attention kernel and of its combine kernel.
