@@ -126,6 +126,37 @@ def cpu_baseline(wl, layer_inputs, min_seconds=10.0):
     }
 
 
+def tiny_single_thread_oracle(repeats=3):
+    """The oracle on one host thread for the tiny fp32 MQA configuration (1 sequence, 1024 positions,
+    gamma 3): median of `repeats` whole layer-steps (verify + select + 3 drafts) after one warm-up."""
+    import ctypes
+    import numpy as np
+    import oracle
+    from verification_guided_sparse_verify_amd import workloads as W
+
+    gomp = ctypes.CDLL("libgomp.so.1")          # the oracle's OpenMP runtime (gcc -fopenmp)
+    prev = gomp.omp_get_max_threads()
+    gomp.omp_set_num_threads(1)
+    try:
+        wl = W.named_workload(0)
+        inp = W.make_inputs(wl, seed=0, device="cpu")
+        q, k, v, dq = (W.host_bits(inp[n]) for n in ("q", "k", "v", "draft_q"))
+        cus = np.array(wl.cu_seqlens(), np.int32)
+        cuk = np.array(wl.cu_k(), np.int32)
+        times = []
+        for _ in range(repeats + 1):
+            t0 = time.perf_counter()
+            _, sc = oracle.verify_attn(q, k, v, cus, wl.gamma, wl.scale)
+            idx, _, _ = oracle.select_topk(sc, cus, wl.gamma, cuk)
+            for j in range(wl.n_drafts):
+                oracle.sparse_decode_attn(dq[j], k, v, cus, idx, cuk, wl.scale)
+            times.append(time.perf_counter() - t0)
+    finally:
+        gomp.omp_set_num_threads(prev)
+    return {"workload": wl.name, "value": round(statistics.median(times[1:]) * 1e6, 1), "unit": "us/layer-step",
+            "cores": 1, "kind": "oracle", "sample": f"median of {repeats} layer-steps after one warm-up"}
+
+
 def cpu_model() -> str:
     try:
         for ln in open("/proc/cpuinfo"):
@@ -522,6 +553,7 @@ def main():
 
     if cpu_leg:
         result["cpu_baseline"] = cpu_baseline(wl, layer_inputs, args.cpu_seconds)
+        result["cpu_baseline"]["tiny_single_thread"] = tiny_single_thread_oracle()
     print(json.dumps(result), flush=True)
 
 
