@@ -92,6 +92,7 @@ void balance_plan(const AttnPlan& plan, int batch, const int* len, const int* ns
                   vegas::HostPlan* hp) {
     constexpr int unit = vegas::kAttnWaves * vegas::kAttnBlock;
     constexpr int64_t kUnitCost = 512;
+    if (plan.mb > 2) return;   // 3-4 row tiles: row-split workgroups, one unit each
     int64_t prop_max = 0;
     for (int b = 0; b < batch; ++b)
         for (int i = 0; i < ns[b]; ++i)

@@ -841,28 +841,16 @@ attn_split_kernel(const AttnArgs a) {
     __shared__ int plan_s[3];
     const int g = blockIdx.x % a.hkv;
     const int unit_id = blockIdx.x / a.hkv;
-    if (a.hp.nwg > 0) {
-        // Host plan with a unit table: this workgroup runs units
-        // wg_first[w] .. wg_first[w+1]-1 (w = unit_id < nwg: the grid).
-        const int k0 = a.hp.wg_first[unit_id], k1 = a.hp.wg_first[unit_id + 1];
-        for (int k = k0; k < k1; ++k) {
-            if (k > k0) __syncthreads();              // the previous unit's LDS reads are done
-            const int ub = a.hp.u_bs[k] & 31, us = a.hp.u_bs[k] >> 5;
-            SeqSpan usp;
-            usp.seq0 = a.hp.seq0[ub];
-            usp.n_b = a.hp.n_b[ub];
-            usp.L = a.hp.L[ub];
-            usp.lo = a.hp.lo[ub];
-            usp.len = a.hp.len[ub];
-            usp.ib0 = a.hp.ib0[ub];
-            split_unit<BF16, D, MB, GATHER, COLLECT, RS>(a, g, ub, us, a.hp.u_start[k], a.hp.u_end[k], usp, smem,
-                                                         idx_s, page_s, score_s);
-        }
-        return;
-    }
-    int b, split, chunk;
-    SeqSpan sp;
-    if (a.hp.n > 0) {
+    // This workgroup's units: entries k0 .. k0+nunits-1 of the unit table, or
+    // the one unit (b, split) of the per-sequence plan.  One call site of
+    // split_unit, so the kernel holds one copy of it.
+    int k0 = 0, nunits = 1;
+    int b = 0, split = 0, chunk = 0;
+    SeqSpan sp{};
+    if (RS == 1 && a.hp.nwg > 0) {
+        k0 = a.hp.wg_first[unit_id];
+        nunits = a.hp.wg_first[unit_id + 1] - k0;
+    } else if (a.hp.n > 0) {
         // Host plan: the unit's sequence, split and span are in the arguments.
         b = -1;
         for (int t = 0; t < a.hp.n; ++t)
@@ -913,15 +901,40 @@ attn_split_kernel(const AttnArgs a) {
             before += all;
         }
         __syncthreads();
-        b = plan_s[0];
+        b = __builtin_amdgcn_readfirstlane(plan_s[0]);           // uniform: kept in scalar registers
         if (b < 0) return;                                        // uniform per workgroup
-        split = plan_s[1];
-        chunk = plan_s[2];
+        split = __builtin_amdgcn_readfirstlane(plan_s[1]);
+        chunk = __builtin_amdgcn_readfirstlane(plan_s[2]);
         sp = seq_span<GATHER>(a, b);
     }
-    const int start = sp.lo + split * chunk;
-    split_unit<BF16, D, MB, GATHER, COLLECT, RS>(a, g, b, split, start, min(start + chunk, sp.lo + sp.len), sp,
-                                                 smem, idx_s, page_s, score_s);
+    if constexpr (RS > 1) {
+        // Row-split workgroups run one unit (the host never gives them a unit
+        // table): the unit loop would push the two-waves-per-SIMD kernel past
+        // its registers.
+        const int start = sp.lo + split * chunk;
+        split_unit<BF16, D, MB, GATHER, COLLECT, RS>(a, g, b, split, start, min(start + chunk, sp.lo + sp.len), sp,
+                                                     smem, idx_s, page_s, score_s);
+    } else {
+        for (int i = 0; i < nunits; ++i) {
+            int slot = split, start = sp.lo + split * chunk, end = min(start + chunk, sp.lo + sp.len);
+            if (a.hp.nwg > 0) {
+                const int k = k0 + i;
+                b = a.hp.u_bs[k] & 31;
+                slot = a.hp.u_bs[k] >> 5;
+                start = a.hp.u_start[k];
+                end = a.hp.u_end[k];
+                sp.seq0 = a.hp.seq0[b];
+                sp.n_b = a.hp.n_b[b];
+                sp.L = a.hp.L[b];
+                sp.lo = a.hp.lo[b];
+                sp.len = a.hp.len[b];
+                sp.ib0 = a.hp.ib0[b];
+                if (i > 0) __syncthreads();                       // the previous unit's LDS reads are done
+            }
+            split_unit<BF16, D, MB, GATHER, COLLECT, RS>(a, g, b, slot, start, end, sp, smem, idx_s, page_s,
+                                                         score_s);
+        }
+    }
 }
 
 // Merge the split partials of one (sequence, KV head, 16-row tile, 16-wide d
