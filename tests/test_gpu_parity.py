@@ -616,6 +616,8 @@ HOSTPLAN_CASES = FUSED_CASES + [
     # ragged lengths for which the host balances the verification splits over the batch
     ("bf16", 12, 64, 8, 64, 3, [1705, 6093, 6444, 35657, 19991, 18445, 12287, 1781, 29032, 4948, 8582, 1443],
      Fraction(5, 100)),
+    ("f32", 12, 32, 8, 64, 3, [2361, 4845, 2222, 5051, 10012, 14071, 2837, 4297, 2075, 28095, 3332, 37128],
+     Fraction(5, 100)),
 ]
 
 
