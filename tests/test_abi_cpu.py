@@ -100,14 +100,23 @@ def test_verify_argument_errors(V):
         return L.vegas_verify_attn(ctypes.byref(s), 4, p["q"], p["k"], p["v"], p["cu"], p["maxs"], p["total"],
                                    p["mask"], p["scores"], p["out"], p["ws"], p["wsb"], None)
 
+    def msg():
+        return L.vegas_last_error_message().decode()
+
     assert call(q=None) == 1
+    assert "must be non-NULL" in msg()
     assert call(out=FAKE + 4) == 1                       # misaligned
+    assert "16-byte aligned" in msg()
     assert call(mask=1 << 5) == 1                        # row 5 does not exist for gamma 4
+    assert "rows >= gamma+1 = 5" in msg()
     assert call(scores=None) == 1                        # collection on, no buffer
+    assert "scores is NULL" in msg()
     assert call(wsb=ws - 1) == 3
+    assert msg() == f"workspace needs {ws} bytes, got {ws - 1}"
     assert call(maxs=3) == 1
+    assert "max_seqlen_k 3 < gamma+1" in msg()
     assert call(total=4) == 1
-    assert "workspace" in L.vegas_last_error_message().decode() or True
+    assert "total_kv 4 < batch*(gamma+1)" in msg()
 
 
 def test_select_and_decode_argument_errors(V):
@@ -256,8 +265,9 @@ def test_hostplan_offsets_are_checked_before_launch(V):
     assert vs(good_cu, [0, 50, 40, 150, 200]) == 1              # cu_k decreasing
     assert va([-1, 1000, 2000, 3000, 4000]) == 1
     assert dr(good_cu, [0, 50, 100, 151, 200]) == 1             # a list longer than max_idx
+    assert L.vegas_last_error_message().decode() == "list 2 holds 51 indices, more than max_idx 50"
     assert dr([0, 1000, 2000, 3000, 3000 - 1], [0, 1, 2, 3, 4]) == 1
-    assert "max_idx" in L.vegas_last_error_message().decode() or True
+    assert L.vegas_last_error_message().decode() == "host cu_seqlens_k decreases at 3 (3000 -> 2999)"
     # well-formed host offsets get as far as the workspace check
     assert L.vegas_sparse_decode_attn_hostplan(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 4000, FAKE, FAKE, 50,
                                                FAKE, FAKE, dws - 1, None,

@@ -162,6 +162,14 @@ def _hh_positions(wl: Workload, L: int, gen: torch.Generator) -> torch.Tensor:
     return (starts[:, None] + torch.arange(wl.hh_run)[None, :]).reshape(-1)
 
 
+def heavy_hitter_positions(wl: Workload, seed: int = 0, layer: int = 0) -> List[torch.Tensor]:
+    """The planted heavy-hitter positions of every sequence, as make_inputs draws them for the
+    same seed and layer (the only draws of its host-side generator)."""
+    cpu_gen = torch.Generator(device="cpu")
+    cpu_gen.manual_seed(seed * 1000003 + layer + 7919)
+    return [_hh_positions(wl, L, cpu_gen) for L in wl.prefix_lens]
+
+
 def _unit(n_rows: int, d: int, gen: torch.Generator, device) -> torch.Tensor:
     u = torch.randn(n_rows, d, generator=gen, device=device, dtype=torch.float32)
     return u / u.norm(dim=-1, keepdim=True)
@@ -180,8 +188,7 @@ def make_inputs(wl: Workload, seed: int = 0, device="cpu", layer: int = 0, out: 
     dev = torch.device(device)
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed * 1000003 + layer)
-    cpu_gen = torch.Generator(device="cpu")
-    cpu_gen.manual_seed(seed * 1000003 + layer + 7919)
+    hh_all = heavy_hitter_positions(wl, seed, layer)
     B, Hq, Hkv, D, W = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.gamma + 1
     G = Hq // Hkv
     cu = wl.cu_seqlens()
@@ -199,7 +206,7 @@ def make_inputs(wl: Workload, seed: int = 0, device="cpu", layer: int = 0, out: 
         L = wl.prefix_lens[b]
         kf = torch.randn(s1 - s0, Hkv, D, generator=gen, device=dev, dtype=torch.float32)
         gain = torch.zeros(s1 - s0, dtype=torch.float32)
-        hh = _hh_positions(wl, L, cpu_gen)
+        hh = hh_all[b]
         if hh.numel():
             gain.index_add_(0, hh, torch.full((hh.numel(),), wl.hh_gain))
         if wl.sink_count:
