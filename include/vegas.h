@@ -215,6 +215,21 @@ vegas_status_t vegas_verify_attn_hostplan(const vegas_attn_shape_t* shape, int32
                                           int32_t total_kv, uint32_t collect_mask, float* scores,
                                           void* out, void* workspace, size_t workspace_bytes,
                                           void* stream, const vegas_host_offsets_t* host);
+/*
+ * Which split plan a host-planned verification call takes for these offsets
+ * (the plan is a design choice of this library, not a step of the method):
+ * *balanced = 1 when the batch's positions are cut into equal slices (the
+ * case above whose verification output differs from the device-planned
+ * call's in the merge's rounding), 0 for the per-sequence plan or a batch
+ * planned on the device; *workgroups = workgroups per KV head of the
+ * verification launch.  Host arguments only; validated as by
+ * vegas_verify_attn_hostplan (VEGAS_ERR_INVALID_ARGUMENT on bad offsets).
+ * Nothing is launched.
+ */
+vegas_status_t vegas_verify_hostplan_info(const vegas_attn_shape_t* shape, int32_t gamma,
+                                          int32_t max_seqlen_k, int32_t total_kv,
+                                          const vegas_host_offsets_t* host, int32_t* balanced,
+                                          int32_t* workgroups);
 /* vegas_verify_select with host offsets; workspace as for vegas_verify_select. */
 vegas_status_t vegas_verify_select_hostplan(const vegas_attn_shape_t* shape, int32_t gamma,
                                             const void* q, const void* k, const void* v,

@@ -9,6 +9,8 @@ and compare it with the CPU oracle on the same bits, by the rules:
 """
 from __future__ import annotations
 
+import json
+import os
 import sys
 
 import numpy as np
@@ -21,6 +23,35 @@ from verification_guided_sparse_verify_amd.step import LayerStep
 ATOL = {"bf16": 2e-2, "f32": 1e-4}
 SCORE_RTOL = 1e-3
 THETA_TOL = 1e-3
+
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+MARGINS = os.path.join(ROOT, "gpurun_out", "parity_margins.json")
+
+
+def record_margins(case: str, wl: W.Workload, worst: dict, seqs):
+    """Keep a case's worst errors next to its tolerances in gpurun_out/parity_margins.json (one
+    entry per case, merged with the entries of earlier cases), so the distance to each bound is
+    on record, not only the pass."""
+    atol = ATOL[wl.dtype]
+    entry = {"workload": wl.name, "sequences_checked": list(seqs), "of": wl.batch,
+             "out_max_abs_err": worst["out"], "out_tol": atol,
+             "score_max_rel_err": worst["score"], "score_tol": SCORE_RTOL,
+             "draft_max_abs_err": worst["draft"], "draft_tol": atol,
+             "selection_diffs_outside_tie_band": 0,
+             "selection_diffs_inside_tie_band": worst.get("sel_diff", 0)}
+    os.makedirs(os.path.dirname(MARGINS), exist_ok=True)
+    data = {}
+    if os.path.exists(MARGINS):
+        try:
+            with open(MARGINS) as f:
+                data = json.load(f)
+        except (OSError, ValueError):
+            data = {}
+    data[case] = entry
+    with open(MARGINS, "w") as f:
+        json.dump(data, f, indent=1)
+    log(f"  margins {case}: {json.dumps(entry)}")
 
 
 def log(msg: str):
@@ -58,7 +89,7 @@ def check_layer(wl: W.Workload, inp, st: LayerStep, seqs=None, check_drafts: boo
     out_all = st.out.float()
     sc_all = st.scores
     idx_all = st.indices
-    worst = {"out": 0.0, "score": 0.0, "draft": 0.0}
+    worst = {"out": 0.0, "score": 0.0, "draft": 0.0, "sel_diff": 0}
     for b in seqs:
         L = wl.prefix_lens[b]
         kb = wl.k_per_seq[b]
@@ -81,6 +112,7 @@ def check_layer(wl: W.Workload, inp, st: LayerStep, seqs=None, check_drafts: boo
             assert np.all(np.diff(t_gpu) > 0), f"seq {b}: indices not strictly ascending"
             assert t_gpu[0] >= 0 and t_gpu[-1] < L, f"seq {b}: index outside the prefix"
         diff = set(t_gpu.tolist()) ^ set(t_ref.tolist())
+        worst["sel_diff"] += len(diff)
         bad = [i for i in diff if abs(S[i] - theta[0]) > THETA_TOL]
         assert not bad, f"seq {b}: selection differs beyond the threshold band at {bad[:10]}"
         # drafting over the GPU's own list

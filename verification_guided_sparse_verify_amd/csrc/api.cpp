@@ -751,6 +751,37 @@ vegas_status_t vegas_verify_attn_hostplan(const vegas_attn_shape_t* shape, int32
                        out, workspace, workspace_bytes, stream, 0, nullptr, host->cu_seqlens_k);
 }
 
+vegas_status_t vegas_verify_hostplan_info(const vegas_attn_shape_t* shape, int32_t gamma, int32_t max_seqlen_k,
+                                          int32_t total_kv, const vegas_host_offsets_t* host, int32_t* balanced,
+                                          int32_t* workgroups) {
+    vegas_status_t st = check_shape(shape);
+    if (st != VEGAS_OK) return st;
+    if ((st = check_gamma(gamma, shape)) != VEGAS_OK) return st;
+    if (!balanced || !workgroups) return fail(VEGAS_ERR_INVALID_ARGUMENT, "balanced and workgroups must be non-NULL");
+    if (!host || !host->cu_seqlens_k) return fail(VEGAS_ERR_INVALID_ARGUMENT, "host cu_seqlens_k must be non-NULL");
+    const int W = gamma + 1;
+    if (max_seqlen_k < W) return fail(VEGAS_ERR_INVALID_ARGUMENT, "max_seqlen_k %d < gamma+1 = %d", max_seqlen_k, W);
+    if ((st = check_host_offsets(host->cu_seqlens_k, shape->batch, total_kv, "cu_seqlens_k")) != VEGAS_OK) return st;
+    for (int b = 0; b < shape->batch; ++b) {
+        const int len = host->cu_seqlens_k[b + 1] - host->cu_seqlens_k[b];
+        if (len < W || len > max_seqlen_k)
+            return fail(VEGAS_ERR_INVALID_ARGUMENT, "sequence %d has %d rows, outside [gamma+1, max_seqlen_k] = [%d, %d]",
+                        b, len, W, max_seqlen_k);
+    }
+    const int G = shape->num_q_heads / shape->num_kv_heads;
+    const AttnPlan plan = plan_attn(shape->dtype == VEGAS_DTYPE_BF16, shape->batch, shape->num_kv_heads, W * G,
+                                    shape->head_dim, max_seqlen_k, false);
+    *balanced = 0;
+    *workgroups = plan.max_units;
+    if (shape->batch <= vegas::kHostPlanMax) {
+        vegas::HostPlan hp{};
+        host_plan(plan, shape->batch, W, 0, total_kv, host->cu_seqlens_k, nullptr, false, &hp);
+        *balanced = hp.nwg > 0 ? 1 : 0;
+        *workgroups = hp.nwg > 0 ? hp.nwg : hp.first[hp.n];
+    }
+    return VEGAS_OK;
+}
+
 vegas_status_t vegas_verify_select_hostplan(const vegas_attn_shape_t* shape, int32_t gamma, const void* q,
                                             const void* k, const void* v, const int32_t* cu_seqlens_k,
                                             int32_t max_seqlen_k, int32_t total_kv, uint32_t collect_mask,

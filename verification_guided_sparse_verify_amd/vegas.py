@@ -33,6 +33,7 @@ EXPORTED = (
     "vegas_verify_local_workspace_size", "vegas_verify_attn_local", "vegas_streaming_indices",
     "vegas_spec_accept_workspace_size", "vegas_spec_accept",
     "vegas_verify_attn_hostplan", "vegas_verify_select_hostplan", "vegas_sparse_decode_attn_hostplan",
+    "vegas_verify_hostplan_info",
 )
 
 
@@ -108,6 +109,8 @@ def lib():
             "vegas_verify_select_hostplan": ([SP, I32, P, P, P, P, I32, I32, U32, P, P, P, P, P, SZ, P, HP],
                                              ctypes.c_int),
             "vegas_sparse_decode_attn_hostplan": ([SP, P, P, P, P, I32, P, P, I32, P, P, SZ, P, HP], ctypes.c_int),
+            "vegas_verify_hostplan_info": ([SP, I32, I32, I32, HP, ctypes.POINTER(I32), ctypes.POINTER(I32)],
+                                           ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -214,6 +217,16 @@ def vegas_verify_attn_hostplan(shape: AttnShape, gamma: int, q, k, v, cu_seqlens
                                             _ptr(scores), _ptr(out), _ptr(workspace), _nbytes(workspace),
                                             _stream(stream), ctypes.byref(host)),
            "vegas_verify_attn_hostplan")
+
+
+def vegas_verify_hostplan_info(shape: AttnShape, gamma: int, max_seqlen_k: int, total_kv: int,
+                               host: HostOffsets) -> tuple[bool, int]:
+    """(balanced, workgroups per KV head) of the split plan a host-planned verification takes."""
+    bal, wgs = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib().vegas_verify_hostplan_info(ctypes.byref(shape), gamma, max_seqlen_k, total_kv, ctypes.byref(host),
+                                            ctypes.byref(bal), ctypes.byref(wgs)),
+           "vegas_verify_hostplan_info")
+    return bool(bal.value), int(wgs.value)
 
 
 def vegas_verify_select_hostplan(shape: AttnShape, gamma: int, q, k, v, cu_seqlens_k, max_seqlen_k: int,
