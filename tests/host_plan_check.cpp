@@ -202,8 +202,10 @@ void check_attn(const Case& c, bool gather, size_t ws_bytes, const char* entry, 
     const char* w0 = reinterpret_cast<const char*>(a.part_o);
     const char* wml = reinterpret_cast<const char*>(a.part_ml);
     const char* wsp = reinterpret_cast<const char*>(a.seq_splits);
-    REQUIRE((size_t)(wml - w0) >= slots * mb * 16 * c.D * 4, "part_o region short");
-    REQUIRE((size_t)(wsp - wml) >= slots * mb * 16 * 2 * 4, "part_ml region short");
+    // a single row tile keeps its M valid rows, wider tiles all 16 rows of each tile
+    const size_t rows = mb == 1 ? (size_t)M : (size_t)mb * 16;
+    REQUIRE((size_t)(wml - w0) >= slots * rows * c.D * 4, "part_o region short");
+    REQUIRE((size_t)(wsp - wml) >= slots * rows * 2 * 4, "part_ml region short");
     REQUIRE((size_t)(wsp - w0) + (size_t)B * 4 <= ws_bytes, "split counts past the workspace");
 
     std::vector<int> len, lo;
@@ -228,6 +230,20 @@ void check_attn(const Case& c, bool gather, size_t ws_bytes, const char* entry, 
     REQUIRE(dp.units <= a.max_units, "device plan: %lld units > max_units %d", dp.units, a.max_units);
 
     const vegas::HostPlan& hp = a.hp;
+    // the collected-score LDS buffer (sized at launch) holds the longest unit
+    if (!gather) {
+        if (hp.n == 0) REQUIRE(a.score_cap == cap, "device plan: score buffer %d, cap %d", a.score_cap, cap);
+        REQUIRE(a.score_cap <= cap, "score buffer %d above cap %d", a.score_cap, cap);
+        if (hp.n > 0 && hp.nwg == 0)
+            for (int b = 0; b < B; ++b)
+                if (hp.first[b + 1] > hp.first[b])
+                    REQUIRE(std::min(hp.chunk[b], hp.len[b]) <= a.score_cap, "seq %d split %d > score buffer %d", b,
+                            std::min(hp.chunk[b], hp.len[b]), a.score_cap);
+        if (hp.nwg > 0)
+            for (int u = 0; u < hp.wg_first[hp.nwg]; ++u)
+                REQUIRE(hp.u_end[u] - hp.u_start[u] <= a.score_cap, "unit %d longer than the score buffer %d", u,
+                        a.score_cap);
+    }
     if (hp.n == 0) return;
     REQUIRE(hp.n == B && B <= vegas::kHostPlanMax, "host plan over %d sequences", hp.n);
     if (hp.nwg == 0) {

@@ -327,6 +327,10 @@ SELECT_CASES = [
     (2, 3, [32769, 5], [3000, 5], 2),
     (4, 1, [20000, 7], [1000, 7], 0),
     (3, 2, [4000, 31, 1], [3999, 1, 1], 1),
+    # 128 and 129 chunks of 2048 positions; all-tied scores over more than 8192 positions
+    (2, 3, [262140, 1000], [13107, 50], 2),
+    (2, 3, [262141, 77], [13000, 3], 1),
+    (1, 0, [9000, 30000], [4500, 29000], 0),
 ]
 
 

@@ -71,9 +71,11 @@ AttnPlan plan_attn(bool bf16, int batch, int hkv, int M, int head_dim, int max_n
     p.target = std::max(1, kRoundWorkgroups / hkv);
     p.nsplit = (int)std::max<int64_t>(p.target + 1, (n + cap - 1) / cap);
     p.max_units = (int)std::max<int64_t>(p.target, (batch * n + cap - 1) / cap) + 2 * batch;
+    // a single 16-row tile keeps only its M valid rows in a partial (part_rows in attn.hip)
+    const size_t rows = p.mb == 1 ? (size_t)M : (size_t)p.mb * 16;
     const size_t slots = (size_t)batch * hkv * p.nsplit;
-    p.part_o = slots * p.mb * 16 * head_dim * sizeof(float);
-    p.part_ml = slots * p.mb * 16 * 2 * sizeof(float);
+    p.part_o = slots * rows * head_dim * sizeof(float);
+    p.part_ml = slots * rows * 2 * sizeof(float);
     p.splits = (size_t)batch * sizeof(int32_t);
     return p;
 }
@@ -198,6 +200,18 @@ void host_plan(const AttnPlan& plan, int batch, int W, int window, int32_t total
     hp->n = batch;
     hp->nwg = 0;
     if (!gather && total > 0) balance_plan(plan, batch, len, ns, total, hp);
+}
+
+// Longest unit (split or balanced slice) of a host plan, in positions.
+int longest_unit(const vegas::HostPlan& hp) {
+    int m = 0;
+    if (hp.nwg > 0) {
+        for (int u = 0; u < hp.wg_first[hp.nwg]; ++u) m = std::max(m, hp.u_end[u] - hp.u_start[u]);
+    } else {
+        for (int b = 0; b < hp.n; ++b)
+            if (hp.first[b + 1] > hp.first[b]) m = std::max(m, std::min(hp.chunk[b], hp.len[b]));
+    }
+    return m;
 }
 
 // Host offsets: non-decreasing, within [0, total] (total < 0: no bound).
@@ -435,6 +449,8 @@ vegas_status_t verify_impl(const vegas_attn_shape_t* shape, int32_t gamma, const
         if (shape->batch <= vegas::kHostPlanMax)
             host_plan(plan, shape->batch, W, window, total_kv, cu_host, nullptr, false, &a.hp);
     }
+    a.score_cap = plan.cap;
+    if (a.hp.n > 0) a.score_cap = longest_unit(a.hp);
     return hip_status(vegas::launch_attn(a, shape->dtype == VEGAS_DTYPE_BF16, shape->head_dim, plan.mb,
                                          false, collect_mask != 0u, static_cast<hipStream_t>(stream), fused),
                       "verify launch");

@@ -380,6 +380,16 @@ __device__ __forceinline__ void batch_plan(const AttnArgs& a, int* red, int (&ns
     plan(best);
 }
 
+// Rows of a 16-row tile a split partial keeps in the workspace: a single tile
+// keeps only its M valid rows (e.g. the G rows of a drafting pass: a quarter
+// of the bytes at G = 4), wider tiles all 16.  Partial slot layout, in float4
+// units: ((d tile * MB + row tile) * 4 + lane / 16) * rows + lane % 16, for
+// lane % 16 < rows; the (m, l) pairs: row tile * rows + lane % 16.
+template <int MB>
+__device__ __forceinline__ int part_rows(const AttnArgs& a) {
+    return MB == 1 ? a.M : 16;
+}
+
 // Headroom of the lazily moved softmax reference (log2 units): block
 // probabilities are at most 2^8, far inside bf16/fp32 range.
 constexpr float kRescaleSlack = 8.f;
@@ -777,17 +787,19 @@ __device__ __forceinline__ void split_unit(const AttnArgs& a, int g, int b, int 
         __syncthreads();
     }
 
-    if (pw == 0) {       // partials in the combine's layout: all MB row tiles of the workgroup
+    const int prow = part_rows<MB>(a);
+    if (pw == 0 && lr < prow) {   // partials in the combine's layout: all MB row tiles of the workgroup
         const size_t slot_i = ((size_t)b * a.hkv + g) * a.nsplit + slot;
-        f32x4_t* po = reinterpret_cast<f32x4_t*>(a.part_o) + slot_i * (DB * MB * 64);
+        f32x4_t* po = reinterpret_cast<f32x4_t*>(a.part_o) + slot_i * (DB * MB * 4 * prow);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int qb = 0; qb < MBW; ++qb) po[(db * MB + rh * MBW + qb) * 64 + lane] = ws.o[db][qb];
+            for (int qb = 0; qb < MBW; ++qb) po[((db * MB + rh * MBW + qb) * 4 + lg) * prow + lr] = ws.o[db][qb];
         if (lg == 0) {
 #pragma unroll
             for (int qb = 0; qb < MBW; ++qb) {
-                float2* pml = reinterpret_cast<float2*>(a.part_ml) + slot_i * (MB * 16) + (rh * MBW + qb) * 16 + lr;
+                float2* pml =
+                    reinterpret_cast<float2*>(a.part_ml) + slot_i * (MB * prow) + (rh * MBW + qb) * prow + lr;
                 *pml = make_float2(ws.m_run[qb], ws.l_run[qb]);
             }
         }
@@ -823,9 +835,14 @@ attn_split_kernel(const AttnArgs a) {
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[MAIN];
     __shared__ int idx_s[GATHER ? kMaxGatherChunk : 1];
-    __shared__ int page_s[GATHER ? 1 : kMaxPagesPerSplit];
-    // Collected scores of this split, written to HBM once the split is done.
-    __shared__ float score_s[COLLECT ? collect_chunk_cap(BF16, D) : 1];
+    // LDS sized at launch: the collected scores of the longest unit of the
+    // plan (a.score_cap floats; collection only), written to HBM once a unit
+    // is done, then a paged verification's page list.  Sized to what the
+    // call needs, a verification workgroup leaves room on its CU for the
+    // workgroups of a selection running beside it.
+    extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
+    float* score_s = reinterpret_cast<float*>(dyn_lds);
+    int* page_s = reinterpret_cast<int*>(dyn_lds + (COLLECT ? attn_score_lds_bytes(a.score_cap) : 0));
 
     // Fused selection: clear its histograms and counts (read after this launch).
     if (a.sel_zero)
@@ -978,14 +995,17 @@ __global__ void __launch_bounds__(kCombineWaves * 64) attn_combine_kernel(const 
     const size_t slot0 = ((size_t)b * a.hkv + g) * a.nsplit;
     const float2* pml = reinterpret_cast<const float2*>(a.part_ml);
     const f32x4_t* po = reinterpret_cast<const f32x4_t*>(a.part_o);
+    const int prow = part_rows<MB>(a);      // lanes of rows past it hold no partial (and no output)
+    const bool kept = lr < prow;
     for (int s0 = wave; s0 < nsv; s0 += U * kCombineWaves) {
         float2 ml[U];
         f32x4_t ov[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int s = min(s0 + u * kCombineWaves, nsv - 1);
-            ml[u] = pml[(slot0 + s) * (MB * 16) + j];
-            ov[u] = po[(slot0 + s) * (NREG * 64) + (db * MB + qb) * 64 + lane];
+            ml[u] = kept ? pml[(slot0 + s) * (MB * prow) + qb * prow + lr] : make_float2(kNegInf, 0.f);
+            ov[u] = kept ? po[(slot0 + s) * (NREG * 4 * prow) + ((db * MB + qb) * 4 + lg) * prow + lr]
+                         : f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -1050,9 +1070,11 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream, const SelectArgs* sel
     const int per_head = a.hp.nwg > 0 ? a.hp.nwg : (a.hp.n > 0 ? a.hp.first[a.hp.n] : a.max_units);
     const unsigned split_grid = (unsigned)(a.hkv * per_head);
     const unsigned comb_grid = (unsigned)(a.batch * a.hkv * MB * (D / 16));
+    const size_t dyn = (COLLECT ? attn_score_lds_bytes(a.score_cap) : 0) +
+                       (!GATHER && a.page_shift >= 0 ? kMaxPagesPerSplit * sizeof(int) : 0);
     if (split_grid > 0)
         hipLaunchKernelGGL((attn_split_kernel<BF16, D, MB, GATHER, COLLECT, RS>), dim3(split_grid),
-                           dim3(kAttnWaves * RS * 64), 0, stream, a);
+                           dim3(kAttnWaves * RS * 64), dyn, stream, a);
     if (comb_grid > 0) {
         if constexpr (COLLECT && !GATHER) {
             if (sel) {

@@ -39,6 +39,11 @@ __host__ __device__ constexpr int attn_ring_bytes(bool bf16, int head_dim) {
 __host__ __device__ constexpr int collect_chunk_cap(bool bf16, int head_dim) {
     return (144 * 1024 - attn_ring_bytes(bf16, head_dim)) / 4 / 64 * 64;
 }
+// LDS bytes of a split workgroup's collected-score buffer for units of at most
+// `positions` positions (the buffer is sized at launch).
+__host__ __device__ constexpr int attn_score_lds_bytes(int positions) {
+    return (positions * 4 + 15) / 16 * 16;
+}
 
 // Split plan computed on the host from host copies of the sequence offsets,
 // passed in the kernel arguments (batches of at most kHostPlanMax sequences):
@@ -90,6 +95,7 @@ struct AttnArgs {
     int32_t nsplit;
     int32_t max_units;
     int32_t* seq_splits;           // workspace [batch]: splits of each sequence (split kernel -> combine)
+    int32_t score_cap;             // longest unit of the plan (<= chunk_cap): the collected-score LDS buffer
     float scale;                   // softmax scale s
     float scale_log2;              // s * log2(e)
     uint32_t collect_mask;

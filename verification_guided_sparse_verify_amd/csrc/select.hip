@@ -179,8 +179,11 @@ __global__ void __launch_bounds__(kSelThreads) sel_cand_kernel(const SelectArgs 
 
 __global__ void __launch_bounds__(kSelThreads) sel_write_kernel(const SelectArgs a) {
     __shared__ uint32_t bins[1024];
-    __shared__ uint32_t gt[kSelMaxChunks];
-    __shared__ uint32_t ties[kSelMaxChunks];
+    // Per-chunk counts of candidates above and equal to theta (a.nchunks each,
+    // sized at launch: small enough to share a CU with a verification workgroup).
+    extern __shared__ uint32_t sel_dyn[];
+    uint32_t* gt = sel_dyn;
+    uint32_t* ties = sel_dyn + a.nchunks;
     __shared__ int wsum[kSelThreads / 64];
     __shared__ uint64_t wsum64[kSelThreads / 64];
     __shared__ uint32_t cross[2];
@@ -361,7 +364,7 @@ hipError_t launch_select_tail(const SelectArgs& a, hipStream_t stream) {
     if (a.nchunks > 0) {
         const dim3 grid(a.nchunks, a.batch);
         hipLaunchKernelGGL(sel_cand_kernel, grid, dim3(kSelThreads), 0, stream, a);
-        hipLaunchKernelGGL(sel_write_kernel, grid, dim3(kSelThreads), 0, stream, a);
+        hipLaunchKernelGGL(sel_write_kernel, grid, dim3(kSelThreads), 2 * a.nchunks * sizeof(uint32_t), stream, a);
     }
     return hipGetLastError();
 }
