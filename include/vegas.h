@@ -275,7 +275,28 @@ vegas_status_t vegas_sparse_decode_attn_hostplan(const vegas_attn_shape_t* shape
                                                  const vegas_host_offsets_t* host);
 
 /*
- * Paged KV cache (NEXT to the contiguous layout above).
+ * vegas_sparse_decode_attn without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops and
+ * harnesses that forbid allocation).  Same kernels and results as
+ * vegas_sparse_decode_attn (host != NULL: as vegas_sparse_decode_attn_hostplan
+ * with those host offsets); allocates nothing.
+ * Scratch: a static device array of vegas_noalloc_scratch_bytes() bytes (16 MiB)
+ * inside the library, one copy per GPU, held until the process ends.  A call
+ * whose vegas_sparse_decode_workspace_size exceeds it returns
+ * VEGAS_ERR_UNSUPPORTED and launches nothing.  All calls on one GPU share the
+ * array: calls that may overlap on one GPU (different streams, or threads)
+ * race and must be ordered by the caller.
+ */
+vegas_status_t vegas_sparse_decode_attn_noalloc(const vegas_attn_shape_t* shape, const void* q,
+                                                const void* k, const void* v,
+                                                const int32_t* cu_seqlens_k, int32_t total_kv,
+                                                const int32_t* indices, const int32_t* cu_idx,
+                                                int32_t max_idx, void* out, void* stream,
+                                                const vegas_host_offsets_t* host);
+size_t vegas_noalloc_scratch_bytes(void);
+
+/*
+ * Paged KV cache, beside the contiguous layout above.
  * The pages hook vLLM's attention, whose KV cache is paged, and run drafting
  * as paged attention with a page size of one token ("Vegas ...", sec. 4
  * "Serving framework integration"; its Appendix D reports the same latency

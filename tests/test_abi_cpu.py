@@ -291,3 +291,22 @@ def test_probe_library_exports_and_rejects_bad_arguments(V):
     assert fn(FAKE, unit + 16, 256, FAKE, None) == -1       # not a whole number of slices
     assert fn(FAKE, unit, 0, FAKE, None) == -1              # no workgroups
     assert fn(FAKE, unit, 256, None, None) == -1            # no sink
+
+
+def test_noalloc_drafting_rejects_calls_beyond_its_scratch(V):
+    """The allocation-free drafting entry point checks the call's scratch need against its static
+    scratch before touching the device: too large a call returns VEGAS_ERR_UNSUPPORTED with both
+    sizes in the message."""
+    L = V.lib()
+    assert V.vegas_noalloc_scratch_bytes() == 16 << 20
+    s = shape(V, dtype=V.VEGAS_DTYPE_F32, batch=1024, num_q_heads=256, num_kv_heads=16)
+    need = V.vegas_sparse_decode_workspace_size(s, 100000)
+    assert need > V.vegas_noalloc_scratch_bytes()
+    assert L.vegas_sparse_decode_attn_noalloc(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 10 ** 6, FAKE, FAKE, 100000,
+                                              FAKE, None, None) == 2
+    assert L.vegas_last_error_message().decode() == (
+        f"this call needs {need} bytes of scratch, more than the {16 << 20} of the static scratch "
+        "(vegas_sparse_decode_attn takes a workspace of any size)")
+    # invalid shapes are rejected as by the workspace entry point
+    assert L.vegas_sparse_decode_attn_noalloc(ctypes.byref(shape(V, head_dim=96)), FAKE, FAKE, FAKE, FAKE, 100, FAKE,
+                                              FAKE, 10, FAKE, None, None) == 2

@@ -13,7 +13,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libvegas.so")
 PROBE_LIB = os.path.join(PKG, "libvegas_probe.so")
 
-SOURCES = ["attn.hip", "select.hip", "accept.hip", "api.cpp"]
+SOURCES = ["attn.hip", "select.hip", "accept.hip", "api.cpp", "noalloc.cpp"]
 PROBE_SOURCES = ["probe.hip"]      # measurement helper, its own library
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

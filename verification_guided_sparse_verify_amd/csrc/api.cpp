@@ -25,6 +25,17 @@ vegas_status_t fail(vegas_status_t st, const char* fmt, ...) {
     return st;
 }
 
+}  // namespace
+
+namespace vegas {
+int set_last_error(int status, const char* message) {
+    g_last_error = message;
+    return status;
+}
+}  // namespace vegas
+
+namespace {
+
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -8,6 +8,10 @@
 
 namespace vegas {
 
+// Record `message` as the calling thread's last error detail (what
+// vegas_last_error_message returns); returns `status`.
+int set_last_error(int status, const char* message);
+
 // Waves per attention workgroup and positions per wave iteration.
 constexpr int kAttnWaves = 4;
 constexpr int kAttnBlock = 16;

@@ -33,7 +33,7 @@ EXPORTED = (
     "vegas_verify_local_workspace_size", "vegas_verify_attn_local", "vegas_streaming_indices",
     "vegas_spec_accept_workspace_size", "vegas_spec_accept",
     "vegas_verify_attn_hostplan", "vegas_verify_select_hostplan", "vegas_sparse_decode_attn_hostplan",
-    "vegas_verify_hostplan_info",
+    "vegas_verify_hostplan_info", "vegas_sparse_decode_attn_noalloc", "vegas_noalloc_scratch_bytes",
 )
 
 
@@ -111,6 +111,8 @@ def lib():
             "vegas_sparse_decode_attn_hostplan": ([SP, P, P, P, P, I32, P, P, I32, P, P, SZ, P, HP], ctypes.c_int),
             "vegas_verify_hostplan_info": ([SP, I32, I32, I32, HP, ctypes.POINTER(I32), ctypes.POINTER(I32)],
                                            ctypes.c_int),
+            "vegas_sparse_decode_attn_noalloc": ([SP, P, P, P, P, I32, P, P, I32, P, P, HP], ctypes.c_int),
+            "vegas_noalloc_scratch_bytes": ([], SZ),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -217,6 +219,19 @@ def vegas_verify_attn_hostplan(shape: AttnShape, gamma: int, q, k, v, cu_seqlens
                                             _ptr(scores), _ptr(out), _ptr(workspace), _nbytes(workspace),
                                             _stream(stream), ctypes.byref(host)),
            "vegas_verify_attn_hostplan")
+
+
+def vegas_sparse_decode_attn_noalloc(shape: AttnShape, q, k, v, cu_seqlens_k, total_kv: int, indices, cu_idx,
+                                     max_idx: int, out, stream=None, host: HostOffsets | None = None) -> None:
+    """vegas_sparse_decode_attn on the library's static scratch (no workspace argument)."""
+    _check(lib().vegas_sparse_decode_attn_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k),
+                                                  total_kv, _ptr(indices), _ptr(cu_idx), max_idx, _ptr(out),
+                                                  _stream(stream), ctypes.byref(host) if host is not None else None),
+           "vegas_sparse_decode_attn_noalloc")
+
+
+def vegas_noalloc_scratch_bytes() -> int:
+    return int(lib().vegas_noalloc_scratch_bytes())
 
 
 def vegas_verify_hostplan_info(shape: AttnShape, gamma: int, max_seqlen_k: int, total_kv: int,
