@@ -52,15 +52,26 @@ def algorithmic_bytes(wl):
 
 
 def kernel_source_hash():
-    """Hash of the attention kernels' source with comments and blank lines removed (a change
-    of comments alone leaves the kernels, and so the counters, as they were)."""
+    """Hash of the attention kernels' source with comments, blank lines and the measurement-only
+    VEGAS_PHASE_TRACE blocks removed (a change of comments or of the trace build alone leaves the
+    product kernels, and so the counters, as they were)."""
     h = hashlib.sha256()
     for f in ("attn.hip", "internal.h", "select_device.h"):
         with open(os.path.join(ROOT, "verification_guided_sparse_verify_amd", "csrc", f)) as fh:
             text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        state = ""                     # "trace": inside the trace branch; "else": in its #else branch
         for ln in text.splitlines():
             code = re.sub(r"//.*", "", ln).strip()
-            if code:
+            if code == "#ifdef VEGAS_PHASE_TRACE":
+                state = "trace"
+                continue
+            if state and code == "#else":
+                state = "else"
+                continue
+            if state and code == "#endif":
+                state = ""
+                continue
+            if code and state != "trace":
                 h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
@@ -206,6 +217,58 @@ def stream_read_ceiling(nbytes: int = 4 << 30, reps: int = 5):
             "kernel": "vegas_probe_stream_read (16-byte non-temporal direct-to-LDS copies, 8 KB in flight per wave)"}
 
 
+def gather_read_ceiling(wl, layer_inputs, steps, reps=3):
+    """Best HBM rate of a plain gather kernel (libvegas_probe.so) reading exactly the bytes of the
+    drafting passes: the K and V slices of every KV head of the selected rows of every layer (rows
+    cold, layer after layer, as in the timed steps), over a few workgroup counts and depths of
+    blocks in flight.  A measured practical peak for the drafting call, next to the published one."""
+    import ctypes
+    import torch
+    from verification_guided_sparse_verify_amd import build as B
+    if not os.path.exists(B.PROBE_LIB):
+        return None
+    probe = ctypes.CDLL(B.PROBE_LIB)
+    fn = probe.vegas_probe_gather_read
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                   ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    es = 2 if wl.dtype == "bf16" else 4
+    slice_bytes = wl.head_dim * es
+    row_bytes = wl.num_kv_heads * slice_bytes
+    cu, cuk = wl.cu_seqlens(), wl.cu_k()
+    offs = torch.repeat_interleave(torch.tensor(cu[:-1], dtype=torch.int32),
+                                   torch.tensor(wl.k_per_seq)).to("cuda")
+    lists = [(inp["k"], inp["v"], (st.indices[: cuk[-1]] + offs).contiguous()) for inp, st in zip(layer_inputs, steps)]
+    nbytes = sum(int(r.numel()) for _, _, r in lists) * row_bytes * 2
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    best = (0.0, 0, 0)
+    for wgs in (256, 512, 1024):
+        for inflight in (1, 2, 3):
+            times = []
+            for r in range(reps + 1):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for k, v, rows in lists:
+                    rc = fn(k.data_ptr(), v.data_ptr(), rows.data_ptr(), rows.numel(), wl.total_kv, row_bytes,
+                            slice_bytes, wl.num_kv_heads, wgs, inflight, sink.data_ptr(), stream.cuda_stream)
+                    if rc != 0:
+                        raise RuntimeError(f"vegas_probe_gather_read returned {rc}")
+                b.record(stream)
+                times.append((a, b))
+            torch.cuda.synchronize()
+            us = min(x.elapsed_time(y) for x, y in times[1:]) * 1e3
+            gbps = nbytes / (us * 1e-6) / 1e9
+            if gbps > best[0]:
+                best = (gbps, wgs, inflight)
+    return {"gbps": round(best[0], 1), "workgroups": best[1], "blocks_in_flight_per_wave": best[2],
+            "bytes": nbytes, "layers": len(lists),
+            "kernel": ("vegas_probe_gather_read (the drafting pass's K/V slices of the selected rows of every "
+                       "layer, 16-byte non-temporal direct-to-LDS copies, no arithmetic)")}
+
+
 def collect_sweep(base, gammas=(1, 3, 5, 7, 11, 15), reps=8):
     """Verification time of one layer of `base` (its prefix, heads and batch) with collection
     off, Collect-2-Query (rows 0 and gamma) and all gamma+1 rows, for several gamma.  The pages
@@ -254,6 +317,91 @@ def collect_sweep(base, gammas=(1, 3, 5, 7, 11, 15), reps=8):
         torch.cuda.empty_cache()
     print(json.dumps({"collect_sweep": base.name, "unit": "us per verification call (split + combine)",
                       "rows": rows}), flush=True)
+
+
+def phase_trace(layers=8, reps=3):
+    """Per-workgroup phase timestamps of the 128K verification call (one-call form's split kernel,
+    host-planned, with collection) from the measurement build libvegas_trace.so: start, end of the
+    block loop and end of every split workgroup, the CU it ran on (XCD, shader engine, CU ids) and its
+    (sequence, split, KV head); `layers` layers, `reps` calls each after a warm-up, with KV head g on
+    the workgroups w = g (mod Hkv) (which the dispatcher deals to XCD g) and again with the KV heads
+    rotated over the XCDs.  Prints one JSON line of summaries."""
+    import ctypes
+    import numpy as np
+    import torch
+    from verification_guided_sparse_verify_amd import build as B
+    from verification_guided_sparse_verify_amd import vegas as V
+    from verification_guided_sparse_verify_amd import workloads as W
+    from verification_guided_sparse_verify_amd.step import LayerStep
+
+    V._lib = None
+    V.LIB_PATH = B.TRACE_LIB
+    L = V.lib()
+    L.vegas_trace_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    L.vegas_trace_set_rotation.argtypes = [ctypes.c_int]
+    wl = W.named_workload(2)
+    steps = []
+    for layer in range(layers):
+        inp = W.make_inputs(wl, seed=0, device="cuda", layer=layer)
+        steps.append(LayerStep(inp, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.gamma, wl.seqlens,
+                               wl.k_per_seq, wl.scale, n_drafts=wl.n_drafts))
+    torch.cuda.synchronize()
+    out = {"phase_trace": wl.name, "layers": layers, "calls_per_layer": reps,
+           "call": "vegas_verify_attn_hostplan with collection (split kernel; libvegas_trace.so)",
+           "clock": "wall_clock64, 100 MHz", "mappings": {}}
+    buf = np.zeros(4096 * 8, np.uint64)
+    for rotate in (0, 1):
+        assert L.vegas_trace_set_rotation(rotate) == 0
+        recs = []
+        for rep in range(reps + 1):
+            for st in steps:
+                st.verify(collect=True, host_plan=True)
+                torch.cuda.synchronize()
+                assert L.vegas_trace_read(buf.ctypes.data, buf.nbytes) == 0
+                if rep > 0:
+                    recs.append(buf.reshape(4096, 8)[:256].astype(np.int64).copy())
+        loop, end, start, keys = [], [], [], []
+        call_end = []
+        for r in recs:
+            t0 = r[:, 0].min()
+            loop.append((r[:, 1] - r[:, 0]) / 100.0)
+            end.append((r[:, 2] - t0) / 100.0)
+            start.append((r[:, 0] - t0) / 100.0)
+            call_end.append(float(((r[:, 2] - t0) / 100.0).max()))
+            keys.append(r)
+        loop, end, start = np.concatenate(loop), np.concatenate(end), np.concatenate(start)
+        allr = np.concatenate(keys)
+        xcc = allr[:, 4] & 15
+        cu = ((allr[:, 3] >> 8) & 15) + 16 * ((allr[:, 3] >> 12) & 1) + 32 * ((allr[:, 3] >> 13) & 7) + 256 * xcc
+        wgs = np.tile(np.arange(256), len(recs))
+
+        def means(key):
+            return {int(k): round(float(loop[key == k].mean()), 1) for k in np.unique(key)}
+
+        def split_half(ids):
+            a, b = [], []
+            for k in np.unique(ids):
+                v = loop[ids == k]
+                if len(v) >= 4:
+                    a.append(v[0::2].mean())
+                    b.append(v[1::2].mean())
+            return round(float(np.corrcoef(a, b)[0, 1]), 3)
+
+        pct = lambda x: [round(float(v), 1) for v in np.percentile(x, [0, 10, 50, 90, 100])]
+        out["mappings"]["kv_heads_rotated_over_xcds" if rotate else "kv_head_g_on_xcd_g"] = {
+            "block_loop_us_p0_p10_p50_p90_max": pct(loop),
+            "workgroup_end_us_p0_p10_p50_p90_max": pct(end),
+            "last_workgroup_end_us_mean_over_calls": round(float(np.mean(call_end)), 1),
+            "last_start_us_max": round(float(start.max()), 2),
+            "block_loop_mean_us_by_kv_head": means(allr[:, 7]),
+            "block_loop_mean_us_by_xcd": means(xcc),
+            "block_loop_mean_us_by_split": means(allr[:, 6]),
+            "block_loop_mean_us_by_sequence": means(allr[:, 5]),
+            "split_half_correlation_per_workgroup": split_half(wgs),
+            "split_half_correlation_per_cu": split_half(cu),
+        }
+    L.vegas_trace_set_rotation(0)
+    print(json.dumps(out), flush=True)
 
 
 def accept_bench(reps=50):
@@ -330,6 +478,9 @@ def main():
     ap.add_argument("--device-plan", action="store_true",
                     help="time the entry points that plan splits on the device (default: the *_hostplan entry "
                          "points, which take host copies of the offsets; same results)")
+    ap.add_argument("--phase-trace", action="store_true",
+                    help="only record per-workgroup phase timestamps of the 128K verification call with the "
+                         "measurement build libvegas_trace.so and print their summary")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a device copy of BYTES bytes three times (counter calibration)")
     args = ap.parse_args()
@@ -344,6 +495,9 @@ def main():
         return
     if args.accept_bench:
         accept_bench()
+        return
+    if args.phase_trace:
+        phase_trace(layers=args.layers or 8)
         return
 
     import torch
@@ -550,6 +704,12 @@ def main():
         if ceiling:
             result["roofline"]["frac_of_stream_ceiling"] = round(verify_gbps / ceiling["gbps"], 4)
             result["layer_step_frac_of_stream_ceiling"] = round(step_gbps / ceiling["gbps"], 4)
+        if not args.page_size:
+            gceil = gather_read_ceiling(wl, layer_inputs, steps)
+            result["gather_read_ceiling"] = gceil
+            if gceil:
+                result["per_call_gbps"]["draft"]["frac_of_gather_ceiling"] = round(
+                    result["per_call_gbps"]["draft"]["gbps"] / gceil["gbps"], 4)
 
     if cpu_leg:
         result["cpu_baseline"] = cpu_baseline(wl, layer_inputs, args.cpu_seconds)

@@ -280,9 +280,9 @@ def test_probe_library_exports_and_rejects_bad_arguments(V):
     from verification_guided_sparse_verify_amd import build as B
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "vegas_probe.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(vegas_[a-z_0-9]+)\s*\(", text)))
-    assert names == ["vegas_probe_stream_read"]
+    assert names == ["vegas_probe_gather_read", "vegas_probe_stream_read"]
     nm = subprocess.run(["nm", "-D", "--defined-only", B.PROBE_LIB], capture_output=True, text=True).stdout
-    assert "vegas_probe_stream_read" in nm
+    assert "vegas_probe_stream_read" in nm and "vegas_probe_gather_read" in nm
     fn = ctypes.CDLL(B.PROBE_LIB).vegas_probe_stream_read
     fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     unit = 32768 * 256
@@ -310,3 +310,39 @@ def test_noalloc_drafting_rejects_calls_beyond_its_scratch(V):
     # invalid shapes are rejected as by the workspace entry point
     assert L.vegas_sparse_decode_attn_noalloc(ctypes.byref(shape(V, head_dim=96)), FAKE, FAKE, FAKE, FAKE, 100, FAKE,
                                               FAKE, 10, FAKE, None, None) == 2
+
+
+def test_gather_probe_rejects_bad_arguments(V):
+    """The gather-ceiling probe validates its arguments before launching anything."""
+    from verification_guided_sparse_verify_amd import build as B
+    fn = ctypes.CDLL(B.PROBE_LIB).vegas_probe_gather_read
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int32] * 7 + [ctypes.c_void_p] * 2
+
+    def call(**kw):
+        p = dict(k=FAKE, v=FAKE, rows=FAKE, n=100, total=1000, row=2048, slice=256, heads=8, wgs=256, inflight=2,
+                 sink=FAKE)
+        p.update(kw)
+        return fn(p["k"], p["v"], p["rows"], p["n"], p["total"], p["row"], p["slice"], p["heads"], p["wgs"],
+                  p["inflight"], p["sink"], None)
+
+    assert call(k=None) == -1
+    assert call(v=FAKE + 8) == -1              # misaligned
+    assert call(n=0) == -1
+    assert call(slice=512) == -1               # only 128- or 256-byte slices
+    assert call(row=1024) == -1                # eight 256-byte slices do not fit a 1 KB row
+    assert call(wgs=260) == -1                 # not a multiple of the head count
+    assert call(inflight=4) == -1
+    assert call(n=300000, wgs=8) == -1         # more than 4096 entries per workgroup
+    assert call(sink=None) == -1
+
+
+def test_trace_build_is_separate_from_the_product_library(V):
+    """The phase-timestamp measurement build exports its reader; the product library has no trace
+    code (the instrumentation exists only under VEGAS_PHASE_TRACE)."""
+    from verification_guided_sparse_verify_amd import build as B
+    nm = lambda p: subprocess.run(["nm", "-D", "--defined-only", p], capture_output=True, text=True).stdout
+    trace, product = nm(B.TRACE_LIB), nm(V.LIB_PATH)
+    assert "vegas_trace_read" in trace and "vegas_trace_set_rotation" in trace
+    assert "vegas_trace" not in product
+    for name in V.EXPORTED:              # and the same C ABI otherwise
+        assert name in trace

@@ -12,6 +12,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libvegas.so")
 PROBE_LIB = os.path.join(PKG, "libvegas_probe.so")
+# Measurement build of the same sources with per-workgroup phase timestamps in
+# the split kernel (VEGAS_PHASE_TRACE); loaded only by bench.py --phase-trace.
+TRACE_LIB = os.path.join(PKG, "libvegas_trace.so")
 
 SOURCES = ["attn.hip", "select.hip", "accept.hip", "api.cpp", "noalloc.cpp"]
 PROBE_SOURCES = ["probe.hip"]      # measurement helper, its own library
@@ -26,21 +29,23 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    """Build libvegas.so and libvegas_probe.so; returns the path of libvegas.so."""
+    """Build libvegas.so, libvegas_probe.so and libvegas_trace.so; returns the path of libvegas.so."""
     _build_lib(SOURCES, LIB, verbose)
     _build_lib(PROBE_SOURCES, PROBE_LIB, verbose)
+    _build_lib(SOURCES, TRACE_LIB, verbose, extra=["-DVEGAS_PHASE_TRACE"], subdir="trace")
     return LIB
 
 
-def _build_lib(sources, lib, verbose: bool) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def _build_lib(sources, lib, verbose: bool, extra=(), subdir: str = "") -> str:
+    bdir = os.path.join(BUILD, subdir)
+    os.makedirs(bdir, exist_ok=True)
     procs = []
     objs = []
     for src in sources:
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))

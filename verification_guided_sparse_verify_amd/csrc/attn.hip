@@ -39,6 +39,21 @@
 #include "select_device.h"
 
 namespace vegas {
+
+#ifdef VEGAS_PHASE_TRACE
+// Measurement build only (libvegas_trace.so, never the product library):
+// each split workgroup records its start, the end of its last unit's block
+// loop and its end (the 100 MHz constant clock), the hardware ids of the CU
+// it ran on and its (sequence, split, KV head); vegas_trace_read copies the
+// records out.  g_trace_rotate != 0 maps workgroup w to KV head
+// (w + w / Hkv) % Hkv instead of w % Hkv, so a KV head's workgroups land on
+// every XCD (the dispatcher deals workgroups to the XCDs in turn).
+constexpr int kTraceMax = 4096;
+__device__ unsigned long long g_trace[kTraceMax][8];
+__device__ unsigned long long g_trace_loop[kTraceMax];
+__device__ int g_trace_rotate;
+#endif
+
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -732,6 +747,9 @@ __device__ __forceinline__ void split_unit(const AttnArgs& a, int g, int b, int 
         }
     }
     wait_vmem<0>();
+#ifdef VEGAS_PHASE_TRACE
+    if (threadIdx.x == 0 && blockIdx.x < kTraceMax) g_trace_loop[blockIdx.x] = wall_clock64();
+#endif
 
     // Row sums: each lane summed its own positions.
 #pragma unroll
@@ -837,13 +855,15 @@ attn_split_kernel(const AttnArgs a) {
     __shared__ int idx_s[GATHER ? kMaxGatherChunk : 1];
     // LDS sized at launch: the collected scores of the longest unit of the
     // plan (a.score_cap floats; collection only), written to HBM once a unit
-    // is done, then a paged verification's page list.  Sized to what the
-    // call needs, a verification workgroup leaves room on its CU for the
-    // workgroups of a selection running beside it.
+    // is done, then a paged verification's page list (a host-planned 128K
+    // verification takes 64 KB for its scores where a fixed buffer held 80).
     extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
     float* score_s = reinterpret_cast<float*>(dyn_lds);
     int* page_s = reinterpret_cast<int*>(dyn_lds + (COLLECT ? attn_score_lds_bytes(a.score_cap) : 0));
 
+#ifdef VEGAS_PHASE_TRACE
+    const unsigned long long trace_t0 = wall_clock64();
+#endif
     // Fused selection: clear its histograms and counts (read after this launch).
     if (a.sel_zero)
         for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.sel_zero_n; i += gridDim.x * blockDim.x)
@@ -856,7 +876,11 @@ attn_split_kernel(const AttnArgs a) {
     // combine.
     __shared__ int plan_red[NWV];
     __shared__ int plan_s[3];
+#ifdef VEGAS_PHASE_TRACE
+    const int g = g_trace_rotate ? (blockIdx.x + blockIdx.x / a.hkv) % a.hkv : blockIdx.x % a.hkv;
+#else
     const int g = blockIdx.x % a.hkv;
+#endif
     const int unit_id = blockIdx.x / a.hkv;
     // This workgroup's units: entries k0 .. k0+nunits-1 of the unit table, or
     // the one unit (b, split) of the per-sequence plan.  One call site of
@@ -952,6 +976,19 @@ attn_split_kernel(const AttnArgs a) {
                                                          score_s);
         }
     }
+#ifdef VEGAS_PHASE_TRACE
+    if (threadIdx.x == 0 && blockIdx.x < kTraceMax) {
+        unsigned long long* r = g_trace[blockIdx.x];
+        r[0] = trace_t0;
+        r[1] = g_trace_loop[blockIdx.x];
+        r[2] = wall_clock64();
+        r[3] = __builtin_amdgcn_s_getreg((31 << 11) | 4);    // HW_ID: CU, SH, SE ids
+        r[4] = __builtin_amdgcn_s_getreg((31 << 11) | 20);   // XCC_ID
+        r[5] = (unsigned long long)b;
+        r[6] = (unsigned long long)split;
+        r[7] = (unsigned long long)g;
+    }
+#endif
 }
 
 // Merge the split partials of one (sequence, KV head, 16-row tile, 16-wide d
@@ -1120,6 +1157,16 @@ hipError_t launch_d(const AttnArgs& a, int d, int mb, hipStream_t s, const Selec
 }
 
 }  // namespace
+
+#ifdef VEGAS_PHASE_TRACE
+extern "C" int vegas_trace_read(void* host, size_t bytes) {
+    if (bytes > sizeof(g_trace)) return -1;
+    return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_trace), bytes, 0, hipMemcpyDeviceToHost);
+}
+extern "C" int vegas_trace_set_rotation(int rotate) {
+    return (int)hipMemcpyToSymbol(HIP_SYMBOL(g_trace_rotate), &rotate, sizeof(int), 0, hipMemcpyHostToDevice);
+}
+#endif
 
 hipError_t launch_attn(const AttnArgs& a, bool bf16, int head_dim, int mblocks, bool gather,
                        bool collect, hipStream_t stream, const SelectArgs* sel) {

@@ -42,7 +42,97 @@ __global__ void __launch_bounds__(kThreads) stream_read_kernel(const unsigned ch
     if (acc == 0u && threadIdx.x == 0) sink[blockIdx.x] = 1u;
 }
 
+// Gathered reads: the K and V slices (SLICE bytes of head h) of listed token
+// rows, the access pattern of the drafting pass, with no arithmetic.  A
+// workgroup takes head w % heads and the w / heads-th range of `per_wg` list
+// entries (at most kGatherMaxRange), stages the range's row numbers in LDS,
+// and its waves stream 16-row blocks in turn through private rings of DEPTH
+// blocks (16-byte direct-to-LDS copies, non-temporal policy): a block is
+// awaited while the next DEPTH-1 are in flight, as the drafting pass's ring
+// does.  Row numbers are clamped into [0, total_rows).
+constexpr int kGatherRows = 16;
+constexpr int kGatherMaxRange = 4096;
+template <int SLICE, int DEPTH>
+__global__ void __launch_bounds__(kThreads) gather_read_kernel(const unsigned char* __restrict__ k,
+                                                               const unsigned char* __restrict__ v,
+                                                               const int32_t* __restrict__ rows, int32_t n_rows,
+                                                               int32_t total_rows, int32_t row_bytes, int32_t heads,
+                                                               int32_t per_wg, uint32_t* __restrict__ sink) {
+    constexpr int CPR = SLICE / 16;                // 16-byte chunks per row slice
+    constexpr int RPC = 64 / CPR;                  // rows per wave-wide copy
+    constexpr int COPIES = kGatherRows / RPC;      // copies per tensor per block
+    constexpr int BLK = kGatherRows * SLICE;       // bytes per tensor per block
+    constexpr int OPS = 2 * COPIES;                // copies per block
+    __shared__ __attribute__((aligned(16))) unsigned char ring[kThreads / 64][DEPTH][2 * BLK];
+    __shared__ int idx_s[kGatherMaxRange];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int head = blockIdx.x % heads;
+    const int first = (blockIdx.x / heads) * per_wg;
+    const int count = max(min(first + per_wg, n_rows) - first, 0);
+    for (int i = threadIdx.x; i < count; i += kThreads) idx_s[i] = min(max(rows[first + i], 0), total_rows - 1);
+    __syncthreads();
+    const int nblk = (count + kGatherRows - 1) / kGatherRows;
+    const int mine = wave < nblk ? (nblk - wave + 3) / 4 : 0;      // this wave's blocks: wave, wave + 4, ...
+    auto issue = [&](int j, int stage) {
+        const int blk = wave + 4 * min(j, mine - 1);               // past the last: the last again
+#pragma unroll
+        for (int c = 0; c < COPIES; ++c) {
+            const int e = min(blk * kGatherRows + c * RPC + lane / CPR, count - 1);
+            const size_t off = (size_t)idx_s[e] * (uint32_t)row_bytes + (size_t)head * SLICE + (lane % CPR) * 16;
+            const uint32_t lk = (uint32_t)(uintptr_t)(lds_ptr_t)(&ring[wave][stage][c * 1024]);
+            const uint32_t lv = (uint32_t)(uintptr_t)(lds_ptr_t)(&ring[wave][stage][BLK + c * 1024]);
+            asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(k + off), "{m0}"(lk) : "memory");
+            asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(v + off), "{m0}"(lv) : "memory");
+        }
+    };
+    uint32_t acc = 0;
+    if (mine > 0) {
+#pragma unroll
+        for (int j = 0; j < DEPTH - 1; ++j) issue(j, j);
+        for (int j = 0; j < mine; ++j) {
+            issue(j + DEPTH - 1, (j + DEPTH - 1) % DEPTH);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DEPTH - 1) * OPS) : "memory");   // block j has landed
+            acc ^= reinterpret_cast<const uint32_t*>(&ring[wave][j % DEPTH][0])[lane];
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    if (acc == 0u && lane == 0 && mine > 0 && blockIdx.x == 0x7fffffff) sink[0] = 1u;   // keeps the reads live
+}
+
 }  // namespace
+
+extern "C" int vegas_probe_gather_read(const void* k, const void* v, const int32_t* rows, int32_t n_rows,
+                                       int32_t total_rows, int32_t row_bytes, int32_t slice_bytes, int32_t heads,
+                                       int32_t workgroups, int32_t blocks_in_flight, uint32_t* sink, void* stream) {
+    if (!k || !v || !rows || !sink || n_rows < 1 || total_rows < 1 || heads < 1 || workgroups < heads ||
+        workgroups % heads != 0 || blocks_in_flight < 1 || blocks_in_flight > 3)
+        return -1;
+    if ((slice_bytes != 128 && slice_bytes != 256) || row_bytes < heads * slice_bytes || row_bytes % 16 != 0)
+        return -1;
+    if (((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15u) != 0) return -1;
+    const int per_head = workgroups / heads;
+    const int per_wg = (n_rows + per_head - 1) / per_head;
+    if (per_wg > kGatherMaxRange) return -1;
+    const dim3 grid(workgroups), block(kThreads);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const unsigned char* kb = static_cast<const unsigned char*>(k);
+    const unsigned char* vb = static_cast<const unsigned char*>(v);
+#define VEGAS_PROBE_GATHER(S, D)                                                                                \
+    hipLaunchKernelGGL((gather_read_kernel<S, D>), grid, block, 0, st, kb, vb, rows, n_rows, total_rows, row_bytes, \
+                       heads, per_wg, sink)
+    const int depth = blocks_in_flight + 1;       // ring stages: blocks in flight plus the one awaited
+    if (slice_bytes == 256) {
+        if (depth == 2) VEGAS_PROBE_GATHER(256, 2);
+        else if (depth == 3) VEGAS_PROBE_GATHER(256, 3);
+        else VEGAS_PROBE_GATHER(256, 4);
+    } else {
+        if (depth == 2) VEGAS_PROBE_GATHER(128, 2);
+        else if (depth == 3) VEGAS_PROBE_GATHER(128, 3);
+        else VEGAS_PROBE_GATHER(128, 4);
+    }
+#undef VEGAS_PROBE_GATHER
+    return (int)hipGetLastError();
+}
 
 extern "C" int vegas_probe_stream_read(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink,
                                        void* stream) {
