@@ -8,13 +8,18 @@ select on every layer, then gamma drafting passes run the sparse decode on
 every layer.  The reported value is microseconds per layer-step
 (verify + select + gamma drafts of one layer) = step time / layers.
 
+With several layers, verification + selection runs as the one call in two
+halves: the selection's last steps of layer l go to a second stream, beside
+the verification of layer l+1 (the selected positions are used only by the
+drafting passes, which wait for every selection).
+
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
-Inside the timed region HIP events on the launch stream bracket every
-verification call (the dominant kernel); its average duration and the
-algorithmic bytes of one call (each KV byte of the verified cache read once,
-Q and O, the collected scores written once) give the HBM roofline figure.
-The per-call breakdown of select and drafting comes from two further steps
-with events around every call, after the timed region.
+The timed region runs the steps with no timing events (an event around every
+call adds ~7 us per layer-step).  Further steps after it, with HIP events on
+the launch stream around every call, give the per-call durations: those of
+the verification calls (the dominant kernel) and the algorithmic bytes of one
+call (each KV byte of the verified cache read once, Q and O, the collected
+scores written once) give the HBM roofline figure.
 """
 from __future__ import annotations
 
@@ -461,7 +466,12 @@ def main():
     ap.add_argument("--no-stream-ceiling", action="store_true",
                     help="skip the measured streaming-read ceiling (4 GiB read by a plain kernel)")
     ap.add_argument("--separate-calls", action="store_true",
-                    help="time verification and selection as two library calls instead of one")
+                    help="time verification and selection as two library calls on one stream")
+    ap.add_argument("--single-stream", action="store_true",
+                    help="time verification and selection as one library call on the launch stream (by default "
+                         "a workload of several layers runs the selection's last steps of layer l on a second "
+                         "stream beside the verification of layer l+1; the single-stream figure is reported in "
+                         "any case)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--page-size", type=int, default=0,
                     help="keep every layer's KV cache as a randomly permuted page pool of this page size and "
@@ -542,12 +552,23 @@ def main():
     # Verification and selection as one library call where the path allows it.
     fused = steps[0].fusable and not args.separate_calls
     fused_calls = [st.bind_fused(stream, host_plan=host_plan) for st in steps] if fused else None
+    # The one call in two halves, the selection's last steps (cand, write) of layer l on a second
+    # stream beside the verification of layer l+1: the selected positions are used only by the
+    # drafting passes, which start after every selection has finished, while layer l+1's
+    # verification needs only layer l's output, complete when the first half ends.
+    overlap = fused and host_plan and layers > 1 and not args.single_stream
+    side = torch.cuda.Stream() if overlap else None              # default priority, as the launch stream
+    begin_calls = [st.bind_fused(stream, part="begin") for st in steps] if overlap else None
+    end_calls = [st.bind_fused(side, part="end") for st in steps] if overlap else None
+    verified = [torch.cuda.Event() for _ in steps] if overlap else None
+    selected = torch.cuda.Event() if overlap else None
 
-    def one_step(head_events=None, call_events=None):
+    def one_step(head_events=None, call_events=None, single_stream=False):
         """One speculative iteration: verify + select on every layer, then gamma drafting
         passes over every layer.  head_events: list receiving an event pair around every
-        verify (separate calls) or verify+select (one call); call_events: dict receiving
-        event pairs around every call of the separate-call path."""
+        verify (separate calls) or verify+select (one call, or its first half with the
+        second half on the second stream); call_events: dict receiving event pairs around every
+        call of the separate-call path; single_stream: the one call on the launch stream."""
         def timed(kind, fn, sink):
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
@@ -556,12 +577,13 @@ def main():
             b.record(stream)
             sink[kind].append((a, b))
 
+        halves = overlap and not single_stream
         for li, (verify, _, select, _) in enumerate(bound):
             if call_events is not None:
                 timed("verify", verify, call_events)
                 timed("select", select, call_events)
                 continue
-            head = fused_calls[li] if fused else verify
+            head = begin_calls[li] if halves else (fused_calls[li] if fused else verify)
             if head_events is not None:
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
@@ -571,8 +593,15 @@ def main():
                 head_events.append((a, b))
             else:
                 head()
-            if not fused:
+            if halves:
+                verified[li].record(stream)
+                side.wait_event(verified[li])
+                end_calls[li]()
+            elif not fused:
                 select()
+        if halves:
+            selected.record(side)
+            stream.wait_event(selected)
         for j in range(wl.n_drafts):
             for _, _, _, drafts in bound:
                 if call_events is not None:
@@ -583,12 +612,35 @@ def main():
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
-    head_pairs = []
+    # The timed region runs the steps alone: timing events around every call would add ~7 us
+    # per layer-step (each timed event waits for the work before it); the per-call durations
+    # come from instrumented steps after it.
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        one_step(head_events=head_pairs)
+        one_step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+
+    # Instrumented steps of the same schedule: events around every verification (or
+    # verification + selection) call.
+    head_pairs = []
+    for _ in range(max(2, 12 // layers)):
+        one_step(head_events=head_pairs)
+    torch.cuda.synchronize()
+
+    # The one call on the launch stream alone, for comparison with the two-stream schedule.
+    single_ms, single_heads = None, []
+    if overlap:
+        one_step(single_stream=True)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        n_single = max(3, args.steps // 2)
+        for _ in range(n_single):
+            one_step(single_stream=True)
+        torch.cuda.synchronize()
+        single_ms = (time.perf_counter() - t1) * 1e3 / n_single
+        one_step(head_events=single_heads, single_stream=True)   # the one call's own duration
+        torch.cuda.synchronize()
 
     # Per-call breakdown, outside the timed region: more steps with events around every call.
     call_pairs = {"verify": [], "select": [], "draft": []}
@@ -605,12 +657,18 @@ def main():
     pct = {k: p10_p90(v) for k, v in per.items()}
     head_us = [a.elapsed_time(b) * 1e3 for a, b in head_pairs]
     if fused:
-        # The timed region runs verification + selection as one call; the verification
-        # kernels' own duration comes from the separate-call steps of the breakdown.
+        # The timed region runs verification + selection as one call (or its first half); the
+        # verification kernels' own duration comes from the separate-call steps of the breakdown.
         verify_us = per["verify"]
-        mean["verify_select"] = statistics.fmean(head_us)
-        med["verify_select"] = statistics.median(head_us)
-        pct["verify_select"] = p10_p90(head_us)
+        head_key = "verify_select_first_half" if overlap else "verify_select"
+        mean[head_key] = statistics.fmean(head_us)
+        med[head_key] = statistics.median(head_us)
+        pct[head_key] = p10_p90(head_us)
+        if overlap:
+            one = [a.elapsed_time(b) * 1e3 for a, b in single_heads]
+            mean["verify_select"] = statistics.fmean(one)
+            med["verify_select"] = statistics.median(one)
+            pct["verify_select"] = p10_p90(one)
     else:
         verify_us = head_us
     verify_mean = statistics.fmean(verify_us)
@@ -665,13 +723,23 @@ def main():
             "avg_launch_us": round(verify_mean, 2),
             "launches_timed": len(verify_us),
             "timed_in": ("separate-call breakdown steps after the timed region (which runs verification "
-                         "and selection as one call)" if fused else "the timed region"),
+                         "and selection as one call, or its two halves)" if fused else
+                         "instrumented steps of the timed schedule after the timed region (which runs without "
+                         "timing events)"),
         },
     }
     sfx = "_hostplan" if host_plan else ""
-    result["config"]["calls"] = (f"vegas_verify_select{sfx} + gamma x vegas_sparse_decode_attn{sfx} per layer"
-                                 if fused else
-                                 f"verify{sfx}, select and gamma sparse-decode{sfx} calls per layer")
+    if overlap:
+        result["config"]["calls"] = ("vegas_verify_select_begin_hostplan per layer on the launch stream, "
+                                     "vegas_verify_select_end_hostplan of layer l on a second stream beside layer "
+                                     "l+1; then gamma x vegas_sparse_decode_attn_hostplan per layer")
+        result["layer_step_single_stream_us"] = round(single_ms * 1e3 / layers, 2)
+        result["layer_step_single_stream_calls"] = ("vegas_verify_select_hostplan + gamma x "
+                                                    "vegas_sparse_decode_attn_hostplan per layer, one stream")
+    else:
+        result["config"]["calls"] = (f"vegas_verify_select{sfx} + gamma x vegas_sparse_decode_attn{sfx} per layer"
+                                     if fused else
+                                     f"verify{sfx}, select and gamma sparse-decode{sfx} calls per layer")
     result["config"]["split_plan"] = ("host (host copies of the offsets, computed per call)" if host_plan
                                       else "device")
 

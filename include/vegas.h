@@ -240,6 +240,39 @@ vegas_status_t vegas_verify_select_hostplan(const vegas_attn_shape_t* shape, int
                                             void* stream, const vegas_host_offsets_t* host);
 
 /*
+ * vegas_verify_select_hostplan in two halves, for callers that run the
+ * selection's last steps on another stream beside later work.  The selected
+ * positions are used only by the next drafting pass ("Vegas ...", sec. 3:
+ * selection follows verification, drafting uses its result), while the next
+ * layer's verification needs only this layer's output; the second half can
+ * then overlap the next layer's verification.
+ *   _begin: the verification kernels, with the selection's histogram
+ *           clearing and its summed-score and key step (out and scores are
+ *           complete when it finishes);
+ *   _end:   the selection's remaining steps (indices complete when it
+ *           finishes), on any stream ordered after _begin's completion (for
+ *           example by an event the caller records on _begin's stream).
+ * Both take the same arguments as vegas_verify_select_hostplan, with the same
+ * workspace, which must not be reused until _end has finished; both validate
+ * them, and _end launches nothing else.  Together they give the results of
+ * vegas_verify_select_hostplan bit for bit.
+ */
+vegas_status_t vegas_verify_select_begin_hostplan(const vegas_attn_shape_t* shape, int32_t gamma,
+                                                  const void* q, const void* k, const void* v,
+                                                  const int32_t* cu_seqlens_k, int32_t max_seqlen_k,
+                                                  int32_t total_kv, uint32_t collect_mask,
+                                                  const int32_t* cu_k, float* scores, int32_t* indices,
+                                                  void* out, void* workspace, size_t workspace_bytes,
+                                                  void* stream, const vegas_host_offsets_t* host);
+vegas_status_t vegas_verify_select_end_hostplan(const vegas_attn_shape_t* shape, int32_t gamma,
+                                                const void* q, const void* k, const void* v,
+                                                const int32_t* cu_seqlens_k, int32_t max_seqlen_k,
+                                                int32_t total_kv, uint32_t collect_mask,
+                                                const int32_t* cu_k, float* scores, int32_t* indices,
+                                                void* out, void* workspace, size_t workspace_bytes,
+                                                void* stream, const vegas_host_offsets_t* host);
+
+/*
  * Sparse drafting attention over selected tokens.
  * Defined by "Vegas ..." sec. 4 "Serving framework integration" (paged
  * attention with a page size of one token whose page indices are the

@@ -346,3 +346,24 @@ def test_trace_build_is_separate_from_the_product_library(V):
     assert "vegas_trace" not in product
     for name in V.EXPORTED:              # and the same C ABI otherwise
         assert name in trace
+
+
+def test_verify_select_halves_check_arguments(V):
+    """Both halves of the one call validate like it before launching anything."""
+    L = V.lib()
+    s = shape(V)
+    need = V.vegas_verify_select_workspace_size(s, 4, 1000, 4000)
+    good = V.host_offsets([0, 1000, 2000, 3000, 4000], [0, 50, 100, 150, 200])
+    bad = V.host_offsets([0, 1000, 900, 3000, 4000], [0, 50, 100, 150, 200])
+    for name in ("vegas_verify_select_begin_hostplan", "vegas_verify_select_end_hostplan"):
+        fn = getattr(L, name)
+
+        def call(host, wsb=need, mask=1 | 16):
+            return fn(ctypes.byref(s), 4, FAKE, FAKE, FAKE, FAKE, 1000, 4000, mask, FAKE, FAKE, FAKE, FAKE, FAKE, wsb,
+                      None, ctypes.byref(host) if host is not None else None)
+
+        assert call(None) == 1
+        assert call(bad) == 1
+        assert "decreases" in L.vegas_last_error_message().decode()
+        assert call(good, wsb=need - 1) == 3
+        assert call(good, mask=0) == 1

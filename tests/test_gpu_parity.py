@@ -699,3 +699,39 @@ def test_hostplan_calls_equal_device_planned_calls(case):
         st.run(fused=True, host_plan=True)
         torch.cuda.synchronize()
         check_layer(wl, inp, st)
+
+
+@pytest.mark.parametrize("case", FUSED_CASES,
+                         ids=lambda c: c if isinstance(c, str) else f"{c[0]}-B{c[1]}-{c[2]}x{c[3]}-D{c[4]}-g{c[5]}-L{c[6]}")
+def test_verify_select_halves_on_two_streams_equal_one_call(case):
+    """vegas_verify_select_begin_hostplan on one stream, then vegas_verify_select_end_hostplan on a
+    second stream ordered after it by an event: output, scores and selection equal the one call's bit
+    for bit, from any workspace contents, twice in a row."""
+    if isinstance(case, str):
+        wl = W.named_workload(4)
+    else:
+        dtype, B, hq, hkv, d, gamma, prefixes, ratio = case
+        wl = W.custom_workload(dtype, B, hq, hkv, d, gamma, prefixes, ratio=ratio)
+    log(f"case: verify+select halves on two streams {wl.name}")
+    inp = W.make_inputs(wl, seed=6, device="cuda")
+    st = LayerStep(inp, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.gamma, wl.seqlens,
+                   wl.k_per_seq, wl.scale, n_drafts=wl.n_drafts)
+    cu, cuk = wl.cu_seqlens(), wl.cu_k()
+    st.verify_select(host_plan=True)
+    torch.cuda.synchronize()
+    ref = (st.out.clone(), [st.scores[:, cu[b]:cu[b] + wl.prefix_lens[b]].clone() for b in range(wl.batch)],
+           st.indices[: cuk[-1]].clone())
+    side = torch.cuda.Stream()
+    for rep, fill in enumerate((0x5A, 0xFF)):
+        st.workspace.fill_(fill)
+        st.out.fill_(3.0)
+        st.scores.fill_(float("nan"))
+        st.indices.fill_(-7)
+        st.run(fused=True, host_plan=True, select_stream=side)
+        torch.cuda.synchronize()
+        assert torch.equal(st.out.view(torch.uint8), ref[0].view(torch.uint8)), rep
+        for b in range(wl.batch):
+            assert torch.equal(st.scores[:, cu[b]:cu[b] + wl.prefix_lens[b]], ref[1][b]), (rep, b)
+        assert torch.equal(st.indices[: cuk[-1]], ref[2]), rep
+    if not isinstance(case, str):
+        check_layer(wl, inp, st)

@@ -24,10 +24,12 @@ def _gpu_only():
 
 
 def _timed_layer(wl: W.Workload, layer: int):
+    """One layer through the calls bench.py times for this workload: with several layers the one
+    call in two halves, the second on another stream; with one layer the one call."""
     inp = W.make_inputs(wl, seed=0, device="cuda", layer=layer)
     st = LayerStep(inp, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.gamma, wl.seqlens,
                    wl.k_per_seq, wl.scale, n_drafts=wl.n_drafts)
-    st.run(fused=True, host_plan=True)
+    st.run(fused=True, host_plan=True, select_stream=torch.cuda.Stream() if wl.layers > 1 else None)
     torch.cuda.synchronize()
     return inp, st
 

@@ -379,7 +379,8 @@ vegas_status_t verify_impl(const vegas_attn_shape_t* shape, int32_t gamma, const
                            const void* v, const vegas_paged_kv_t* pages, const int32_t* cu_seqlens_k,
                            int32_t max_seqlen_k, int32_t total_kv, uint32_t collect_mask, float* scores,
                            void* out, void* workspace, size_t workspace_bytes, void* stream, int32_t window = 0,
-                           const vegas::SelectArgs* fused = nullptr, const int32_t* cu_host = nullptr) {
+                           const vegas::SelectArgs* fused = nullptr, const int32_t* cu_host = nullptr,
+                           bool launch = true) {
     vegas_status_t st = check_shape(shape);
     if (st != VEGAS_OK) return st;
     if ((st = check_gamma(gamma, shape)) != VEGAS_OK) return st;
@@ -462,6 +463,7 @@ vegas_status_t verify_impl(const vegas_attn_shape_t* shape, int32_t gamma, const
     }
     a.score_cap = plan.cap;
     if (a.hp.n > 0) a.score_cap = longest_unit(a.hp);
+    if (!launch) return VEGAS_OK;                  // arguments checked only
     return hip_status(vegas::launch_attn(a, shape->dtype == VEGAS_DTYPE_BF16, shape->head_dim, plan.mb,
                                          false, collect_mask != 0u, static_cast<hipStream_t>(stream), fused),
                       "verify launch");
@@ -712,11 +714,16 @@ vegas_status_t vegas_verify_select_workspace_size(const vegas_attn_shape_t* shap
 
 namespace {
 
+// Which launches of the one-call verification + selection a call issues: all
+// of them, the verification kernels (with the selection's clearing and key
+// steps), or the selection's remaining steps.
+enum class Part { kAll, kBegin, kEnd };
+
 vegas_status_t verify_select_impl(const vegas_attn_shape_t* shape, int32_t gamma, const void* q, const void* k,
                                   const void* v, const int32_t* cu_seqlens_k, int32_t max_seqlen_k,
                                   int32_t total_kv, uint32_t collect_mask, const int32_t* cu_k, float* scores,
                                   int32_t* indices, void* out, void* workspace, size_t workspace_bytes,
-                                  void* stream, const vegas_host_offsets_t* host) {
+                                  void* stream, const vegas_host_offsets_t* host, Part part = Part::kAll) {
     size_t need = 0, vb = 0;
     vegas_status_t st = vegas_verify_select_workspace_size(shape, gamma, max_seqlen_k, total_kv, &need);
     if (st != VEGAS_OK) return st;
@@ -749,9 +756,10 @@ vegas_status_t verify_select_impl(const vegas_attn_shape_t* shape, int32_t gamma
         }
     }
     if ((st = verify_impl(shape, gamma, q, k, v, nullptr, cu_seqlens_k, max_seqlen_k, total_kv, collect_mask,
-                          scores, out, workspace, vb, stream, 0, &sa, host ? host->cu_seqlens_k : nullptr)) !=
-        VEGAS_OK)
+                          scores, out, workspace, vb, stream, 0, &sa, host ? host->cu_seqlens_k : nullptr,
+                          part != Part::kEnd)) != VEGAS_OK)
         return st;
+    if (part == Part::kBegin) return VEGAS_OK;
     return hip_status(vegas::launch_select_tail(sa, static_cast<hipStream_t>(stream)), "select launch");
 }
 
@@ -819,6 +827,30 @@ vegas_status_t vegas_verify_select_hostplan(const vegas_attn_shape_t* shape, int
         return fail(VEGAS_ERR_INVALID_ARGUMENT, "host offsets (cu_seqlens_k and cu_idx = cu_k) must be non-NULL");
     return verify_select_impl(shape, gamma, q, k, v, cu_seqlens_k, max_seqlen_k, total_kv, collect_mask, cu_k,
                               scores, indices, out, workspace, workspace_bytes, stream, host);
+}
+
+vegas_status_t vegas_verify_select_begin_hostplan(const vegas_attn_shape_t* shape, int32_t gamma, const void* q,
+                                                  const void* k, const void* v, const int32_t* cu_seqlens_k,
+                                                  int32_t max_seqlen_k, int32_t total_kv, uint32_t collect_mask,
+                                                  const int32_t* cu_k, float* scores, int32_t* indices, void* out,
+                                                  void* workspace, size_t workspace_bytes, void* stream,
+                                                  const vegas_host_offsets_t* host) {
+    if (!host || !host->cu_seqlens_k || !host->cu_idx)
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "host offsets (cu_seqlens_k and cu_idx = cu_k) must be non-NULL");
+    return verify_select_impl(shape, gamma, q, k, v, cu_seqlens_k, max_seqlen_k, total_kv, collect_mask, cu_k,
+                              scores, indices, out, workspace, workspace_bytes, stream, host, Part::kBegin);
+}
+
+vegas_status_t vegas_verify_select_end_hostplan(const vegas_attn_shape_t* shape, int32_t gamma, const void* q,
+                                                const void* k, const void* v, const int32_t* cu_seqlens_k,
+                                                int32_t max_seqlen_k, int32_t total_kv, uint32_t collect_mask,
+                                                const int32_t* cu_k, float* scores, int32_t* indices, void* out,
+                                                void* workspace, size_t workspace_bytes, void* stream,
+                                                const vegas_host_offsets_t* host) {
+    if (!host || !host->cu_seqlens_k || !host->cu_idx)
+        return fail(VEGAS_ERR_INVALID_ARGUMENT, "host offsets (cu_seqlens_k and cu_idx = cu_k) must be non-NULL");
+    return verify_select_impl(shape, gamma, q, k, v, cu_seqlens_k, max_seqlen_k, total_kv, collect_mask, cu_k,
+                              scores, indices, out, workspace, workspace_bytes, stream, host, Part::kEnd);
 }
 
 vegas_status_t vegas_sparse_decode_workspace_size(const vegas_attn_shape_t* shape, int32_t max_idx,

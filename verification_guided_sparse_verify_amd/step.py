@@ -126,8 +126,20 @@ class LayerStep:
         V.vegas_sparse_decode_attn(self.shape, i["draft_q"][j], i["k"], i["v"], i["cu_seqlens_k"], self.total_kv,
                                    self.indices, i["cu_k"], self.max_k, self.draft_out[j], self.workspace, stream)
 
-    def run(self, stream=None, fused: bool = False, host_plan: bool = False):
-        if fused:
+    def run(self, stream=None, fused: bool = False, host_plan: bool = False, select_stream=None):
+        """One layer step.  select_stream (with fused and host_plan): the selection's last steps run
+        there after the verification kernels, and the drafting passes wait for them."""
+        if fused and select_stream is not None:
+            launch = stream if stream is not None else torch.cuda.current_stream()
+            self.bind_fused(launch, part="begin")()
+            verified = torch.cuda.Event()
+            verified.record(launch)
+            select_stream.wait_event(verified)
+            self.bind_fused(select_stream, part="end")()
+            selected = torch.cuda.Event()
+            selected.record(select_stream)
+            launch.wait_event(selected)
+        elif fused:
             self.verify_select(stream, host_plan)
         else:
             self.verify(self.selection == "vegas", stream)
@@ -194,9 +206,9 @@ class LayerStep:
                   for j in range(self.n_drafts)]
         return verify, plain, select, drafts
 
-    def bind_fused(self, stream=None, host_plan: bool = False):
+    def bind_fused(self, stream=None, host_plan: bool = False, part: str = ""):
         """Argument-free callable of the one-call verification + selection (host_plan: the
-        host-planned entry point)."""
+        host-planned entry point; part "begin" or "end": that half of it, host-planned)."""
         if not self.fusable:
             raise ValueError("the one-call verification + selection needs a contiguous cache and Vegas selection")
         i = self.inp
@@ -205,9 +217,9 @@ class LayerStep:
                 i["cu_k"].data_ptr(), self.scores.data_ptr(), self.indices.data_ptr(), self.out.data_ptr(),
                 self.workspace.data_ptr(), self.workspace.numel(), V._stream(stream))
         name = "vegas_verify_select"
-        if host_plan:
+        if host_plan or part:
             args += (ctypes.byref(self.host),)
-            name = "vegas_verify_select_hostplan"
+            name = f"vegas_verify_select_{part}_hostplan" if part else "vegas_verify_select_hostplan"
         fn = getattr(V.lib(), name)
 
         def go():

@@ -34,6 +34,7 @@ EXPORTED = (
     "vegas_spec_accept_workspace_size", "vegas_spec_accept",
     "vegas_verify_attn_hostplan", "vegas_verify_select_hostplan", "vegas_sparse_decode_attn_hostplan",
     "vegas_verify_hostplan_info", "vegas_sparse_decode_attn_noalloc", "vegas_noalloc_scratch_bytes",
+    "vegas_verify_select_begin_hostplan", "vegas_verify_select_end_hostplan",
 )
 
 
@@ -113,6 +114,10 @@ def lib():
                                            ctypes.c_int),
             "vegas_sparse_decode_attn_noalloc": ([SP, P, P, P, P, I32, P, P, I32, P, P, HP], ctypes.c_int),
             "vegas_noalloc_scratch_bytes": ([], SZ),
+            "vegas_verify_select_begin_hostplan": ([SP, I32, P, P, P, P, I32, I32, U32, P, P, P, P, P, SZ, P, HP],
+                                                   ctypes.c_int),
+            "vegas_verify_select_end_hostplan": ([SP, I32, P, P, P, P, I32, I32, U32, P, P, P, P, P, SZ, P, HP],
+                                                 ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -252,6 +257,27 @@ def vegas_verify_select_hostplan(shape: AttnShape, gamma: int, q, k, v, cu_seqle
                                               _ptr(cu_k), _ptr(scores), _ptr(indices), _ptr(out), _ptr(workspace),
                                               _nbytes(workspace), _stream(stream), ctypes.byref(host)),
            "vegas_verify_select_hostplan")
+
+
+def _verify_select_half(name, shape, gamma, q, k, v, cu_seqlens_k, max_seqlen_k, total_kv, collect_mask, cu_k, scores,
+                        indices, out, workspace, host, stream):
+    _check(getattr(lib(), name)(ctypes.byref(shape), gamma, _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), max_seqlen_k,
+                                total_kv, collect_mask & 0xFFFFFFFF, _ptr(cu_k), _ptr(scores), _ptr(indices), _ptr(out),
+                                _ptr(workspace), _nbytes(workspace), _stream(stream), ctypes.byref(host)), name)
+
+
+def vegas_verify_select_begin_hostplan(shape: AttnShape, gamma: int, q, k, v, cu_seqlens_k, max_seqlen_k: int,
+                                       total_kv: int, collect_mask: int, cu_k, scores, indices, out, workspace,
+                                       host: HostOffsets, stream=None) -> None:
+    _verify_select_half("vegas_verify_select_begin_hostplan", shape, gamma, q, k, v, cu_seqlens_k, max_seqlen_k,
+                        total_kv, collect_mask, cu_k, scores, indices, out, workspace, host, stream)
+
+
+def vegas_verify_select_end_hostplan(shape: AttnShape, gamma: int, q, k, v, cu_seqlens_k, max_seqlen_k: int,
+                                     total_kv: int, collect_mask: int, cu_k, scores, indices, out, workspace,
+                                     host: HostOffsets, stream=None) -> None:
+    _verify_select_half("vegas_verify_select_end_hostplan", shape, gamma, q, k, v, cu_seqlens_k, max_seqlen_k,
+                        total_kv, collect_mask, cu_k, scores, indices, out, workspace, host, stream)
 
 
 def vegas_sparse_decode_workspace_size(shape: AttnShape, max_idx: int) -> int:
