@@ -247,11 +247,11 @@ vegas_status_t vegas_verify_select_hostplan(const vegas_attn_shape_t* shape, int
  * layer's verification needs only this layer's output; the second half can
  * then overlap the next layer's verification.
  *   _begin: the verification kernels, with the selection's histogram
- *           clearing and its summed-score and key step (out and scores are
- *           complete when it finishes);
- *   _end:   the selection's remaining steps (indices complete when it
- *           finishes), on any stream ordered after _begin's completion (for
- *           example by an event the caller records on _begin's stream).
+ *           clearing (out and scores are complete when it finishes);
+ *   _end:   the selection's remaining steps, from the summed scores and
+ *           their keys to the lists (indices complete when it finishes), on
+ *           any stream ordered after _begin's completion (for example by an
+ *           event the caller records on _begin's stream).
  * Both take the same arguments as vegas_verify_select_hostplan, with the same
  * workspace, which must not be reused until _end has finished; both validate
  * them, and _end launches nothing else.  Together they give the results of

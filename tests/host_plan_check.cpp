@@ -64,6 +64,11 @@ hipError_t launch_select_tail(const SelectArgs& a, hipStream_t) {
     g_cap.s = a;
     return hipSuccess;
 }
+hipError_t launch_select_from_keys(const SelectArgs& a, hipStream_t) {
+    g_cap.sel_tail = true;
+    g_cap.s = a;
+    return hipSuccess;
+}
 hipError_t launch_spec_accept(const AcceptArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_streaming_indices(int, int, int, const int32_t*, int32_t, const int32_t*, int32_t, int32_t*,
                                     hipStream_t) {

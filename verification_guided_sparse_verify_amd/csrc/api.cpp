@@ -380,7 +380,7 @@ vegas_status_t verify_impl(const vegas_attn_shape_t* shape, int32_t gamma, const
                            int32_t max_seqlen_k, int32_t total_kv, uint32_t collect_mask, float* scores,
                            void* out, void* workspace, size_t workspace_bytes, void* stream, int32_t window = 0,
                            const vegas::SelectArgs* fused = nullptr, const int32_t* cu_host = nullptr,
-                           bool launch = true) {
+                           bool launch = true, bool keys_in_combine = true) {
     vegas_status_t st = check_shape(shape);
     if (st != VEGAS_OK) return st;
     if ((st = check_gamma(gamma, shape)) != VEGAS_OK) return st;
@@ -464,8 +464,10 @@ vegas_status_t verify_impl(const vegas_attn_shape_t* shape, int32_t gamma, const
     a.score_cap = plan.cap;
     if (a.hp.n > 0) a.score_cap = longest_unit(a.hp);
     if (!launch) return VEGAS_OK;                  // arguments checked only
+    // (fused without the keys step: the split kernel still clears the selection's histograms)
     return hip_status(vegas::launch_attn(a, shape->dtype == VEGAS_DTYPE_BF16, shape->head_dim, plan.mb,
-                                         false, collect_mask != 0u, static_cast<hipStream_t>(stream), fused),
+                                         false, collect_mask != 0u, static_cast<hipStream_t>(stream),
+                                         keys_in_combine ? fused : nullptr),
                       "verify launch");
 }
 
@@ -715,8 +717,9 @@ vegas_status_t vegas_verify_select_workspace_size(const vegas_attn_shape_t* shap
 namespace {
 
 // Which launches of the one-call verification + selection a call issues: all
-// of them, the verification kernels (with the selection's clearing and key
-// steps), or the selection's remaining steps.
+// of them (the keys step in the verification combine kernel); the
+// verification kernels only (the split kernel clearing the selection's
+// histograms); or the selection's remaining steps (keys, candidates, write).
 enum class Part { kAll, kBegin, kEnd };
 
 vegas_status_t verify_select_impl(const vegas_attn_shape_t* shape, int32_t gamma, const void* q, const void* k,
@@ -757,9 +760,11 @@ vegas_status_t verify_select_impl(const vegas_attn_shape_t* shape, int32_t gamma
     }
     if ((st = verify_impl(shape, gamma, q, k, v, nullptr, cu_seqlens_k, max_seqlen_k, total_kv, collect_mask,
                           scores, out, workspace, vb, stream, 0, &sa, host ? host->cu_seqlens_k : nullptr,
-                          part != Part::kEnd)) != VEGAS_OK)
+                          part != Part::kEnd, part == Part::kAll)) != VEGAS_OK)
         return st;
     if (part == Part::kBegin) return VEGAS_OK;
+    if (part == Part::kEnd)
+        return hip_status(vegas::launch_select_from_keys(sa, static_cast<hipStream_t>(stream)), "select launch");
     return hip_status(vegas::launch_select_tail(sa, static_cast<hipStream_t>(stream)), "select launch");
 }
 

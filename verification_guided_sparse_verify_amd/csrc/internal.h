@@ -178,7 +178,9 @@ __host__ __device__ constexpr int select_zeroed_words(int batch) { return batch 
 
 // All four selection launches (zero, keys, cand, write) ...
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
-// ... or the last two, after a fused verification pass did zero and keys.
+// ... or the last two, after a fused verification pass did zero and keys ...
 hipError_t launch_select_tail(const SelectArgs& a, hipStream_t stream);
+// ... or the last three, after a verification pass that only cleared the histograms.
+hipError_t launch_select_from_keys(const SelectArgs& a, hipStream_t stream);
 
 }  // namespace vegas

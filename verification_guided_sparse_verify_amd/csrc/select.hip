@@ -360,6 +360,13 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
     return e != hipSuccess ? e : launch_select_tail(a, stream);
 }
 
+hipError_t launch_select_from_keys(const SelectArgs& a, hipStream_t stream) {
+    if (a.nchunks > 0)
+        hipLaunchKernelGGL(sel_keys_kernel, dim3(a.nchunks, a.batch), dim3(kSelThreads), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    return e != hipSuccess ? e : launch_select_tail(a, stream);
+}
+
 hipError_t launch_select_tail(const SelectArgs& a, hipStream_t stream) {
     if (a.nchunks > 0) {
         const dim3 grid(a.nchunks, a.batch);
