@@ -9,9 +9,9 @@ every layer.  The reported value is microseconds per layer-step
 (verify + select + gamma drafts of one layer) = step time / layers.
 
 With several layers, verification + selection runs as the one call in two
-halves: the selection's last steps of layer l go to a second stream, beside
-the verification of layer l+1 (the selected positions are used only by the
-drafting passes, which wait for every selection).
+halves: the selection of layer l (keys, candidates, write) goes to a second
+stream, beside the verification of layer l+1 (the selected positions are used
+only by the drafting passes, which wait for each layer's selection).
 
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
 The timed region runs the steps with no timing events (an event around every
@@ -111,7 +111,7 @@ def cpu_baseline(wl, layer_inputs, min_seconds=10.0):
     cus = np.array(wl.cu_seqlens(), np.int32)
     cuk = np.array(wl.cu_k(), np.int32)
     oracle._lib()
-    spent, done = 0.0, 0
+    spent, done, per_layer = 0.0, 0, []
     for inp in layer_inputs:
         q = W.host_bits(inp["q"])
         k = W.host_bits(inp["k"])
@@ -122,10 +122,12 @@ def cpu_baseline(wl, layer_inputs, min_seconds=10.0):
         idx, _, _ = oracle.select_topk(sc, cus, wl.gamma, cuk)
         for j in range(wl.n_drafts):
             oracle.sparse_decode_attn(dq[j], k, v, cus, idx, cuk, wl.scale)
-        spent += time.perf_counter() - t0
+        dt = time.perf_counter() - t0
+        spent += dt
+        per_layer.append(dt)
         done += 1
         del q, k, v, dq, sc
-        if spent >= min_seconds:
+        if spent >= min_seconds and done >= 3:
             break
     omp = os.environ.get("OMP_NUM_THREADS")
     threads = int(omp) if omp and omp.isdigit() else len(os.sched_getaffinity(0))
@@ -133,12 +135,14 @@ def cpu_baseline(wl, layer_inputs, min_seconds=10.0):
     return {
         "value": round(spent * 1e6 / done, 1),
         "unit": "us/layer-step",
+        "median_us": round(statistics.median(per_layer) * 1e6, 1),
+        "per_layer_us": [round(x * 1e6, 1) for x in per_layer],
         "cores": min(threads, tasks),
         "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"layers 0..{done - 1} of {len(layer_inputs)}, all {wl.batch} sequences "
                    f"(verify + select + {wl.n_drafts} drafts each), {spent:.2f} s in total, "
-                   f"divided by {done} layer-steps"),
+                   f"divided by {done} layer-steps (at least 3 layers; median_us is their median)"),
     }
 
 
@@ -552,16 +556,16 @@ def main():
     # Verification and selection as one library call where the path allows it.
     fused = steps[0].fusable and not args.separate_calls
     fused_calls = [st.bind_fused(stream, host_plan=host_plan) for st in steps] if fused else None
-    # The one call in two halves, the selection's last steps (cand, write) of layer l on a second
+    # The one call in two halves, the selection of layer l (keys, candidates, write) on a second
     # stream beside the verification of layer l+1: the selected positions are used only by the
-    # drafting passes, which start after every selection has finished, while layer l+1's
-    # verification needs only layer l's output, complete when the first half ends.
+    # drafting passes, which wait for each layer's selection, while layer l+1's verification
+    # needs only layer l's output, complete when the first half ends.
     overlap = fused and host_plan and layers > 1 and not args.single_stream
     side = torch.cuda.Stream() if overlap else None              # default priority, as the launch stream
     begin_calls = [st.bind_fused(stream, part="begin") for st in steps] if overlap else None
     end_calls = [st.bind_fused(side, part="end") for st in steps] if overlap else None
     verified = [torch.cuda.Event() for _ in steps] if overlap else None
-    selected = torch.cuda.Event() if overlap else None
+    selected = [torch.cuda.Event() for _ in steps] if overlap else None
 
     def one_step(head_events=None, call_events=None, single_stream=False):
         """One speculative iteration: verify + select on every layer, then gamma drafting
@@ -577,7 +581,7 @@ def main():
             b.record(stream)
             sink[kind].append((a, b))
 
-        halves = overlap and not single_stream
+        halves = overlap and not single_stream and call_events is None
         for li, (verify, _, select, _) in enumerate(bound):
             if call_events is not None:
                 timed("verify", verify, call_events)
@@ -597,13 +601,13 @@ def main():
                 verified[li].record(stream)
                 side.wait_event(verified[li])
                 end_calls[li]()
+                selected[li].record(side)
             elif not fused:
                 select()
-        if halves:
-            selected.record(side)
-            stream.wait_event(selected)
         for j in range(wl.n_drafts):
-            for _, _, _, drafts in bound:
+            for li, (_, _, _, drafts) in enumerate(bound):
+                if halves and j == 0:
+                    stream.wait_event(selected[li])    # the first drafting pass needs layer li's selection
                 if call_events is not None:
                     timed("draft", drafts[j], call_events)
                 else:
