@@ -14,7 +14,8 @@
 //     units fit the grid it launches;
 //   - coverage: the splits of every sequence cover its positions exactly,
 //     none is empty and none is longer than the LDS buffers allow (the
-//     collected-score buffer, the staged index list, the staged page list);
+//     collected-score buffer, in whole 16-position blocks, the staged index
+//     list, the staged page list);
 //   - the balanced plan's tables: workgroups, units and slot numbers within
 //     their fixed arrays;
 //   - the workspace: partials, split counts and the selection's buffers lie
@@ -239,6 +240,9 @@ void check_attn(const Case& c, bool gather, size_t ws_bytes, const char* entry, 
     if (!gather) {
         if (hp.n == 0) REQUIRE(a.score_cap == cap, "device plan: score buffer %d, cap %d", a.score_cap, cap);
         REQUIRE(a.score_cap <= cap, "score buffer %d above cap %d", a.score_cap, cap);
+        // a unit's last block writes the collected scores of all its 16 positions (also those past
+        // the unit's end): the buffer holds whole blocks
+        REQUIRE(a.score_cap % vegas::kAttnBlock == 0, "score buffer %d not whole blocks", a.score_cap);
         if (hp.n > 0 && hp.nwg == 0)
             for (int b = 0; b < B; ++b)
                 if (hp.first[b + 1] > hp.first[b])

@@ -213,7 +213,11 @@ void host_plan(const AttnPlan& plan, int batch, int W, int window, int32_t total
     if (!gather && total > 0) balance_plan(plan, batch, len, ns, total, hp);
 }
 
-// Longest unit (split or balanced slice) of a host plan, in positions.
+// Longest unit (split or balanced slice) of a host plan, in positions,
+// rounded up to whole 16-position blocks: a unit's last block records the
+// collected scores of all its 16 positions, also those past the unit's end,
+// and the buffer must hold them (past it lies a paged verification's page
+// list).
 int longest_unit(const vegas::HostPlan& hp) {
     int m = 0;
     if (hp.nwg > 0) {
@@ -222,7 +226,7 @@ int longest_unit(const vegas::HostPlan& hp) {
         for (int b = 0; b < hp.n; ++b)
             if (hp.first[b + 1] > hp.first[b]) m = std::max(m, std::min(hp.chunk[b], hp.len[b]));
     }
-    return m;
+    return (m + vegas::kAttnBlock - 1) / vegas::kAttnBlock * vegas::kAttnBlock;
 }
 
 // Host offsets: non-decreasing, within [0, total] (total < 0: no bound).
