@@ -278,6 +278,41 @@ def gather_read_ceiling(wl, layer_inputs, steps, reps=3):
                        "layer, 16-byte non-temporal direct-to-LDS copies, no arithmetic)")}
 
 
+def launch_floor(chain: int = 200, reps: int = 5):
+    """Cost of one kernel boundary in a chain of dependent launches on one stream
+    (libvegas_probe.so's empty chained kernel), for one workgroup and for one round of 256
+    workgroups holding 64 KB of LDS each (one per CU, as the attention kernels run): the floor
+    under each small dependent kernel of a pass."""
+    import ctypes
+    import torch
+    from verification_guided_sparse_verify_amd import build as B
+    if not os.path.exists(B.PROBE_LIB):
+        return None
+    probe = ctypes.CDLL(B.PROBE_LIB)
+    fn = probe.vegas_probe_launch_chain
+    fn.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, wgs, lds in (("one_workgroup", 1, 0), ("256_workgroups_64kb_lds", 256, 65536)):
+        times = []
+        for r in range(reps + 1):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            rc = fn(chain, wgs, lds, sink.data_ptr(), stream.cuda_stream)
+            b.record(stream)
+            if rc != 0:
+                raise RuntimeError(f"vegas_probe_launch_chain returned {rc}")
+            times.append((a, b))
+        torch.cuda.synchronize()
+        out[name] = round(statistics.median(x.elapsed_time(y) for x, y in times[1:]) * 1e3 / chain, 2)
+    out["unit"] = "us per dependent launch"
+    out["kernel"] = f"vegas_probe_launch_chain ({chain} chained launches of an empty kernel, median of {reps})"
+    return out
+
+
 def collect_sweep(base, gammas=(1, 3, 5, 7, 11, 15), reps=8):
     """Verification time of one layer of `base` (its prefix, heads and batch) with collection
     off, Collect-2-Query (rows 0 and gamma) and all gamma+1 rows, for several gamma.  The pages
@@ -782,6 +817,16 @@ def main():
             if gceil:
                 result["per_call_gbps"]["draft"]["frac_of_gather_ceiling"] = round(
                     result["per_call_gbps"]["draft"]["gbps"] / gceil["gbps"], 4)
+
+    floor = launch_floor()
+    if floor:
+        result["dependent_launch_floor"] = floor
+        if fused:
+            # the one call runs the combine with the selection's first step, then two selection
+            # launches (candidates, write): two kernel boundaries more than plain verification
+            f2 = 2 * floor["256_workgroups_64kb_lds"]
+            result["collect_select_launch_floor_us"] = round(f2, 2)
+            result["collect_select_launch_floor_vs_plain_verify"] = round(f2 / plain_us, 4)
 
     if cpu_leg:
         result["cpu_baseline"] = cpu_baseline(wl, layer_inputs, args.cpu_seconds)

@@ -46,6 +46,20 @@ int vegas_probe_gather_read(const void* k, const void* v, const int32_t* rows, i
                             int32_t row_bytes, int32_t slice_bytes, int32_t heads, int32_t workgroups,
                             int32_t blocks_in_flight, uint32_t* sink, void* stream);
 
+/*
+ * Dependent-launch floor: `launches` (1..100000) launches back to back on
+ * `stream` of a kernel with `workgroups` (1..4096) workgroups of 256 threads
+ * and lds_bytes (0..65536) of LDS each, that does no work except that its
+ * first thread increments sink[0] (device uint32 [1]), so each launch reads
+ * what the one before wrote.  The time of a long chain divided by `launches`
+ * is the cost of one kernel boundary in a chain of dependent launches on one
+ * stream (dispatch, workgroup start-up and drain, end-of-kernel cache
+ * write-back): the floor under each of a pass's small dependent kernels.
+ * Asynchronous.  Returns 0, -1 for invalid arguments (nothing launched), or
+ * the HIP error code of the last launch.
+ */
+int vegas_probe_launch_chain(int32_t launches, int32_t workgroups, int32_t lds_bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -280,9 +280,9 @@ def test_probe_library_exports_and_rejects_bad_arguments(V):
     from verification_guided_sparse_verify_amd import build as B
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "vegas_probe.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(vegas_[a-z_0-9]+)\s*\(", text)))
-    assert names == ["vegas_probe_gather_read", "vegas_probe_stream_read"]
+    assert names == ["vegas_probe_gather_read", "vegas_probe_launch_chain", "vegas_probe_stream_read"]
     nm = subprocess.run(["nm", "-D", "--defined-only", B.PROBE_LIB], capture_output=True, text=True).stdout
-    assert "vegas_probe_stream_read" in nm and "vegas_probe_gather_read" in nm
+    assert all(n in nm for n in names)
     fn = ctypes.CDLL(B.PROBE_LIB).vegas_probe_stream_read
     fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     unit = 32768 * 256
@@ -334,6 +334,20 @@ def test_gather_probe_rejects_bad_arguments(V):
     assert call(inflight=4) == -1
     assert call(n=300000, wgs=8) == -1         # more than 4096 entries per workgroup
     assert call(sink=None) == -1
+
+
+def test_launch_chain_probe_rejects_bad_arguments(V):
+    """The dependent-launch probe validates its arguments before launching anything."""
+    from verification_guided_sparse_verify_amd import build as B
+    fn = ctypes.CDLL(B.PROBE_LIB).vegas_probe_launch_chain
+    fn.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    assert fn(10, 256, 0, None, None) == -1         # no sink
+    assert fn(0, 256, 0, FAKE, None) == -1          # no launches
+    assert fn(100001, 256, 0, FAKE, None) == -1     # too long a chain
+    assert fn(10, 0, 0, FAKE, None) == -1           # no workgroups
+    assert fn(10, 4097, 0, FAKE, None) == -1
+    assert fn(10, 256, -1, FAKE, None) == -1        # LDS outside 0..65536
+    assert fn(10, 256, 65537, FAKE, None) == -1
 
 
 def test_trace_build_is_separate_from_the_product_library(V):

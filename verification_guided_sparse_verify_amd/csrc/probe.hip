@@ -1,5 +1,6 @@
-// Streaming-read ceiling probe (libvegas_probe.so): measurement only, shares
-// nothing with the Vegas kernels.  See include/vegas_probe.h.
+// Measurement probes (libvegas_probe.so): streaming and gathered read
+// ceilings and the dependent-launch floor; they share nothing with the Vegas
+// kernels.  See include/vegas_probe.h.
 #include <hip/hip_runtime.h>
 
 #include "vegas_probe.h"
@@ -99,7 +100,25 @@ __global__ void __launch_bounds__(kThreads) gather_read_kernel(const unsigned ch
     if (acc == 0u && lane == 0 && mine > 0 && blockIdx.x == 0x7fffffff) sink[0] = 1u;   // keeps the reads live
 }
 
+// A kernel that only hands one word to the next launch.
+__global__ void __launch_bounds__(kThreads) launch_chain_kernel(uint32_t* __restrict__ sink) {
+    extern __shared__ uint32_t chain_lds[];
+    if (blockIdx.x == 0 && threadIdx.x == 0) sink[0] = sink[0] + 1u;
+    (void)chain_lds;
+}
+
 }  // namespace
+
+extern "C" int vegas_probe_launch_chain(int32_t launches, int32_t workgroups, int32_t lds_bytes, uint32_t* sink,
+                                        void* stream) {
+    if (!sink || launches < 1 || launches > 100000 || workgroups < 1 || workgroups > 4096 || lds_bytes < 0 ||
+        lds_bytes > 65536)
+        return -1;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int i = 0; i < launches; ++i)
+        hipLaunchKernelGGL(launch_chain_kernel, dim3(workgroups), dim3(kThreads), (size_t)lds_bytes, st, sink);
+    return (int)hipGetLastError();
+}
 
 extern "C" int vegas_probe_gather_read(const void* k, const void* v, const int32_t* rows, int32_t n_rows,
                                        int32_t total_rows, int32_t row_bytes, int32_t slice_bytes, int32_t heads,
