@@ -695,11 +695,13 @@ __device__ __forceinline__ void split_unit(const AttnArgs& a, int g, int b, int 
     c.end = end;
 
     // This position group's blocks are pw, pw+kAttnWaves, ...; a ring of NST
-    // stages keeps NST-1 of them in flight.  A block past the last one is
-    // replaced by the last one (re-fetched, served by the caches) so that every
-    // iteration issues the same number of copies and the wait count stays exact.
-    // With the row split every wave runs the same number of iterations (its
-    // barriers must match); the extra ones compute nothing.
+    // stages keeps NST-1 of them in flight.  No copy goes past the group's last
+    // block, so the wait at the top of iteration jj counts the copies of the
+    // blocks after jj that were issued: those of block jj+1 with a three-stage
+    // ring unless jj is the last block, none otherwise.  With the row split
+    // every wave runs the same number of iterations (its barriers must match);
+    // the extra ones compute and copy nothing.
+    static_assert(NST == 2 || NST == 3, "the waits below count one or two stages");
     const int nblk = (end - start + kAttnBlock - 1) / kAttnBlock;
     const int nmine = pw < nblk ? (nblk - pw + kAttnWaves - 1) / kAttnWaves : 0;
     const int nloop = RS == 1 ? nmine : (nblk + kAttnWaves - 1) / kAttnWaves;
@@ -713,10 +715,9 @@ __device__ __forceinline__ void split_unit(const AttnArgs& a, int g, int b, int 
             else issue_block<GEO, GATHER, 2>(c, block_pos(jj), lane, stage);
         }
     };
-    if (nmine > 0) {
 #pragma unroll
-        for (int st = 0; st < NST - 1; ++st) issue(st, ring + st * GEO::STAGE);
-    }
+    for (int st = 0; st < NST - 1; ++st)
+        if (st < nmine) issue(st, ring + st * GEO::STAGE);
     // Retire the Q loads here, where the compiler can see it (its wait also
     // covers the first blocks' copies, issued after them), so that its own
     // wait for them is not placed inside the block loop.
@@ -728,7 +729,9 @@ __device__ __forceinline__ void split_unit(const AttnArgs& a, int g, int b, int 
             if (!ws.qvalid[qb]) ws.qf[qb][ch] = zero_frag<BF16>();
         }
     for (int jj = 0; jj < nloop; ++jj) {
-        wait_vmem<(NST - 2) * OPS>();                     // this wave's copies of block jj have landed
+        // this wave's copies of block jj have landed
+        if (NST == 3 && jj + 1 < nmine) wait_vmem<(NST - 2) * OPS>();
+        else wait_vmem<0>();
         if constexpr (RS > 1) {
             __syncthreads();                              // ... and its partner's; stage jj-1 is free
             if constexpr (COLLECT) {                      // the second half's part of block jj-1
@@ -736,7 +739,7 @@ __device__ __forceinline__ void split_unit(const AttnArgs& a, int g, int b, int 
                 ws.pend_idx = -1;
             }
         }
-        if (nmine > 0) issue(jj + NST - 1, ring + ((jj + NST - 1) % NST) * GEO::STAGE);
+        if (jj + NST - 1 < nmine) issue(jj + NST - 1, ring + ((jj + NST - 1) % NST) * GEO::STAGE);
         if (jj < nmine) {
             if (RS > 1 && rh == 1)
                 compute_block<GEO, BF16, D, MBW, GATHER, COLLECT, true>(a, ws, block_pos(jj), L, end, start, lane,
