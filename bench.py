@@ -56,27 +56,35 @@ def algorithmic_bytes(wl):
             "layer_step": verify + select + wl.n_drafts * draft}
 
 
+def product_code_lines(text):
+    """The lines of a kernel source that the product build compiles, without comments, blank
+    lines and the measurement-only VEGAS_PHASE_TRACE branches (their #else branches stay)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    state = ""                         # "trace": inside the trace branch; "else": in its #else branch
+    out = []
+    for ln in text.splitlines():
+        code = re.sub(r"//.*", "", ln).strip()
+        if code == "#ifdef VEGAS_PHASE_TRACE":
+            state = "trace"
+            continue
+        if state and code == "#else":
+            state = "else"
+            continue
+        if state and code == "#endif":
+            state = ""
+            continue
+        if code and state != "trace":
+            out.append(code)
+    return out
+
+
 def kernel_source_hash():
-    """Hash of the attention kernels' source with comments, blank lines and the measurement-only
-    VEGAS_PHASE_TRACE blocks removed (a change of comments or of the trace build alone leaves the
-    product kernels, and so the counters, as they were)."""
+    """Hash of the attention kernels' product code (product_code_lines): a change of comments or
+    of the trace build alone leaves the product kernels, and so the counters, as they were."""
     h = hashlib.sha256()
     for f in ("attn.hip", "internal.h", "select_device.h"):
         with open(os.path.join(ROOT, "verification_guided_sparse_verify_amd", "csrc", f)) as fh:
-            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
-        state = ""                     # "trace": inside the trace branch; "else": in its #else branch
-        for ln in text.splitlines():
-            code = re.sub(r"//.*", "", ln).strip()
-            if code == "#ifdef VEGAS_PHASE_TRACE":
-                state = "trace"
-                continue
-            if state and code == "#else":
-                state = "else"
-                continue
-            if state and code == "#endif":
-                state = ""
-                continue
-            if code and state != "trace":
+            for code in product_code_lines(fh.read()):
                 h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
