@@ -64,7 +64,6 @@ AttnPlan plan_attn(bool bf16, int batch, int hkv, int M, int head_dim, int max_n
                    int page_size = 0) {
     AttnPlan p;
     p.mb = (M + 15) / 16;
-    if (!gather && p.mb == 3) p.mb = 4;   // verification runs 3-4 row tiles as two halves of 2
     const int unit = vegas::kAttnWaves * vegas::kAttnBlock;
     const int64_t n = max_n > 0 ? max_n : 1;
     // Both caps are multiples of `unit`.  Verification uses the same plan with
@@ -105,7 +104,6 @@ void balance_plan(const AttnPlan& plan, int batch, const int* len, const int* ns
                   vegas::HostPlan* hp) {
     constexpr int unit = vegas::kAttnWaves * vegas::kAttnBlock;
     constexpr int64_t kUnitCost = 512;
-    if (plan.mb > 2) return;   // 3-4 row tiles: row-split workgroups, one unit each
     int64_t prop_max = 0;
     for (int b = 0; b < batch; ++b)
         for (int i = 0; i < ns[b]; ++i)

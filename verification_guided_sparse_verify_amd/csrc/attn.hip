@@ -16,8 +16,7 @@
 // rows.  The four waves take 16-position blocks in turn; each wave streams its
 // blocks through a private two-stage LDS ring filled by the load-to-LDS path
 // (no VGPR round trip), computing one block while the next is in flight.
-// (With 3-4 row tiles, eight waves split the rows in two halves per position
-// group: see attn_split_kernel.)  Per block and wave:
+// A wave holds all the row tiles (up to four).  Per block and wave:
 //   S^T[pos, row] = K[pos, :] . Q[row, :]          16x16x32 bf16 MFMA; K from
 //                                                   the ring, Q in registers
 //   collection (verification only)                 collected rows summed over
@@ -264,30 +263,24 @@ __device__ __forceinline__ uint64_t row_offset(const SplitCtx& c, int p) {
 // lanes reading one chunk column of 16 rows hit distinct banks); V chunks are
 // XORed with the row's 4-row group (so the transposed reads, four lane groups
 // on rows 4 apart, hit distinct banks).
-// PART selects the tiles this wave copies: 3 both, 1 the K tile, 2 the V tile
-// (a row-split workgroup's two waves of a position group share the copies).
-template <class GEO, bool GATHER, int PART = 3>
+template <class GEO, bool GATHER>
 __device__ __forceinline__ void issue_block(const SplitCtx& c, int p0, int lane, unsigned char* stage) {
     // All row offsets first (in gather mode, LDS reads of the index list that
     // then complete together), then the copies back to back.
     uint64_t off[GEO::TLD];
 #pragma unroll
     for (int i = 0; i < GEO::TLD; ++i) off[i] = row_offset<GATHER>(c, p0 + i * GEO::RPI + lane / GEO::CPR);
-    if constexpr ((PART & 1) != 0) {
 #pragma unroll
-        for (int i = 0; i < GEO::TLD; ++i) {
-            const int row = i * GEO::RPI + lane / GEO::CPR;
-            const int cc = (lane % GEO::CPR) ^ (row & GEO::KSWZ);
-            copy16_to_lds(c.kbase + off[i] + cc * 16, stage + i * 1024);
-        }
+    for (int i = 0; i < GEO::TLD; ++i) {
+        const int row = i * GEO::RPI + lane / GEO::CPR;
+        const int cc = (lane % GEO::CPR) ^ (row & GEO::KSWZ);
+        copy16_to_lds(c.kbase + off[i] + cc * 16, stage + i * 1024);
     }
-    if constexpr ((PART & 2) != 0) {
 #pragma unroll
-        for (int i = 0; i < GEO::TLD; ++i) {
-            const int row = i * GEO::RPI + lane / GEO::CPR;
-            const int cc = (lane % GEO::CPR) ^ (GEO::SWZU * ((row >> 2) & 3));
-            copy16_to_lds(c.vbase + off[i] + cc * 16, stage + GEO::TILE + i * 1024);
-        }
+    for (int i = 0; i < GEO::TLD; ++i) {
+        const int row = i * GEO::RPI + lane / GEO::CPR;
+        const int cc = (lane % GEO::CPR) ^ (GEO::SWZU * ((row >> 2) & 3));
+        copy16_to_lds(c.vbase + off[i] + cc * 16, stage + GEO::TILE + i * 1024);
     }
 }
 
@@ -418,10 +411,6 @@ struct WaveState {
     int rrow[MB];
     float m_run[MB], l_run[MB];
     f32x4_t o[D / 16][MB];
-    // Row split: this wave's partial collected score of its last block, added
-    // to the LDS buffer after the next workgroup barrier (idx -1: none).
-    float pend_val;
-    int pend_idx;
 };
 
 // PV step (fp32): acc += V^T(16 d x 16 pos) . P^T(16 pos x 16 rows).  Lane
@@ -434,7 +423,7 @@ __device__ __forceinline__ f32x4_t mfma_pv(const uint32_t (&vt)[4], const float 
 }
 
 // One 16-position block: S^T, collection, mask, online softmax, O^T += V^T P^T.
-template <class GEO, bool BF16, int D, int MB, bool GATHER, bool COLLECT, bool HOLD = false>
+template <class GEO, bool BF16, int D, int MB, bool GATHER, bool COLLECT>
 __device__ __forceinline__ void compute_block(const AttnArgs& a, WaveState<BF16, D, MB>& ws, int p0, int L,
                                               int end, int start, int lane, const unsigned char* stage,
                                               float* score_s) {
@@ -476,13 +465,7 @@ __device__ __forceinline__ void compute_block(const AttnArgs& a, WaveState<BF16,
             }
             const float sum = row16_sum4(x, lr);      // position 4*lg + lr/4 of the block
             if ((lr & 3) == 0) {
-                const int idx = p0 - start + 4 * lg + (lr >> 2);
-                if constexpr (HOLD) {
-                    ws.pend_val = a.scale * sum;
-                    ws.pend_idx = idx;
-                } else {
-                    score_s[idx] = a.scale * sum;
-                }
+                score_s[p0 - start + 4 * lg + (lr >> 2)] = a.scale * sum;
             }
         }
     }
@@ -586,44 +569,33 @@ __device__ __forceinline__ void compute_block(const AttnArgs& a, WaveState<BF16,
     lds_fence();   // this stage's reads are done before it is refilled
 }
 
-// RS = 2 (row split, verification with 3-4 row tiles): eight waves, two per
-// position group; wave (pw, rh) takes blocks pw, pw + kAttnWaves, ... and the
-// row tiles rh*MBW .. rh*MBW + MBW - 1.  The two waves of a position group
-// share one ring (one copies the K tile, the other the V tile) and every
-// block iteration ends its waits with a workgroup barrier.  Two waves per SIMD
-// then overlap one wave's MFMA with the other's softmax arithmetic.
 // One unit of the split kernel: positions [start, end) of sequence b (span
 // sp; under a local mask no row sees a key before row 0's band, sp.lo) for KV
 // head g and all query rows of the KV head.  The unit's partial goes to slot
 // `slot` of (b, g).  Called by whole workgroups (every branch on its
 // arguments is uniform); the LDS arrays are the kernel's.
-template <bool BF16, int D, int MB, bool GATHER, bool COLLECT, int RS>
+template <bool BF16, int D, int MB, bool GATHER, bool COLLECT>
 __device__ __forceinline__ void split_unit(const AttnArgs& a, int g, int b, int slot, int start, int end,
                                            const SeqSpan& sp, unsigned char* smem, int* idx_s, int* page_s,
                                            float* score_s) {
-    constexpr int MBW = MB / RS;                  // row tiles per wave
-    constexpr int NT = kAttnWaves * RS * 64;      // threads
-    using GEO = Geo<BF16, D, MBW>;
+    constexpr int NT = kAttnWaves * 64;           // threads
+    using GEO = Geo<BF16, D, MB>;
     using T = typename std::conditional<BF16, uint16_t, float>::type;
     constexpr int DC = GEO::DC, DB = GEO::DB, NREG = GEO::NREG, NST = GEO::NST;
-    constexpr int OPS = GEO::BLOCK_OPS / RS;      // copies one wave issues per block
+    constexpr int OPS = GEO::BLOCK_OPS;           // copies one wave issues per block
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int pw = wave % kAttnWaves;             // position group
-    const int rh = wave / kAttnWaves;             // row half (0 unless RS = 2)
+    const int pw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // position group (wave)
     const int lr = lane & 15;
     const int lg = lane >> 4;
     const int seq0 = sp.seq0, n_b = sp.n_b, L = sp.L, ib0 = sp.ib0;
     if (n_b <= 0 || start >= end) return;                         // uniform per workgroup
 
 
-    WaveState<BF16, D, MBW> ws;
-    ws.pend_idx = -1;
-    ws.pend_val = 0.f;
+    WaveState<BF16, D, MB> ws;
 #pragma unroll
-    for (int qb = 0; qb < MBW; ++qb) {
-        // B operand of S^T: query row 16*(rh*MBW + qb) + lane%16, elements 32*ch + 8*(lane/16) .. +7
-        const int j = 16 * (rh * MBW + qb) + lr;
+    for (int qb = 0; qb < MB; ++qb) {
+        // B operand of S^T: query row 16*qb + lane%16, elements 32*ch + 8*(lane/16) .. +7
+        const int j = 16 * qb + lr;
         const bool valid = j < a.M;
         const int r = valid ? j / a.G : a.W - 1;
         const int hl = valid ? j % a.G : 0;
@@ -698,23 +670,13 @@ __device__ __forceinline__ void split_unit(const AttnArgs& a, int g, int b, int 
     // stages keeps NST-1 of them in flight.  No copy goes past the group's last
     // block, so the wait at the top of iteration jj counts the copies of the
     // blocks after jj that were issued: those of block jj+1 with a three-stage
-    // ring unless jj is the last block, none otherwise.  With the row split
-    // every wave runs the same number of iterations (its barriers must match);
-    // the extra ones compute and copy nothing.
+    // ring unless jj is the last block, none otherwise.
     static_assert(NST == 2 || NST == 3, "the waits below count one or two stages");
     const int nblk = (end - start + kAttnBlock - 1) / kAttnBlock;
     const int nmine = pw < nblk ? (nblk - pw + kAttnWaves - 1) / kAttnWaves : 0;
-    const int nloop = RS == 1 ? nmine : (nblk + kAttnWaves - 1) / kAttnWaves;
     unsigned char* ring = smem + pw * (NST * GEO::STAGE);
     auto block_pos = [&](int jj) { return start + (pw + kAttnWaves * min(jj, nmine - 1)) * kAttnBlock; };
-    auto issue = [&](int jj, unsigned char* stage) {
-        if constexpr (RS == 1) {
-            issue_block<GEO, GATHER, 3>(c, block_pos(jj), lane, stage);
-        } else {
-            if (rh == 0) issue_block<GEO, GATHER, 1>(c, block_pos(jj), lane, stage);
-            else issue_block<GEO, GATHER, 2>(c, block_pos(jj), lane, stage);
-        }
-    };
+    auto issue = [&](int jj, unsigned char* stage) { issue_block<GEO, GATHER>(c, block_pos(jj), lane, stage); };
 #pragma unroll
     for (int st = 0; st < NST - 1; ++st)
         if (st < nmine) issue(st, ring + st * GEO::STAGE);
@@ -722,32 +684,19 @@ __device__ __forceinline__ void split_unit(const AttnArgs& a, int g, int b, int 
     // covers the first blocks' copies, issued after them), so that its own
     // wait for them is not placed inside the block loop.
 #pragma unroll
-    for (int qb = 0; qb < MBW; ++qb)
+    for (int qb = 0; qb < MB; ++qb)
 #pragma unroll
         for (int ch = 0; ch < DC; ++ch) {
             keep_live(ws.qf[qb][ch]);
             if (!ws.qvalid[qb]) ws.qf[qb][ch] = zero_frag<BF16>();
         }
-    for (int jj = 0; jj < nloop; ++jj) {
+    for (int jj = 0; jj < nmine; ++jj) {
         // this wave's copies of block jj have landed
         if (NST == 3 && jj + 1 < nmine) wait_vmem<(NST - 2) * OPS>();
         else wait_vmem<0>();
-        if constexpr (RS > 1) {
-            __syncthreads();                              // ... and its partner's; stage jj-1 is free
-            if constexpr (COLLECT) {                      // the second half's part of block jj-1
-                if (rh == 1 && ws.pend_idx >= 0) score_s[ws.pend_idx] += ws.pend_val;
-                ws.pend_idx = -1;
-            }
-        }
         if (jj + NST - 1 < nmine) issue(jj + NST - 1, ring + ((jj + NST - 1) % NST) * GEO::STAGE);
-        if (jj < nmine) {
-            if (RS > 1 && rh == 1)
-                compute_block<GEO, BF16, D, MBW, GATHER, COLLECT, true>(a, ws, block_pos(jj), L, end, start, lane,
-                                                                        ring + (jj % NST) * GEO::STAGE, score_s);
-            else
-                compute_block<GEO, BF16, D, MBW, GATHER, COLLECT, false>(a, ws, block_pos(jj), L, end, start, lane,
-                                                                         ring + (jj % NST) * GEO::STAGE, score_s);
-        }
+        compute_block<GEO, BF16, D, MB, GATHER, COLLECT>(a, ws, block_pos(jj), L, end, start, lane,
+                                                         ring + (jj % NST) * GEO::STAGE, score_s);
     }
     wait_vmem<0>();
 #ifdef VEGAS_PHASE_TRACE
@@ -756,17 +705,14 @@ __device__ __forceinline__ void split_unit(const AttnArgs& a, int g, int b, int 
 
     // Row sums: each lane summed its own positions.
 #pragma unroll
-    for (int qb = 0; qb < MBW; ++qb) {
+    for (int qb = 0; qb < MB; ++qb) {
         ws.l_run[qb] = pair32_sum(pair16_sum(ws.l_run[qb]));
     }
 
     // Tree merge of the position groups' (m, l, O) through LDS, in fragment
-    // order, one tree per row half.
+    // order.
     __syncthreads();
-    if constexpr (RS > 1 && COLLECT) {                    // the second half's part of its last block
-        if (rh == 1 && ws.pend_idx >= 0) score_s[ws.pend_idx] += ws.pend_val;
-    }
-    float* fs = reinterpret_cast<float*>(smem) + rh * (kAttnWaves / 2) * (GEO::MSLOT / 4);
+    float* fs = reinterpret_cast<float*>(smem);
     constexpr int SLOTF = GEO::MSLOT / 4;
 #pragma unroll
     for (int half = kAttnWaves / 2; half >= 1; half >>= 1) {
@@ -775,21 +721,21 @@ __device__ __forceinline__ void split_unit(const AttnArgs& a, int g, int b, int 
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int qb = 0; qb < MBW; ++qb)
-                    *reinterpret_cast<f32x4_t*>(slot + ((db * MBW + qb) * 64 + lane) * 4) = ws.o[db][qb];
+                for (int qb = 0; qb < MB; ++qb)
+                    *reinterpret_cast<f32x4_t*>(slot + ((db * MB + qb) * 64 + lane) * 4) = ws.o[db][qb];
 #pragma unroll
-            for (int qb = 0; qb < MBW; ++qb) {
+            for (int qb = 0; qb < MB; ++qb) {
                 slot[NREG * 256 + qb * 64 + lane] = ws.m_run[qb];
-                slot[NREG * 256 + (MBW + qb) * 64 + lane] = ws.l_run[qb];
+                slot[NREG * 256 + (MB + qb) * 64 + lane] = ws.l_run[qb];
             }
         }
         __syncthreads();
         if (pw < half) {
             const float* slot = fs + pw * SLOTF;
 #pragma unroll
-            for (int qb = 0; qb < MBW; ++qb) {
+            for (int qb = 0; qb < MB; ++qb) {
                 const float mb = slot[NREG * 256 + qb * 64 + lane];
-                const float lb = slot[NREG * 256 + (MBW + qb) * 64 + lane];
+                const float lb = slot[NREG * 256 + (MB + qb) * 64 + lane];
                 const float mm = fmaxf(ws.m_run[qb], mb);
                 if (mm != kNegInf) {
                     const float ca = fast_exp2(ws.m_run[qb] - mm);
@@ -799,7 +745,7 @@ __device__ __forceinline__ void split_unit(const AttnArgs& a, int g, int b, int 
 #pragma unroll
                     for (int db = 0; db < DB; ++db) {
                         const f32x4_t ob =
-                            *reinterpret_cast<const f32x4_t*>(slot + ((db * MBW + qb) * 64 + lane) * 4);
+                            *reinterpret_cast<const f32x4_t*>(slot + ((db * MB + qb) * 64 + lane) * 4);
                         ws.o[db][qb] = ca * ws.o[db][qb] + cb * ob;
                     }
                 }
@@ -815,12 +761,11 @@ __device__ __forceinline__ void split_unit(const AttnArgs& a, int g, int b, int 
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int qb = 0; qb < MBW; ++qb) po[((db * MB + rh * MBW + qb) * 4 + lg) * prow + lr] = ws.o[db][qb];
+            for (int qb = 0; qb < MB; ++qb) po[((db * MB + qb) * 4 + lg) * prow + lr] = ws.o[db][qb];
         if (lg == 0) {
 #pragma unroll
-            for (int qb = 0; qb < MBW; ++qb) {
-                float2* pml =
-                    reinterpret_cast<float2*>(a.part_ml) + slot_i * (MB * prow) + (rh * MBW + qb) * prow + lr;
+            for (int qb = 0; qb < MB; ++qb) {
+                float2* pml = reinterpret_cast<float2*>(a.part_ml) + slot_i * (MB * prow) + qb * prow + lr;
                 *pml = make_float2(ws.m_run[qb], ws.l_run[qb]);
             }
         }
@@ -844,14 +789,13 @@ __device__ __forceinline__ void split_unit(const AttnArgs& a, int g, int b, int 
     }
 }
 
-template <bool BF16, int D, int MB, bool GATHER, bool COLLECT, int RS>
-__global__ void __launch_bounds__(kAttnWaves * RS * 64)
+template <bool BF16, int D, int MB, bool GATHER, bool COLLECT>
+__global__ void __launch_bounds__(kAttnWaves * 64)
 attn_split_kernel(const AttnArgs a) {
-    static_assert(MB % RS == 0 && (RS == 1 || (RS == 2 && !GATHER)), "row split: verification, even tile count");
-    constexpr int NT = kAttnWaves * RS * 64;      // threads
+    constexpr int NT = kAttnWaves * 64;           // threads
     constexpr int NWV = NT / 64;                  // waves
-    using GEO = Geo<BF16, D, MB / RS>;
-    constexpr int MERGE = RS * (kAttnWaves / 2) * GEO::MSLOT;
+    using GEO = Geo<BF16, D, MB>;
+    constexpr int MERGE = (kAttnWaves / 2) * GEO::MSLOT;
     constexpr int MAIN = GEO::RING > MERGE ? GEO::RING : MERGE;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[MAIN];
@@ -891,7 +835,7 @@ attn_split_kernel(const AttnArgs a) {
     int k0 = 0, nunits = 1;
     int b = 0, split = 0, chunk = 0;
     SeqSpan sp{};
-    if (RS == 1 && a.hp.nwg > 0) {
+    if (a.hp.nwg > 0) {
         k0 = a.hp.wg_first[unit_id];
         nunits = a.hp.wg_first[unit_id + 1] - k0;
     } else if (a.hp.n > 0) {
@@ -951,33 +895,23 @@ attn_split_kernel(const AttnArgs a) {
         chunk = __builtin_amdgcn_readfirstlane(plan_s[2]);
         sp = seq_span<GATHER>(a, b);
     }
-    if constexpr (RS > 1) {
-        // Row-split workgroups run one unit (the host never gives them a unit
-        // table): the unit loop would push the two-waves-per-SIMD kernel past
-        // its registers.
-        const int start = sp.lo + split * chunk;
-        split_unit<BF16, D, MB, GATHER, COLLECT, RS>(a, g, b, split, start, min(start + chunk, sp.lo + sp.len), sp,
-                                                     smem, idx_s, page_s, score_s);
-    } else {
-        for (int i = 0; i < nunits; ++i) {
-            int slot = split, start = sp.lo + split * chunk, end = min(start + chunk, sp.lo + sp.len);
-            if (a.hp.nwg > 0) {
-                const int k = k0 + i;
-                b = a.hp.u_bs[k] & 31;
-                slot = a.hp.u_bs[k] >> 5;
-                start = a.hp.u_start[k];
-                end = a.hp.u_end[k];
-                sp.seq0 = a.hp.seq0[b];
-                sp.n_b = a.hp.n_b[b];
-                sp.L = a.hp.L[b];
-                sp.lo = a.hp.lo[b];
-                sp.len = a.hp.len[b];
-                sp.ib0 = a.hp.ib0[b];
-                if (i > 0) __syncthreads();                       // the previous unit's LDS reads are done
-            }
-            split_unit<BF16, D, MB, GATHER, COLLECT, RS>(a, g, b, slot, start, end, sp, smem, idx_s, page_s,
-                                                         score_s);
+    for (int i = 0; i < nunits; ++i) {
+        int slot = split, start = sp.lo + split * chunk, end = min(start + chunk, sp.lo + sp.len);
+        if (a.hp.nwg > 0) {
+            const int k = k0 + i;
+            b = a.hp.u_bs[k] & 31;
+            slot = a.hp.u_bs[k] >> 5;
+            start = a.hp.u_start[k];
+            end = a.hp.u_end[k];
+            sp.seq0 = a.hp.seq0[b];
+            sp.n_b = a.hp.n_b[b];
+            sp.L = a.hp.L[b];
+            sp.lo = a.hp.lo[b];
+            sp.len = a.hp.len[b];
+            sp.ib0 = a.hp.ib0[b];
+            if (i > 0) __syncthreads();                           // the previous unit's LDS reads are done
         }
+        split_unit<BF16, D, MB, GATHER, COLLECT>(a, g, b, slot, start, end, sp, smem, idx_s, page_s, score_s);
     }
 #ifdef VEGAS_PHASE_TRACE
     if (threadIdx.x == 0 && blockIdx.x < kTraceMax) {
@@ -1104,7 +1038,7 @@ __global__ void __launch_bounds__(kCombineWaves * 64) attn_combine_kernel(const 
     }
 }
 
-template <bool BF16, int D, int MB, bool GATHER, bool COLLECT, int RS = 1>
+template <bool BF16, int D, int MB, bool GATHER, bool COLLECT>
 hipError_t launch_t(const AttnArgs& a, hipStream_t stream, const SelectArgs* sel) {
     // (a host plan knows the exact workgroup count; the device plan's grid is its bound)
     const int per_head = a.hp.nwg > 0 ? a.hp.nwg : (a.hp.n > 0 ? a.hp.first[a.hp.n] : a.max_units);
@@ -1113,8 +1047,8 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream, const SelectArgs* sel
     const size_t dyn = (COLLECT ? attn_score_lds_bytes(a.score_cap) : 0) +
                        (!GATHER && a.page_shift >= 0 ? kMaxPagesPerSplit * sizeof(int) : 0);
     if (split_grid > 0)
-        hipLaunchKernelGGL((attn_split_kernel<BF16, D, MB, GATHER, COLLECT, RS>), dim3(split_grid),
-                           dim3(kAttnWaves * RS * 64), dyn, stream, a);
+        hipLaunchKernelGGL((attn_split_kernel<BF16, D, MB, GATHER, COLLECT>), dim3(split_grid),
+                           dim3(kAttnWaves * 64), dyn, stream, a);
     if (comb_grid > 0) {
         if constexpr (COLLECT && !GATHER) {
             if (sel) {
@@ -1133,21 +1067,12 @@ template <bool BF16, int D, bool GATHER, bool COLLECT>
 hipError_t launch_mb(const AttnArgs& a, int mb, hipStream_t s, const SelectArgs* sel) {
     if (mb == 1) return launch_t<BF16, D, 1, GATHER, COLLECT>(a, s, sel);
     if (mb == 2) return launch_t<BF16, D, 2, GATHER, COLLECT>(a, s, sel);
-    // fp32 at D = 128 stops at 32 rows per KV head (LDS budget).  Verification
-    // with more than 32 rows runs 4 row tiles as two halves of 2 (the host
-    // rounds 3 tiles up to 4); gathering has one query row per head and keeps
-    // one wave per position group.
+    // fp32 at D = 128 stops at 32 rows per KV head (LDS budget).  Three and
+    // four row tiles keep one wave per position group with all the tiles in
+    // its registers (at most 256 VGPRs + 198 AGPRs, bf16 at D = 128).
     if constexpr (BF16 || D == 64) {
-        if constexpr (GATHER) {
-            if (mb == 3) return launch_t<BF16, D, 3, GATHER, COLLECT>(a, s, sel);
-            if (mb == 4) return launch_t<BF16, D, 4, GATHER, COLLECT>(a, s, sel);
-        } else {
-            // Plain verification (collect_mask 0) runs the collecting kernel too:
-            // with no row collected it computes the same attention, and at
-            // this shape it measured faster than the kernel compiled without
-            // the collection step (Qwen3-32B-shaped layer: 417 against 440 us).
-            if (mb == 4) return launch_t<BF16, D, 4, GATHER, true, 2>(a, s, sel);
-        }
+        if (mb == 3) return launch_t<BF16, D, 3, GATHER, COLLECT>(a, s, sel);
+        if (mb == 4) return launch_t<BF16, D, 4, GATHER, COLLECT>(a, s, sel);
     }
     return hipErrorInvalidValue;
 }
