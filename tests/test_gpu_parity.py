@@ -55,10 +55,12 @@ SWEEP = [
     ("bf16", 1, 64, 8, 128, 6, [2000], Fraction(10, 100)),
     ("bf16", 4, 32, 8, 128, 4, [3000, 1, 200, 9999], Fraction(5, 100)),
     ("bf16", 2, 16, 8, 64, 3, [777, 12000], Fraction(1)),
-    # 40 and 56 query rows per KV head: the row-split verification (3 tiles padded to 4)
+    # 40, 48 and 56 query rows per KV head: three and four row tiles held by one wave
     ("bf16", 2, 64, 8, 64, 4, [3000, 517], Fraction(5, 100)),
     ("f32", 1, 64, 8, 64, 6, [900], Fraction(5, 100)),
     ("bf16", 3, 64, 8, 128, 6, [5000, 64, 2047], Fraction(5, 100)),
+    ("bf16", 2, 32, 4, 128, 4, [2500, 4100], Fraction(5, 100)),
+    ("f32", 2, 32, 4, 64, 5, [1500, 33], Fraction(5, 100)),
 ]
 
 
@@ -633,6 +635,9 @@ HOSTPLAN_CASES = FUSED_CASES + [
     ("bf16", 12, 64, 8, 64, 3, [1705, 6093, 6444, 35657, 19991, 18445, 12287, 1781, 29032, 4948, 8582, 1443],
      Fraction(5, 100)),
     ("f32", 12, 32, 8, 64, 3, [2361, 4845, 2222, 5051, 10012, 14071, 2837, 4297, 2075, 28095, 3332, 37128],
+     Fraction(5, 100)),
+    # the same balancing with four row tiles per KV head (56 rows)
+    ("bf16", 12, 64, 8, 128, 6, [1705, 6093, 6444, 35657, 19991, 18445, 12287, 1781, 29032, 4948, 8582, 1443],
      Fraction(5, 100)),
 ]
 
