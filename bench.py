@@ -625,10 +625,15 @@ def main():
             sink[kind].append((a, b))
 
         halves = overlap and not single_stream and call_events is None
-        for li, (verify, _, select, _) in enumerate(bound):
+        for li, (verify, verify_plain, select, _) in enumerate(bound):
             if call_events is not None:
+                # separate calls, then plain verification and the one call on the same layer, so that
+                # the collection + selection overhead compares calls made in the same conditions
                 timed("verify", verify, call_events)
                 timed("select", select, call_events)
+                timed("plain", verify_plain, call_events)
+                if fused:
+                    timed("one_call", fused_calls[li], call_events)
                 continue
             head = begin_calls[li] if halves else (fused_calls[li] if fused else verify)
             if head_events is not None:
@@ -690,11 +695,13 @@ def main():
         torch.cuda.synchronize()
 
     # Per-call breakdown, outside the timed region: more steps with events around every call.
-    call_pairs = {"verify": [], "select": [], "draft": []}
+    call_pairs = {"verify": [], "select": [], "draft": [], "plain": [], "one_call": []}
     for _ in range(max(2, 12 // layers)):          # at least a dozen calls of each kind
         one_step(call_events=call_pairs)
     torch.cuda.synchronize()
-    per = {k: [a.elapsed_time(b) * 1e3 for a, b in v] for k, v in call_pairs.items()}   # microseconds
+    per = {k: [a.elapsed_time(b) * 1e3 for a, b in v] for k, v in call_pairs.items() if v}   # microseconds
+    plain_us = statistics.fmean(per.pop("plain"))
+    one_call_us = statistics.fmean(per.pop("one_call")) if fused else None
     mean = {k: statistics.fmean(v) for k, v in per.items()}
     med = {k: statistics.median(v) for k, v in per.items()}
 
@@ -790,22 +797,14 @@ def main():
     result["config"]["split_plan"] = ("host (host copies of the offsets, computed per call)" if host_plan
                                       else "device")
 
-    # Plain verification (collection off) on the same layers, for the collection + select overhead.
-    plain = []
-    for _ in range(max(3, 12 // layers)):
-        for _, verify_plain, _, _ in bound:
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            verify_plain()
-            b.record(stream)
-            plain.append((a, b))
-    torch.cuda.synchronize()
-    plain_us = statistics.fmean(a.elapsed_time(b) * 1e3 for a, b in plain)
+    # Plain verification (collection off) was timed in the breakdown steps, layer by layer next to
+    # the separate calls and the one call, for the collection + select overhead.
     result["plain_verify_us"] = round(plain_us, 2)
     separate = (mean["verify"] + mean["select"]) / plain_us - 1
     result["collect_select_overhead_vs_plain_verify"] = round(
-        (mean["verify_select"] if fused else verify_mean + mean["select"]) / plain_us - 1, 4)
+        (one_call_us if fused else verify_mean + mean["select"]) / plain_us - 1, 4)
+    if fused:
+        result["one_call_breakdown_us"] = round(one_call_us, 2)
     result["collect_select_overhead_separate_calls"] = round(separate, 4)
     # Achieved algorithmic bandwidth of each of the three calls (per-call means of the breakdown).
     result["per_call_gbps"] = {
