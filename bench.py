@@ -13,6 +13,10 @@ halves: the selection of layer l (keys, candidates, write) goes to a second
 stream, beside the verification of layer l+1 (the selected positions are used
 only by the drafting passes, which wait for each layer's selection).
 
+Each step of several layers ends with a synchronisation, as a decoding loop's
+iteration does: the next iteration's host-planned calls take host copies of
+sequence lengths that depend on the tokens this iteration accepts.
+
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
 The timed region runs the steps with no timing events (an event around every
 call adds ~7 us per layer-step).  Further steps after it, with HIP events on
@@ -519,6 +523,11 @@ def main():
                          "a workload of several layers runs the selection's last steps of layer l on a second "
                          "stream beside the verification of layer l+1; the single-stream figure is reported in "
                          "any case)")
+    ap.add_argument("--no-step-sync", action="store_true",
+                    help="let the host queue the next step before the GPU has finished the previous one (by "
+                         "default a step of several layers, one decoding iteration, ends with a synchronisation: "
+                         "the host-planned calls of the next iteration take host copies of sequence lengths that "
+                         "depend on this iteration's accepted tokens)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--page-size", type=int, default=0,
                     help="keep every layer's KV cache as a randomly permuted page pool of this page size and "
@@ -667,11 +676,30 @@ def main():
     # The timed region runs the steps alone: timing events around every call would add ~7 us
     # per layer-step (each timed event waits for the work before it); the per-call durations
     # come from instrumented steps after it.
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        one_step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    # A step of several layers is one decoding iteration: the host plans the next iteration's calls
+    # from sequence lengths that depend on this iteration's accepted tokens, so it waits for the
+    # step to finish before queueing the next one. (A one-layer workload stands for one layer of
+    # such an iteration, whose next layer would follow without a host round trip.)
+    step_sync = layers > 1 and not args.no_step_sync
+
+    def timed_steps(n, **kw):
+        t = time.perf_counter()
+        for _ in range(n):
+            one_step(**kw)
+            if step_sync:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t
+
+    elapsed = timed_steps(args.steps)
+    # The same steps with the host queueing ahead of the GPU, for comparison.
+    elapsed_ahead = None
+    if step_sync:
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            one_step()
+        torch.cuda.synchronize()
+        elapsed_ahead = time.perf_counter() - t1
 
     # Instrumented steps of the same schedule: events around every verification (or
     # verification + selection) call.
@@ -685,12 +713,8 @@ def main():
     if overlap:
         one_step(single_stream=True)
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
         n_single = max(3, args.steps // 2)
-        for _ in range(n_single):
-            one_step(single_stream=True)
-        torch.cuda.synchronize()
-        single_ms = (time.perf_counter() - t1) * 1e3 / n_single
+        single_ms = timed_steps(n_single, single_stream=True) * 1e3 / n_single
         one_step(head_events=single_heads, single_stream=True)   # the one call's own duration
         torch.cuda.synchronize()
 
@@ -796,6 +820,10 @@ def main():
                                      f"verify{sfx}, select and gamma sparse-decode{sfx} calls per layer")
     result["config"]["split_plan"] = ("host (host copies of the offsets, computed per call)" if host_plan
                                       else "device")
+    result["config"]["host_sync"] = ("after every step (one decoding iteration): the next iteration's host plans "
+                                      "need its accepted lengths" if step_sync else "none between steps")
+    if elapsed_ahead is not None:
+        result["layer_step_host_ahead_us"] = round(elapsed_ahead * 1e6 / args.steps / layers, 2)
 
     # Plain verification (collection off) was timed in the breakdown steps, layer by layer next to
     # the separate calls and the one call, for the collection + select overhead.
