@@ -46,6 +46,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr int kRoundWorkgroups = 256;
 
 struct AttnPlan {
+    bool pair = false;   // gather: workgroups take two KV heads (the split kernel's PAIR layout)
     int mb = 0;          // 16-row query tiles per KV head
     int target = 0;      // splits per KV head for the whole batch, shared by length
     int cap = 0;         // longest split
@@ -75,10 +76,17 @@ AttnPlan plan_attn(bool bf16, int batch, int hkv, int M, int head_dim, int max_n
         if (page_cap < cap) cap = (int)page_cap;
     }
     p.cap = cap;
+    // A drafting pass with one query tile and an even KV head count runs its
+    // workgroups on head pairs: both heads' 256-byte slices of every gathered
+    // row in one workgroup, 512 contiguous bytes a row (a gather probe read
+    // the drafting bytes ~5% faster so); twice the splits per head then keep
+    // one round of workgroups.
+    p.pair = gather && p.mb == 1 && hkv % 2 == 0;
+    const int groups = p.pair ? hkv / 2 : hkv;
     // Bounds of the device plan (seq_plan / batch_plan in attn.hip): a sequence
     // gets at most max(target + 1, ceil(len / cap)) splits (the float share can
     // round one up), the batch at most max(target, ceil(total / cap)) + 2 * batch.
-    p.target = std::max(1, kRoundWorkgroups / hkv);
+    p.target = std::max(1, kRoundWorkgroups / groups);
     p.nsplit = (int)std::max<int64_t>(p.target + 1, (n + cap - 1) / cap);
     p.max_units = (int)std::max<int64_t>(p.target, (batch * n + cap - 1) / cap) + 2 * batch;
     // a single 16-row tile keeps only its M valid rows in a partial (part_rows in attn.hip)
@@ -554,6 +562,7 @@ vegas_status_t decode_impl(const vegas_attn_shape_t* shape, const void* q, const
     a.scale_log2 = shape->softmax_scale * 1.4426950408889634f;
     a.collect_mask = 0u;
     a.page_shift = shift;
+    a.pair = plan.pair ? 1 : 0;
     if (pages) {
         a.block_table = pages->block_table;
         a.max_pages = pages->max_pages_per_seq;

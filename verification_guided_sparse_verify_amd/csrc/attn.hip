@@ -574,8 +574,8 @@ __device__ __forceinline__ void compute_block(const AttnArgs& a, WaveState<BF16,
 // head g and all query rows of the KV head.  The unit's partial goes to slot
 // `slot` of (b, g).  Called by whole workgroups (every branch on its
 // arguments is uniform); the LDS arrays are the kernel's.
-template <bool BF16, int D, int MB, bool GATHER, bool COLLECT>
-__device__ __forceinline__ void split_unit(const AttnArgs& a, int g, int b, int slot, int start, int end,
+template <bool BF16, int D, int MB, bool GATHER, bool COLLECT, bool PAIR>
+__device__ __forceinline__ void split_unit(const AttnArgs& a, int g0, int b, int slot, int start, int end,
                                            const SeqSpan& sp, unsigned char* smem, int* idx_s, int* page_s,
                                            float* score_s) {
     constexpr int NT = kAttnWaves * 64;           // threads
@@ -583,8 +583,15 @@ __device__ __forceinline__ void split_unit(const AttnArgs& a, int g, int b, int 
     using T = typename std::conditional<BF16, uint16_t, float>::type;
     constexpr int DC = GEO::DC, DB = GEO::DB, NREG = GEO::NREG, NST = GEO::NST;
     constexpr int OPS = GEO::BLOCK_OPS;           // copies one wave issues per block
+    // PAIR (gather only): waves 2i and 2i+1 take KV heads g0 and g0+1 of the
+    // same rows, so a block's copies read 512 contiguous bytes of every row;
+    // each head has two position groups.
+    static_assert(!PAIR || GATHER, "head pairs are a gather layout");
+    constexpr int NPG = PAIR ? kAttnWaves / 2 : kAttnWaves;    // position groups per KV head
     const int lane = threadIdx.x & 63;
-    const int pw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // position group (wave)
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave
+    const int pw = PAIR ? wv >> 1 : wv;                                  // its position group
+    const int g = PAIR ? g0 + (wv & 1) : g0;                             // its KV head
     const int lr = lane & 15;
     const int lg = lane >> 4;
     const int seq0 = sp.seq0, n_b = sp.n_b, L = sp.L, ib0 = sp.ib0;
@@ -666,16 +673,16 @@ __device__ __forceinline__ void split_unit(const AttnArgs& a, int g, int b, int 
     c.start = start;
     c.end = end;
 
-    // This position group's blocks are pw, pw+kAttnWaves, ...; a ring of NST
+    // This position group's blocks are pw, pw+NPG, ...; a ring of NST
     // stages keeps NST-1 of them in flight.  No copy goes past the group's last
     // block, so the wait at the top of iteration jj counts the copies of the
     // blocks after jj that were issued: those of block jj+1 with a three-stage
     // ring unless jj is the last block, none otherwise.
     static_assert(NST == 2 || NST == 3, "the waits below count one or two stages");
     const int nblk = (end - start + kAttnBlock - 1) / kAttnBlock;
-    const int nmine = pw < nblk ? (nblk - pw + kAttnWaves - 1) / kAttnWaves : 0;
-    unsigned char* ring = smem + pw * (NST * GEO::STAGE);
-    auto block_pos = [&](int jj) { return start + (pw + kAttnWaves * min(jj, nmine - 1)) * kAttnBlock; };
+    const int nmine = pw < nblk ? (nblk - pw + NPG - 1) / NPG : 0;
+    unsigned char* ring = smem + wv * (NST * GEO::STAGE);
+    auto block_pos = [&](int jj) { return start + (pw + NPG * min(jj, nmine - 1)) * kAttnBlock; };
     auto issue = [&](int jj, unsigned char* stage) { issue_block<GEO, GATHER>(c, block_pos(jj), lane, stage); };
 #pragma unroll
     for (int st = 0; st < NST - 1; ++st)
@@ -709,15 +716,17 @@ __device__ __forceinline__ void split_unit(const AttnArgs& a, int g, int b, int 
         ws.l_run[qb] = pair32_sum(pair16_sum(ws.l_run[qb]));
     }
 
-    // Tree merge of the position groups' (m, l, O) through LDS, in fragment
-    // order.
+    // Tree merge of each KV head's position groups' (m, l, O) through LDS, in
+    // fragment order (with head pairs, both heads' merges side by side).
     __syncthreads();
     float* fs = reinterpret_cast<float*>(smem);
     constexpr int SLOTF = GEO::MSLOT / 4;
+    constexpr int HW = PAIR ? 2 : 1;              // heads per workgroup
+    const int hsel = PAIR ? (wv & 1) : 0;
 #pragma unroll
-    for (int half = kAttnWaves / 2; half >= 1; half >>= 1) {
+    for (int half = NPG / 2; half >= 1; half >>= 1) {
         if (pw >= half && pw < 2 * half) {
-            float* slot = fs + (pw - half) * SLOTF;
+            float* slot = fs + ((pw - half) * HW + hsel) * SLOTF;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -731,7 +740,7 @@ __device__ __forceinline__ void split_unit(const AttnArgs& a, int g, int b, int 
         }
         __syncthreads();
         if (pw < half) {
-            const float* slot = fs + pw * SLOTF;
+            const float* slot = fs + (pw * HW + hsel) * SLOTF;
 #pragma unroll
             for (int qb = 0; qb < MB; ++qb) {
                 const float mb = slot[NREG * 256 + qb * 64 + lane];
@@ -789,7 +798,7 @@ __device__ __forceinline__ void split_unit(const AttnArgs& a, int g, int b, int 
     }
 }
 
-template <bool BF16, int D, int MB, bool GATHER, bool COLLECT>
+template <bool BF16, int D, int MB, bool GATHER, bool COLLECT, bool PAIR>
 __global__ void __launch_bounds__(kAttnWaves * 64)
 attn_split_kernel(const AttnArgs a) {
     constexpr int NT = kAttnWaves * 64;           // threads
@@ -816,19 +825,21 @@ attn_split_kernel(const AttnArgs a) {
         for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.sel_zero_n; i += gridDim.x * blockDim.x)
             a.sel_zero[i] = 0u;
 
-    // Workgroup -> (KV head g, its units).  Without a unit table a workgroup
-    // runs one unit (sequence b, split): the units of all sequences' split
-    // plans, in order; workgroups past the last unit have no work.  With the
-    // device plan, workgroup 0 publishes every sequence's split count for the
-    // combine.
+    // Workgroup -> (KV head g, or heads g and g+1 with PAIR; its units).
+    // Without a unit table a workgroup runs one unit (sequence b, split): the
+    // units of all sequences' split plans, in order; workgroups past the last
+    // unit have no work.  With the device plan, workgroup 0 publishes every
+    // sequence's split count for the combine.
     __shared__ int plan_red[NWV];
     __shared__ int plan_s[3];
+    const int hgroups = PAIR ? a.hkv / 2 : a.hkv;
 #ifdef VEGAS_PHASE_TRACE
-    const int g = g_trace_rotate ? (blockIdx.x + blockIdx.x / a.hkv) % a.hkv : blockIdx.x % a.hkv;
+    const int hg = g_trace_rotate ? (blockIdx.x + blockIdx.x / hgroups) % hgroups : blockIdx.x % hgroups;
 #else
-    const int g = blockIdx.x % a.hkv;
+    const int hg = blockIdx.x % hgroups;
 #endif
-    const int unit_id = blockIdx.x / a.hkv;
+    const int g = PAIR ? 2 * hg : hg;
+    const int unit_id = blockIdx.x / hgroups;
     // This workgroup's units: entries k0 .. k0+nunits-1 of the unit table, or
     // the one unit (b, split) of the per-sequence plan.  One call site of
     // split_unit, so the kernel holds one copy of it.
@@ -911,7 +922,8 @@ attn_split_kernel(const AttnArgs a) {
             sp.ib0 = a.hp.ib0[b];
             if (i > 0) __syncthreads();                           // the previous unit's LDS reads are done
         }
-        split_unit<BF16, D, MB, GATHER, COLLECT>(a, g, b, slot, start, end, sp, smem, idx_s, page_s, score_s);
+        split_unit<BF16, D, MB, GATHER, COLLECT, PAIR>(a, g, b, slot, start, end, sp, smem, idx_s, page_s,
+                                                       score_s);
     }
 #ifdef VEGAS_PHASE_TRACE
     if (threadIdx.x == 0 && blockIdx.x < kTraceMax) {
@@ -1038,16 +1050,16 @@ __global__ void __launch_bounds__(kCombineWaves * 64) attn_combine_kernel(const 
     }
 }
 
-template <bool BF16, int D, int MB, bool GATHER, bool COLLECT>
+template <bool BF16, int D, int MB, bool GATHER, bool COLLECT, bool PAIR>
 hipError_t launch_t(const AttnArgs& a, hipStream_t stream, const SelectArgs* sel) {
     // (a host plan knows the exact workgroup count; the device plan's grid is its bound)
     const int per_head = a.hp.nwg > 0 ? a.hp.nwg : (a.hp.n > 0 ? a.hp.first[a.hp.n] : a.max_units);
-    const unsigned split_grid = (unsigned)(a.hkv * per_head);
+    const unsigned split_grid = (unsigned)((PAIR ? a.hkv / 2 : a.hkv) * per_head);
     const unsigned comb_grid = (unsigned)(a.batch * a.hkv * MB * (D / 16));
     const size_t dyn = (COLLECT ? attn_score_lds_bytes(a.score_cap) : 0) +
                        (!GATHER && a.page_shift >= 0 ? kMaxPagesPerSplit * sizeof(int) : 0);
     if (split_grid > 0)
-        hipLaunchKernelGGL((attn_split_kernel<BF16, D, MB, GATHER, COLLECT>), dim3(split_grid),
+        hipLaunchKernelGGL((attn_split_kernel<BF16, D, MB, GATHER, COLLECT, PAIR>), dim3(split_grid),
                            dim3(kAttnWaves * 64), dyn, stream, a);
     if (comb_grid > 0) {
         if constexpr (COLLECT && !GATHER) {
@@ -1065,14 +1077,21 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream, const SelectArgs* sel
 
 template <bool BF16, int D, bool GATHER, bool COLLECT>
 hipError_t launch_mb(const AttnArgs& a, int mb, hipStream_t s, const SelectArgs* sel) {
-    if (mb == 1) return launch_t<BF16, D, 1, GATHER, COLLECT>(a, s, sel);
-    if (mb == 2) return launch_t<BF16, D, 2, GATHER, COLLECT>(a, s, sel);
+    if constexpr (GATHER) {
+        // head pairs for the one-tile drafting passes (G <= 16) at an even KV head count
+        if (a.pair) {
+            if (mb == 1 && a.hkv % 2 == 0) return launch_t<BF16, D, 1, true, false, true>(a, s, sel);
+            return hipErrorInvalidValue;
+        }
+    }
+    if (mb == 1) return launch_t<BF16, D, 1, GATHER, COLLECT, false>(a, s, sel);
+    if (mb == 2) return launch_t<BF16, D, 2, GATHER, COLLECT, false>(a, s, sel);
     // fp32 at D = 128 stops at 32 rows per KV head (LDS budget).  Three and
     // four row tiles keep one wave per position group with all the tiles in
     // its registers (at most 256 VGPRs + 198 AGPRs, bf16 at D = 128).
     if constexpr (BF16 || D == 64) {
-        if (mb == 3) return launch_t<BF16, D, 3, GATHER, COLLECT>(a, s, sel);
-        if (mb == 4) return launch_t<BF16, D, 4, GATHER, COLLECT>(a, s, sel);
+        if (mb == 3) return launch_t<BF16, D, 3, GATHER, COLLECT, false>(a, s, sel);
+        if (mb == 4) return launch_t<BF16, D, 4, GATHER, COLLECT, false>(a, s, sel);
     }
     return hipErrorInvalidValue;
 }

@@ -110,6 +110,7 @@ struct AttnArgs {
     int32_t num_pages;
     int32_t page_shift;            // log2(page size); -1: contiguous varlen cache
     int32_t window;                // verification local mask: row r sees keys (L+r-window, L+r]; 0: none
+    int32_t pair;                  // gather: each workgroup takes KV heads g and g+1 (two waves each)
     // Fused selection (verification with collection only): the split kernel
     // clears sel_zero[0 .. sel_zero_n) and the combine kernel runs the
     // selection's first step on the finished scores.  NULL: not fused.
