@@ -9,9 +9,10 @@ every layer.  The reported value is microseconds per layer-step
 (verify + select + gamma drafts of one layer) = step time / layers.
 
 With several layers, verification + selection runs as the one call in two
-halves: the selection of layer l (keys, candidates, write) goes to a second
-stream, beside the verification of layer l+1 (the selected positions are used
-only by the drafting passes, which wait for each layer's selection).
+halves: the selections (keys, candidates, write) of a group of four layers go
+to a second stream after the group's last verification, beside the next
+layers' verifications (the selected positions are used only by the drafting
+passes, which wait for each group's selections).
 
 Each step of several layers ends with a synchronisation, as a decoding loop's
 iteration does: the next iteration's host-planned calls take host copies of
@@ -613,6 +614,11 @@ def main():
     # drafting passes, which wait for each layer's selection, while layer l+1's verification
     # needs only layer l's output, complete when the first half ends.
     overlap = fused and host_plan and layers > 1 and not args.single_stream
+    # The second halves go to the side stream in groups of SEL_GROUP layers, each group after its
+    # last layer's first half: every cross-stream event costs the launch stream ~1 us, and the
+    # selections are needed only by the drafting passes (interleaved in one process, 128K step:
+    # 477.5 us per layer-step with a group per layer, 473.6 with groups of four).
+    SEL_GROUP = 4
     side = torch.cuda.Stream() if overlap else None              # default priority, as the launch stream
     begin_calls = [st.bind_fused(stream, part="begin") for st in steps] if overlap else None
     end_calls = [st.bind_fused(side, part="end") for st in steps] if overlap else None
@@ -655,16 +661,20 @@ def main():
             else:
                 head()
             if halves:
-                verified[li].record(stream)
-                side.wait_event(verified[li])
-                end_calls[li]()
-                selected[li].record(side)
+                # the second halves of a group of layers, once the group's last first half is done
+                if (li + 1) % SEL_GROUP == 0 or li == layers - 1:
+                    verified[li].record(stream)
+                    side.wait_event(verified[li])
+                    for lj in range(li - li % SEL_GROUP, li + 1):
+                        end_calls[lj]()
+                    selected[li].record(side)
             elif not fused:
                 select()
         for j in range(wl.n_drafts):
             for li, (_, _, _, drafts) in enumerate(bound):
-                if halves and j == 0:
-                    stream.wait_event(selected[li])    # the first drafting pass needs layer li's selection
+                if halves and j == 0 and li % SEL_GROUP == 0:
+                    # the first drafting pass needs the selections of the group of layer li
+                    stream.wait_event(selected[min(li + SEL_GROUP - 1, layers - 1)])
                 if call_events is not None:
                     timed("draft", drafts[j], call_events)
                 else:
@@ -809,8 +819,9 @@ def main():
     sfx = "_hostplan" if host_plan else ""
     if overlap:
         result["config"]["calls"] = ("vegas_verify_select_begin_hostplan per layer on the launch stream, "
-                                     "vegas_verify_select_end_hostplan of layer l on a second stream beside layer "
-                                     "l+1; then gamma x vegas_sparse_decode_attn_hostplan per layer")
+                                     "vegas_verify_select_end_hostplan of layers 4m..4m+3 on a second stream after "
+                                     "layer 4m+3's first half, beside the next layers; then gamma x "
+                                     "vegas_sparse_decode_attn_hostplan per layer")
         result["layer_step_single_stream_us"] = round(single_ms * 1e3 / layers, 2)
         result["layer_step_single_stream_calls"] = ("vegas_verify_select_hostplan + gamma x "
                                                     "vegas_sparse_decode_attn_hostplan per layer, one stream")
