@@ -242,7 +242,7 @@ void check_attn(const Case& c, bool gather, size_t ws_bytes, const char* entry, 
     {
         const int db = c.D / 16;
         const int mslot = (db * mb * 4 + 2 * mb) * 64 * 4;
-        const int ring = vegas::attn_ring_bytes(bf16, c.D);
+        const int ring = vegas::attn_ring_bytes(bf16, c.D, gather);
         const int main_lds = std::max(ring, (vegas::kAttnWaves / 2) * mslot);
         const long long stat = main_lds + (gather ? vegas::kMaxGatherChunk * 4 : 4) + 64;
         const long long dyn = (!gather && g_cap.collect ? vegas::attn_score_lds_bytes(a.score_cap) : 0) +

@@ -204,7 +204,7 @@ __device__ __forceinline__ void keep_live(Frag<false>& f) {
     keep_live(f.u[1]);
 }
 
-template <bool BF16, int D, int MB>
+template <bool BF16, int D, int MB, bool GATHER>
 struct Geo {
     static constexpr int ES = BF16 ? 2 : 4;       // element bytes
     static constexpr int DC = D / 32;             // k chunks of the QK^T contraction
@@ -216,7 +216,7 @@ struct Geo {
     static constexpr int TLD = kAttnBlock / RPI;  // copies per lane per K (or V) tile
     static constexpr int TILE = kAttnBlock * ROWB;
     static constexpr int STAGE = 2 * TILE;        // K tile then V tile
-    static constexpr int NST = attn_stages(BF16, D);   // ring depth
+    static constexpr int NST = attn_stages(BF16, D, GATHER);   // ring depth
     static constexpr int RING = kAttnWaves * NST * STAGE;
     static constexpr int BLOCK_OPS = 2 * TLD;     // copies one block issues
     static constexpr int SWZU = 16 / EPC;         // chunks per 16-element d tile
@@ -579,7 +579,7 @@ __device__ __forceinline__ void split_unit(const AttnArgs& a, int g0, int b, int
                                            const SeqSpan& sp, unsigned char* smem, int* idx_s, int* page_s,
                                            float* score_s) {
     constexpr int NT = kAttnWaves * 64;           // threads
-    using GEO = Geo<BF16, D, MB>;
+    using GEO = Geo<BF16, D, MB, GATHER>;
     using T = typename std::conditional<BF16, uint16_t, float>::type;
     constexpr int DC = GEO::DC, DB = GEO::DB, NREG = GEO::NREG, NST = GEO::NST;
     constexpr int OPS = GEO::BLOCK_OPS;           // copies one wave issues per block
@@ -803,7 +803,7 @@ __global__ void __launch_bounds__(kAttnWaves * 64)
 attn_split_kernel(const AttnArgs a) {
     constexpr int NT = kAttnWaves * 64;           // threads
     constexpr int NWV = NT / 64;                  // waves
-    using GEO = Geo<BF16, D, MB>;
+    using GEO = Geo<BF16, D, MB, GATHER>;
     constexpr int MERGE = (kAttnWaves / 2) * GEO::MSLOT;
     constexpr int MAIN = GEO::RING > MERGE ? GEO::RING : MERGE;
 

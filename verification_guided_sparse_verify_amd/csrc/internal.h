@@ -19,8 +19,11 @@ constexpr int kAttnBlock = 16;
 // in flight (all but the one being computed) hold at least 8 KB per wave,
 // 32 KB per CU, where streaming reads saturate; deeper rings measured slower.
 // 2 stages (one 8 KB block in flight) except bf16 at D = 64 (4 KB blocks): 3.
-__host__ __device__ constexpr int attn_stages(bool bf16, int head_dim) {
-    return (bf16 && head_dim == 64) ? 3 : 2;
+// Gathered rows (drafting passes, bf16) take 3 stages at any D: scattered
+// rows come back slower than streamed ones, and two blocks in flight per
+// wave read the drafting bytes faster (measured).
+__host__ __device__ constexpr int attn_stages(bool bf16, int head_dim, bool gather = false) {
+    return (bf16 && (head_dim == 64 || gather)) ? 3 : 2;
 }
 // Longest position range one workgroup takes in gather mode: its index list
 // is staged in LDS.
@@ -33,8 +36,8 @@ constexpr int kMaxPageSize = 256;
 constexpr int kMaxBatch = 1024;
 
 // Bytes of one workgroup's K/V ring.
-__host__ __device__ constexpr int attn_ring_bytes(bool bf16, int head_dim) {
-    return kAttnWaves * attn_stages(bf16, head_dim) * 2 * kAttnBlock * head_dim * (bf16 ? 2 : 4);
+__host__ __device__ constexpr int attn_ring_bytes(bool bf16, int head_dim, bool gather = false) {
+    return kAttnWaves * attn_stages(bf16, head_dim, gather) * 2 * kAttnBlock * head_dim * (bf16 ? 2 : 4);
 }
 // Longest position range one workgroup takes in verification: the collected
 // scores of its range are buffered in LDS next to the ring (144 KB in all of
