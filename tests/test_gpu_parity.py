@@ -61,6 +61,10 @@ SWEEP = [
     ("bf16", 3, 64, 8, 128, 6, [5000, 64, 2047], Fraction(5, 100)),
     ("bf16", 2, 32, 4, 128, 4, [2500, 4100], Fraction(5, 100)),
     ("f32", 2, 32, 4, 64, 5, [1500, 33], Fraction(5, 100)),
+    # drafting workgroups on one KV head: an odd KV head count, and 32 query rows per KV head
+    # (two row tiles); the other cases above draft on KV head pairs
+    ("bf16", 2, 12, 3, 64, 3, [2000, 513], Fraction(5, 100)),
+    ("bf16", 2, 64, 2, 128, 1, [3000, 700], Fraction(5, 100)),
 ]
 
 
