@@ -252,8 +252,8 @@ def gather_read_ceiling(wl, layer_inputs, steps, reps=3):
     probe = ctypes.CDLL(B.PROBE_LIB)
     fn = probe.vegas_probe_gather_read
     fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
-                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
-                   ctypes.c_void_p]
+                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                   ctypes.c_void_p, ctypes.c_void_p]
     fn.restype = ctypes.c_int
     es = 2 if wl.dtype == "bf16" else 4
     slice_bytes = wl.head_dim * es
@@ -265,30 +265,33 @@ def gather_read_ceiling(wl, layer_inputs, steps, reps=3):
     nbytes = sum(int(r.numel()) for _, _, r in lists) * row_bytes * 2
     sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
-    best = (0.0, 0, 0)
-    for wgs in (256, 512, 1024):
-        for inflight in (1, 2, 3):
-            times = []
-            for r in range(reps + 1):
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                for k, v, rows in lists:
-                    rc = fn(k.data_ptr(), v.data_ptr(), rows.data_ptr(), rows.numel(), wl.total_kv, row_bytes,
-                            slice_bytes, wl.num_kv_heads, wgs, inflight, sink.data_ptr(), stream.cuda_stream)
-                    if rc != 0:
-                        raise RuntimeError(f"vegas_probe_gather_read returned {rc}")
-                b.record(stream)
-                times.append((a, b))
-            torch.cuda.synchronize()
-            us = min(x.elapsed_time(y) for x, y in times[1:]) * 1e3
-            gbps = nbytes / (us * 1e-6) / 1e9
-            if gbps > best[0]:
-                best = (gbps, wgs, inflight)
+    best = (0.0, 0, 0, 0)
+    for hpw in ((1, 2) if wl.num_kv_heads % 2 == 0 else (1,)):
+        for wgs in (256, 512, 1024):
+            for inflight in (1, 2, 3):
+                times = []
+                for r in range(reps + 1):
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    for k, v, rows in lists:
+                        rc = fn(k.data_ptr(), v.data_ptr(), rows.data_ptr(), rows.numel(), wl.total_kv, row_bytes,
+                                slice_bytes, wl.num_kv_heads, hpw, wgs, inflight, sink.data_ptr(),
+                                stream.cuda_stream)
+                        if rc != 0:
+                            raise RuntimeError(f"vegas_probe_gather_read returned {rc}")
+                    b.record(stream)
+                    times.append((a, b))
+                torch.cuda.synchronize()
+                us = min(x.elapsed_time(y) for x, y in times[1:]) * 1e3
+                gbps = nbytes / (us * 1e-6) / 1e9
+                if gbps > best[0]:
+                    best = (gbps, wgs, inflight, hpw)
     return {"gbps": round(best[0], 1), "workgroups": best[1], "blocks_in_flight_per_wave": best[2],
-            "bytes": nbytes, "layers": len(lists),
+            "heads_per_workgroup": best[3], "bytes": nbytes, "layers": len(lists),
             "kernel": ("vegas_probe_gather_read (the drafting pass's K/V slices of the selected rows of every "
-                       "layer, 16-byte non-temporal direct-to-LDS copies, no arithmetic)")}
+                       "layer, 16-byte non-temporal direct-to-LDS copies, no arithmetic; best of 1 or 2 heads per "
+                       "workgroup, 256-1024 workgroups and 1-3 blocks in flight per wave)")}
 
 
 def launch_floor(chain: int = 200, reps: int = 5):

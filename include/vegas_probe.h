@@ -32,19 +32,23 @@ int vegas_probe_stream_read(const void* src, size_t bytes, int32_t workgroups, u
  * entry e of rows (device int32 [n_rows], token row numbers, clamped into
  * [0, total_rows)), the slice_bytes-byte slice of each of `heads` heads of
  * row rows[e] of k and of v (row r, head h at byte r * row_bytes +
- * h * slice_bytes).  Workgroup w (of `workgroups`, a multiple of heads) reads
- * head w % heads of an equal range of at most 4096 entries, whose row numbers
- * it stages in LDS first; its four waves take 16-row blocks in turn through
- * private rings that keep blocks_in_flight (1..3) blocks in flight while one
- * is awaited (the drafting pass keeps one), with 16-byte direct-to-LDS copies
- * under the non-temporal cache policy.  slice_bytes is 128 or 256; k and v
- * 16-byte aligned.  sink: device uint32 [1], never written in practice (it
- * keeps the reads live).  Asynchronous on `stream`.  Returns 0, -1 for
- * invalid arguments (nothing launched), or the HIP error code of the launch.
+ * h * slice_bytes).  Workgroups take heads_per_workgroup (1 or 2, dividing
+ * heads) heads each: workgroup w (of `workgroups`, a multiple of
+ * heads / heads_per_workgroup) reads an equal range of at most 4096 entries,
+ * whose row numbers it stages in LDS first; with two heads, waves 2i and
+ * 2i+1 read the two heads' slices of the same rows (the drafting kernel's
+ * head pairs).  Each wave takes its head's 16-row blocks in turn through a
+ * private ring: it waits for its oldest block, then issues the next, keeping
+ * blocks_in_flight (1..3) blocks in flight, with 16-byte direct-to-LDS
+ * copies under the non-temporal cache policy and nothing past its last
+ * block.  slice_bytes is 128 or 256; k and v 16-byte aligned.  sink: device
+ * uint32 [1], never written in practice (it keeps the reads live).
+ * Asynchronous on `stream`.  Returns 0, -1 for invalid arguments (nothing
+ * launched), or the HIP error code of the launch.
  */
 int vegas_probe_gather_read(const void* k, const void* v, const int32_t* rows, int32_t n_rows, int32_t total_rows,
-                            int32_t row_bytes, int32_t slice_bytes, int32_t heads, int32_t workgroups,
-                            int32_t blocks_in_flight, uint32_t* sink, void* stream);
+                            int32_t row_bytes, int32_t slice_bytes, int32_t heads, int32_t heads_per_workgroup,
+                            int32_t workgroups, int32_t blocks_in_flight, uint32_t* sink, void* stream);
 
 /*
  * Dependent-launch floor: `launches` (1..100000) launches back to back on

@@ -316,21 +316,24 @@ def test_gather_probe_rejects_bad_arguments(V):
     """The gather-ceiling probe validates its arguments before launching anything."""
     from verification_guided_sparse_verify_amd import build as B
     fn = ctypes.CDLL(B.PROBE_LIB).vegas_probe_gather_read
-    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int32] * 7 + [ctypes.c_void_p] * 2
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int32] * 8 + [ctypes.c_void_p] * 2
 
     def call(**kw):
-        p = dict(k=FAKE, v=FAKE, rows=FAKE, n=100, total=1000, row=2048, slice=256, heads=8, wgs=256, inflight=2,
-                 sink=FAKE)
+        p = dict(k=FAKE, v=FAKE, rows=FAKE, n=100, total=1000, row=2048, slice=256, heads=8, hpw=2, wgs=256,
+                 inflight=2, sink=FAKE)
         p.update(kw)
-        return fn(p["k"], p["v"], p["rows"], p["n"], p["total"], p["row"], p["slice"], p["heads"], p["wgs"],
-                  p["inflight"], p["sink"], None)
+        return fn(p["k"], p["v"], p["rows"], p["n"], p["total"], p["row"], p["slice"], p["heads"], p["hpw"],
+                  p["wgs"], p["inflight"], p["sink"], None)
 
     assert call(k=None) == -1
     assert call(v=FAKE + 8) == -1              # misaligned
     assert call(n=0) == -1
     assert call(slice=512) == -1               # only 128- or 256-byte slices
     assert call(row=1024) == -1                # eight 256-byte slices do not fit a 1 KB row
-    assert call(wgs=260) == -1                 # not a multiple of the head count
+    assert call(wgs=258) == -1                 # not a multiple of the four head pairs
+    assert call(hpw=3) == -1                   # one or two heads per workgroup
+    assert call(heads=7, row=7 * 256) == -1    # an odd head count cannot be paired
+    assert call(hpw=1, wgs=260) == -1
     assert call(inflight=4) == -1
     assert call(n=300000, wgs=8) == -1         # more than 4096 entries per workgroup
     assert call(sink=None) == -1

@@ -53,7 +53,11 @@ __global__ void __launch_bounds__(kThreads) stream_read_kernel(const unsigned ch
 // does.  Row numbers are clamped into [0, total_rows).
 constexpr int kGatherRows = 16;
 constexpr int kGatherMaxRange = 4096;
-template <int SLICE, int DEPTH>
+// HPW heads per workgroup: wave w reads head HPW * (workgroup % groups) + w % HPW
+// and takes the 16-row blocks w / HPW, w / HPW + 4 / HPW, ... of the
+// workgroup's range; each wave waits for its oldest block, then issues the
+// next, keeping DEPTH - 1 blocks in flight, and issues nothing past its last.
+template <int SLICE, int DEPTH, int HPW>
 __global__ void __launch_bounds__(kThreads) gather_read_kernel(const unsigned char* __restrict__ k,
                                                                const unsigned char* __restrict__ v,
                                                                const int32_t* __restrict__ rows, int32_t n_rows,
@@ -64,18 +68,22 @@ __global__ void __launch_bounds__(kThreads) gather_read_kernel(const unsigned ch
     constexpr int COPIES = kGatherRows / RPC;      // copies per tensor per block
     constexpr int BLK = kGatherRows * SLICE;       // bytes per tensor per block
     constexpr int OPS = 2 * COPIES;                // copies per block
+    constexpr int NPG = 4 / HPW;                   // waves per head
+    static_assert(DEPTH >= 2 && DEPTH <= 4, "one to three blocks in flight");
     __shared__ __attribute__((aligned(16))) unsigned char ring[kThreads / 64][DEPTH][2 * BLK];
     __shared__ int idx_s[kGatherMaxRange];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int head = blockIdx.x % heads;
-    const int first = (blockIdx.x / heads) * per_wg;
+    const int groups = heads / HPW;
+    const int head = HPW * (blockIdx.x % groups) + wave % HPW;
+    const int pg = wave / HPW;
+    const int first = (blockIdx.x / groups) * per_wg;
     const int count = max(min(first + per_wg, n_rows) - first, 0);
     for (int i = threadIdx.x; i < count; i += kThreads) idx_s[i] = min(max(rows[first + i], 0), total_rows - 1);
     __syncthreads();
     const int nblk = (count + kGatherRows - 1) / kGatherRows;
-    const int mine = wave < nblk ? (nblk - wave + 3) / 4 : 0;      // this wave's blocks: wave, wave + 4, ...
+    const int mine = pg < nblk ? (nblk - pg + NPG - 1) / NPG : 0;   // this wave's blocks: pg, pg + NPG, ...
     auto issue = [&](int j, int stage) {
-        const int blk = wave + 4 * min(j, mine - 1);               // past the last: the last again
+        const int blk = pg + NPG * j;
 #pragma unroll
         for (int c = 0; c < COPIES; ++c) {
             const int e = min(blk * kGatherRows + c * RPC + lane / CPR, count - 1);
@@ -89,18 +97,21 @@ __global__ void __launch_bounds__(kThreads) gather_read_kernel(const unsigned ch
     uint32_t acc = 0;
     if (mine > 0) {
 #pragma unroll
-        for (int j = 0; j < DEPTH - 1; ++j) issue(j, j);
+        for (int j = 0; j < DEPTH - 1; ++j)
+            if (j < mine) issue(j, j);
         for (int j = 0; j < mine; ++j) {
-            issue(j + DEPTH - 1, (j + DEPTH - 1) % DEPTH);
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DEPTH - 1) * OPS) : "memory");   // block j has landed
+            // block j has landed: the copies of the blocks after it that were issued may still fly
+            const int after = min(DEPTH - 2, mine - 1 - j);
+            if (after >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * OPS) : "memory");
+            else if (after == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(OPS) : "memory");
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if (j + DEPTH - 1 < mine) issue(j + DEPTH - 1, (j + DEPTH - 1) % DEPTH);
             acc ^= reinterpret_cast<const uint32_t*>(&ring[wave][j % DEPTH][0])[lane];
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     if (acc == 0u && lane == 0 && mine > 0 && blockIdx.x == 0x7fffffff) sink[0] = 1u;   // keeps the reads live
 }
 
-// A kernel that only hands one word to the next launch.
 __global__ void __launch_bounds__(kThreads) launch_chain_kernel(uint32_t* __restrict__ sink) {
     extern __shared__ uint32_t chain_lds[];
     if (blockIdx.x == 0 && threadIdx.x == 0) sink[0] = sink[0] + 1u;
@@ -122,33 +133,42 @@ extern "C" int vegas_probe_launch_chain(int32_t launches, int32_t workgroups, in
 
 extern "C" int vegas_probe_gather_read(const void* k, const void* v, const int32_t* rows, int32_t n_rows,
                                        int32_t total_rows, int32_t row_bytes, int32_t slice_bytes, int32_t heads,
-                                       int32_t workgroups, int32_t blocks_in_flight, uint32_t* sink, void* stream) {
-    if (!k || !v || !rows || !sink || n_rows < 1 || total_rows < 1 || heads < 1 || workgroups < heads ||
-        workgroups % heads != 0 || blocks_in_flight < 1 || blocks_in_flight > 3)
+                                       int32_t heads_per_workgroup, int32_t workgroups, int32_t blocks_in_flight,
+                                       uint32_t* sink, void* stream) {
+    if (!k || !v || !rows || !sink || n_rows < 1 || total_rows < 1 || heads < 1 || blocks_in_flight < 1 ||
+        blocks_in_flight > 3 || (heads_per_workgroup != 1 && heads_per_workgroup != 2) ||
+        heads % heads_per_workgroup != 0)
         return -1;
+    const int groups = heads / heads_per_workgroup;
+    if (workgroups < groups || workgroups % groups != 0) return -1;
     if ((slice_bytes != 128 && slice_bytes != 256) || row_bytes < heads * slice_bytes || row_bytes % 16 != 0)
         return -1;
     if (((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15u) != 0) return -1;
-    const int per_head = workgroups / heads;
-    const int per_wg = (n_rows + per_head - 1) / per_head;
+    const int per_group = workgroups / groups;
+    const int per_wg = (n_rows + per_group - 1) / per_group;
     if (per_wg > kGatherMaxRange) return -1;
     const dim3 grid(workgroups), block(kThreads);
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const unsigned char* kb = static_cast<const unsigned char*>(k);
     const unsigned char* vb = static_cast<const unsigned char*>(v);
-#define VEGAS_PROBE_GATHER(S, D)                                                                                \
-    hipLaunchKernelGGL((gather_read_kernel<S, D>), grid, block, 0, st, kb, vb, rows, n_rows, total_rows, row_bytes, \
-                       heads, per_wg, sink)
+#define VEGAS_PROBE_GATHER(S, D, H)                                                                             \
+    hipLaunchKernelGGL((gather_read_kernel<S, D, H>), grid, block, 0, st, kb, vb, rows, n_rows, total_rows,     \
+                       row_bytes, heads, per_wg, sink)
+#define VEGAS_PROBE_GATHER_D(S, H)                 \
+    do {                                           \
+        if (depth == 2) VEGAS_PROBE_GATHER(S, 2, H); \
+        else if (depth == 3) VEGAS_PROBE_GATHER(S, 3, H); \
+        else VEGAS_PROBE_GATHER(S, 4, H);          \
+    } while (0)
     const int depth = blocks_in_flight + 1;       // ring stages: blocks in flight plus the one awaited
     if (slice_bytes == 256) {
-        if (depth == 2) VEGAS_PROBE_GATHER(256, 2);
-        else if (depth == 3) VEGAS_PROBE_GATHER(256, 3);
-        else VEGAS_PROBE_GATHER(256, 4);
+        if (heads_per_workgroup == 1) VEGAS_PROBE_GATHER_D(256, 1);
+        else VEGAS_PROBE_GATHER_D(256, 2);
     } else {
-        if (depth == 2) VEGAS_PROBE_GATHER(128, 2);
-        else if (depth == 3) VEGAS_PROBE_GATHER(128, 3);
-        else VEGAS_PROBE_GATHER(128, 4);
+        if (heads_per_workgroup == 1) VEGAS_PROBE_GATHER_D(128, 1);
+        else VEGAS_PROBE_GATHER_D(128, 2);
     }
+#undef VEGAS_PROBE_GATHER_D
 #undef VEGAS_PROBE_GATHER
     return (int)hipGetLastError();
 }
