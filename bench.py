@@ -532,6 +532,10 @@ def main():
                          "default a step of several layers, one decoding iteration, ends with a synchronisation: "
                          "the host-planned calls of the next iteration take host copies of sequence lengths that "
                          "depend on this iteration's accepted tokens)")
+    ap.add_argument("--kv-offset", type=int, default=None,
+                    help="byte offset of each layer's V cache from its K cache modulo 2 MB (default: the "
+                         "workload generator's KV_OFFSET_BYTES; 0 puts them at the same offset, as two plain "
+                         "allocations usually are)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--page-size", type=int, default=0,
                     help="keep every layer's KV cache as a randomly permuted page pool of this page size and "
@@ -560,6 +564,12 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.kv_offset is not None:
+        if args.kv_offset < 0 or args.kv_offset % 16:
+            print("bench.py: --kv-offset must be a non-negative multiple of 16", file=sys.stderr)
+            sys.exit(2)
+        from verification_guided_sparse_verify_amd import workloads as W
+        W.KV_OFFSET_BYTES = args.kv_offset
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
@@ -793,7 +803,7 @@ def main():
             "kv_cache_bytes": wl.total_kv * wl.num_kv_heads * wl.head_dim * (2 if wl.dtype == "bf16" else 4) * 2 * layers,
             "order": "verify+select over all layers, then gamma drafting passes over all layers",
             "kv_cache": (f"paged, {args.page_size}-token pages in a randomly permuted pool" if args.page_size
-                         else "contiguous varlen"),
+                         else f"contiguous varlen, each layer's V {W.KV_OFFSET_BYTES} B from its K modulo 2 MB"),
             "selection": ("verification-guided (Collect-2-Query + exact top-k)" if args.selection == "vegas"
                           else "query-agnostic: 4 sinks + most recent tokens, same k, no collection"),
         },

@@ -33,6 +33,12 @@
  *  - dtype of q, k, v and out: VEGAS_DTYPE_BF16 (bf16 storage, fp32
  *    accumulation and softmax) or VEGAS_DTYPE_F32.  D (head_dim) is 64 or
  *    128.  q, k, v, out must be 16-byte aligned.
+ *  - Placement (performance only): the passes read the K and V rows of the
+ *    same positions together.  When v's address equals k's modulo 2 MB, as
+ *    two large allocations' addresses usually do, the same heads' slices of
+ *    K and V meet in the memory system and some KV heads read slower; on
+ *    MI355X, putting v a few hundred bytes off (256-768) made the 128K
+ *    Qwen3-8B-shaped layer-step ~1.3% faster.
  *  - Errors: arguments are validated on the host before any launch; a
  *    non-OK status launches nothing (VEGAS_ERR_HIP: a launch failed after
  *    validation).  vegas_last_error_message() returns a per-thread detail

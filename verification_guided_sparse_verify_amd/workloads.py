@@ -175,12 +175,36 @@ def _unit(n_rows: int, d: int, gen: torch.Generator, device) -> torch.Tensor:
     return u / u.norm(dim=-1, keepdim=True)
 
 
+# Byte offset of V's storage from K's, modulo 2 MB, in the device KV caches drawn here.  Both
+# passes read the K and V rows of the same positions together; where the two tensors sit at the
+# same offset modulo 2 MB (as two large allocations do by default), the same heads' slices of K
+# and V meet in the memory system and two of the eight Qwen3 KV heads read ~4% slower, which
+# sets the end of every verification call (interleaved on one MI355X, 128K step: 474.7 us per
+# layer-step with V and K congruent, 467.2-468.6 with V 256, 512 or 768 bytes away).
+KV_OFFSET_BYTES = 512
+_TWO_MB = 2 << 20
+
+
+def kv_cache_pair(total: int, hkv: int, d: int, dtype, device):
+    """Empty K and V caches [total, hkv, d]; on a GPU, V's storage starts KV_OFFSET_BYTES after K's
+    modulo 2 MB (see above).  Both are contiguous and 16-byte aligned."""
+    dev = torch.device(device)
+    k = torch.empty(total, hkv, d, dtype=dtype, device=dev)
+    if dev.type != "cuda":
+        return k, torch.empty(total, hkv, d, dtype=dtype, device=dev)
+    nbytes = k.numel() * k.element_size()
+    raw = torch.empty(nbytes + _TWO_MB, dtype=torch.uint8, device=dev)
+    off = (k.data_ptr() + KV_OFFSET_BYTES - raw.data_ptr()) % _TWO_MB
+    v = raw[off: off + nbytes].view(dtype).view(total, hkv, d)
+    return k, v
+
+
 def make_inputs(wl: Workload, seed: int = 0, device="cpu", layer: int = 0, out: dict | None = None):
     """Draw one layer's inputs on `device` (a torch device string).
 
     Returns a dict of torch tensors on `device`:
       q        [batch*(gamma+1), Hq, D]   verification queries
-      k, v     [total_kv, Hkv, D]
+      k, v     [total_kv, Hkv, D]         (kv_cache_pair: V placed KV_OFFSET_BYTES from K mod 2 MB)
       cu_seqlens_k, cu_k  int32 [batch+1]
       draft_q  [n_drafts, batch, Hq, D]   fresh draft queries, one set per draft step
     If `out` holds preallocated k/v tensors of the right shape they are filled in place.
@@ -195,11 +219,12 @@ def make_inputs(wl: Workload, seed: int = 0, device="cpu", layer: int = 0, out: 
     total = cu[-1]
     dt = wl.torch_dtype
     res = {} if out is None else out
-    for name in ("k", "v"):
-        t = res.get(name)
-        if t is None or tuple(t.shape) != (total, Hkv, D) or t.dtype != dt or t.device != dev:
-            t = torch.empty(total, Hkv, D, dtype=dt, device=dev)
-            res[name] = t
+
+    def fits(t):
+        return t is not None and tuple(t.shape) == (total, Hkv, D) and t.dtype == dt and t.device == dev
+
+    if not (fits(res.get("k")) and fits(res.get("v"))):
+        res["k"], res["v"] = kv_cache_pair(total, Hkv, D, dt, dev)
     u = _unit(B * Hkv, D, gen, dev).view(B, Hkv, D)
     for b in range(B):
         s0, s1 = cu[b], cu[b + 1]
