@@ -68,6 +68,21 @@ SWEEP = [
 ]
 
 
+def test_kv_cache_pair_places_v_off_k():
+    """The generator's device caches: V starts KV_OFFSET_BYTES after K modulo 2 MB, both contiguous
+    and 16-byte aligned, and the drawn values do not depend on the placement."""
+    wl = W.custom_workload("bf16", 2, 8, 2, 128, 2, [3000, 700])
+    inp = W.make_inputs(wl, seed=3, device="cuda:0")
+    k, v = inp["k"], inp["v"]
+    assert k.is_contiguous() and v.is_contiguous()
+    assert k.data_ptr() % 16 == 0 and v.data_ptr() % 16 == 0
+    assert (v.data_ptr() - k.data_ptr()) % (2 << 20) == W.KV_OFFSET_BYTES
+    plain = {n: torch.empty_like(k) for n in ("k", "v")}           # two plain allocations
+    ref = W.make_inputs(wl, seed=3, device="cuda:0", out=plain)
+    assert ref["k"].data_ptr() == plain["k"].data_ptr()
+    assert torch.equal(k, ref["k"]) and torch.equal(v, ref["v"])
+
+
 @pytest.mark.parametrize("case", SWEEP, ids=lambda c: f"{c[0]}-B{c[1]}-{c[2]}x{c[3]}-D{c[4]}-g{c[5]}-L{c[6]}")
 def test_shape_sweep(case):
     dtype, B, hq, hkv, d, gamma, prefixes, ratio = case
