@@ -275,8 +275,9 @@ def page_cache(wl: Workload, inp: dict, page_size: int, seed: int = 0, spare_pag
     are cut into pages of `page_size` rows and the pages are scattered over a randomly
     permuted page pool (with a few unused pages).  A data layout only: no values change.
 
-    Returns {"k_pool", "v_pool": [num_pages, page_size, Hkv, D], "block_table": int32
-    [batch, max_pages] (unused slots point at pool page 0), "num_pages"}.
+    Returns {"k_pool", "v_pool": [num_pages, page_size, Hkv, D] (kv_cache_pair: on a GPU the V pool
+    starts KV_OFFSET_BYTES after the K pool modulo 2 MB), "block_table": int32 [batch, max_pages]
+    (unused slots point at pool page 0), "num_pages"}.
     """
     k, v = inp["k"], inp["v"]
     dev = k.device
@@ -296,8 +297,9 @@ def page_cache(wl: Workload, inp: dict, page_size: int, seed: int = 0, spare_pag
         bt[b, : per[b]] = perm[used: used + per[b]].to(torch.int32)
         used += per[b]
     out["block_table"] = bt.to(dev)
-    for name, src in (("k", k), ("v", v)):
-        pool = torch.zeros(num_pages * page_size, Hkv, D, dtype=src.dtype, device=dev)
+    pools = kv_cache_pair(num_pages * page_size, Hkv, D, k.dtype, dev)   # V off K, as the contiguous caches
+    for (name, src), pool in zip((("k", k), ("v", v)), pools):
+        pool.zero_()
         for b in range(wl.batch):
             t = torch.arange(lens[b], device=dev)
             rows = out["block_table"][b].long()[t // page_size] * page_size + t % page_size
