@@ -536,6 +536,10 @@ def main():
                     help="byte offset of each layer's V cache from its K cache modulo 2 MB (default: the "
                          "workload generator's KV_OFFSET_BYTES; 0 puts them at the same offset, as two plain "
                          "allocations usually are)")
+    ap.add_argument("--kv-gap", type=int, default=None,
+                    help="whole bytes (a multiple of 2 MB) between the end of each layer's K cache, rounded "
+                         "up to 2 MB, and its V cache, which share one allocation (default: the workload "
+                         "generator's KV_GAP_BYTES)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--page-size", type=int, default=0,
                     help="keep every layer's KV cache as a randomly permuted page pool of this page size and "
@@ -570,6 +574,12 @@ def main():
             sys.exit(2)
         from verification_guided_sparse_verify_amd import workloads as W
         W.KV_OFFSET_BYTES = args.kv_offset
+    if args.kv_gap is not None:
+        if args.kv_gap < 0 or args.kv_gap % (2 << 20):
+            print("bench.py: --kv-gap must be a non-negative multiple of 2 MB", file=sys.stderr)
+            sys.exit(2)
+        from verification_guided_sparse_verify_amd import workloads as W
+        W.KV_GAP_BYTES = args.kv_gap
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
@@ -803,7 +813,8 @@ def main():
             "kv_cache_bytes": wl.total_kv * wl.num_kv_heads * wl.head_dim * (2 if wl.dtype == "bf16" else 4) * 2 * layers,
             "order": "verify+select over all layers, then gamma drafting passes over all layers",
             "kv_cache": (f"paged, {args.page_size}-token pages in a randomly permuted pool" if args.page_size
-                         else f"contiguous varlen, each layer's V {W.KV_OFFSET_BYTES} B from its K modulo 2 MB"),
+                         else f"contiguous varlen, each layer's K and V in one allocation, V {W.KV_GAP_BYTES + W.KV_OFFSET_BYTES} B "
+                           f"past K's end rounded up to 2 MB"),
             "selection": ("verification-guided (Collect-2-Query + exact top-k)" if args.selection == "vegas"
                           else "query-agnostic: 4 sinks + most recent tokens, same k, no collection"),
         },

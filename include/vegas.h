@@ -34,11 +34,15 @@
  *    accumulation and softmax) or VEGAS_DTYPE_F32.  D (head_dim) is 64 or
  *    128.  q, k, v, out must be 16-byte aligned.
  *  - Placement (performance only): the passes read the K and V rows of the
- *    same positions together.  When v's address equals k's modulo 2 MB, as
- *    two large allocations' addresses usually do, the same heads' slices of
- *    K and V meet in the memory system and some KV heads read slower; on
- *    MI355X, putting v a few hundred bytes off (256-768) made the 128K
- *    Qwen3-8B-shaped layer-step ~1.3% faster.
+ *    same positions together, so their speed depends on where v sits
+ *    relative to k.  On MI355X, 128K Qwen3-8B-shaped layer: with v's
+ *    address equal to k's modulo 2 MB, as two large allocations' addresses
+ *    usually are, some KV heads read slower (v 256-768 bytes off made the
+ *    layer-step ~1.3% faster); beyond 2 MB, v 1 GiB + 10 MiB + 512 B past k
+ *    in one allocation read 320-323 us per verification against 339-340 at
+ *    1 GiB + 2 MiB + 512 B, and two separate allocations read anywhere in
+ *    between from layer to layer.  The library takes the caller's pointers
+ *    as given.
  *  - Errors: arguments are validated on the host before any launch; a
  *    non-OK status launches nothing (VEGAS_ERR_HIP: a launch failed after
  *    validation).  vegas_last_error_message() returns a per-thread detail

@@ -69,14 +69,18 @@ SWEEP = [
 
 
 def test_kv_cache_pair_places_v_off_k():
-    """The generator's device caches: V starts KV_OFFSET_BYTES after K modulo 2 MB, both contiguous
-    and 16-byte aligned, and the drawn values do not depend on the placement."""
+    """The generator's device caches: K at a 2 MB boundary and V KV_GAP_BYTES + KV_OFFSET_BYTES past
+    K's end rounded up to 2 MB, in one allocation, both contiguous, and the drawn values do not
+    depend on the placement."""
     wl = W.custom_workload("bf16", 2, 8, 2, 128, 2, [3000, 700])
     inp = W.make_inputs(wl, seed=3, device="cuda:0")
     k, v = inp["k"], inp["v"]
     assert k.is_contiguous() and v.is_contiguous()
-    assert k.data_ptr() % 16 == 0 and v.data_ptr() % 16 == 0
-    assert (v.data_ptr() - k.data_ptr()) % (2 << 20) == W.KV_OFFSET_BYTES
+    assert k.data_ptr() % (2 << 20) == 0
+    nbytes = k.numel() * k.element_size()
+    kb = (nbytes + (2 << 20) - 1) // (2 << 20) * (2 << 20)
+    assert v.data_ptr() - k.data_ptr() == kb + W.KV_GAP_BYTES + W.KV_OFFSET_BYTES
+    assert k.untyped_storage().data_ptr() == v.untyped_storage().data_ptr()   # one allocation
     plain = {n: torch.empty_like(k) for n in ("k", "v")}           # two plain allocations
     ref = W.make_inputs(wl, seed=3, device="cuda:0", out=plain)
     assert ref["k"].data_ptr() == plain["k"].data_ptr()

@@ -175,27 +175,40 @@ def _unit(n_rows: int, d: int, gen: torch.Generator, device) -> torch.Tensor:
     return u / u.norm(dim=-1, keepdim=True)
 
 
-# Byte offset of V's storage from K's, modulo 2 MB, in the device KV caches drawn here.  Both
-# passes read the K and V rows of the same positions together; where the two tensors sit at the
-# same offset modulo 2 MB (as two large allocations do by default), the same heads' slices of K
-# and V meet in the memory system and two of the eight Qwen3 KV heads read ~4% slower, which
-# sets the end of every verification call (interleaved on one MI355X, 128K step: 474.7 us per
-# layer-step with V and K congruent, 467.2-468.6 with V 256, 512 or 768 bytes away).
+# Where the device KV caches drawn here sit: each layer's K and V share one allocation, V starting
+# KV_GAP_BYTES + KV_OFFSET_BYTES past the end of K (rounded up to 2 MB).  Both passes read the K
+# and V rows of the same positions together, so how fast a call runs depends on where the two
+# tensors sit relative to each other (measured on one MI355X, 128K Qwen3-8B-shaped layer,
+# verification with collection):
+#   * modulo 2 MB: with V and K congruent, as two large allocations usually are, the same heads'
+#     slices of K and V meet in the memory system and two of the eight KV heads read ~4% slower,
+#     which sets the end of every call (128K step: 474.7 us per layer-step against 467.2-468.6
+#     with V 256, 512 or 768 bytes away);
+#   * beyond 2 MB: with V 1 GiB + 10 MiB + 512 B from K a call took 320-323 us, with V 1 GiB +
+#     2 MiB + 512 B or 2 GiB + 10 MiB + 512 B away 339-340 us, and two separate allocations read
+#     anywhere between the two from layer to layer (two K/V placements interleaved in one process:
+#     460.7 against 468.0 us per layer-step).  One allocation keeps the distance what is asked.
+# At this workload's size the rule below puts V 1 GiB + 10 MiB + 512 B from K; the 32K and the
+# gpt-oss-shaped layers read the same for every distance tried.
 KV_OFFSET_BYTES = 512
+KV_GAP_BYTES = 8 << 20
 _TWO_MB = 2 << 20
 
 
 def kv_cache_pair(total: int, hkv: int, d: int, dtype, device):
-    """Empty K and V caches [total, hkv, d]; on a GPU, V's storage starts KV_OFFSET_BYTES after K's
-    modulo 2 MB (see above).  Both are contiguous and 16-byte aligned."""
+    """Empty K and V caches [total, hkv, d]; on a GPU both live in one allocation, V starting
+    KV_GAP_BYTES + KV_OFFSET_BYTES past K's end rounded up to 2 MB, K at a 2 MB boundary (see
+    above).  Both are contiguous and 16-byte aligned."""
     dev = torch.device(device)
-    k = torch.empty(total, hkv, d, dtype=dtype, device=dev)
     if dev.type != "cuda":
-        return k, torch.empty(total, hkv, d, dtype=dtype, device=dev)
-    nbytes = k.numel() * k.element_size()
-    raw = torch.empty(nbytes + _TWO_MB, dtype=torch.uint8, device=dev)
-    off = (k.data_ptr() + KV_OFFSET_BYTES - raw.data_ptr()) % _TWO_MB
-    v = raw[off: off + nbytes].view(dtype).view(total, hkv, d)
+        return (torch.empty(total, hkv, d, dtype=dtype, device=dev),
+                torch.empty(total, hkv, d, dtype=dtype, device=dev))
+    nbytes = total * hkv * d * torch.empty(0, dtype=dtype).element_size()
+    vstart = (nbytes + _TWO_MB - 1) // _TWO_MB * _TWO_MB + KV_GAP_BYTES + KV_OFFSET_BYTES
+    raw = torch.empty(vstart + nbytes + _TWO_MB, dtype=torch.uint8, device=dev)
+    a0 = (-raw.data_ptr()) % _TWO_MB
+    k = raw[a0: a0 + nbytes].view(dtype).view(total, hkv, d)
+    v = raw[a0 + vstart: a0 + vstart + nbytes].view(dtype).view(total, hkv, d)
     return k, v
 
 
@@ -204,7 +217,7 @@ def make_inputs(wl: Workload, seed: int = 0, device="cpu", layer: int = 0, out: 
 
     Returns a dict of torch tensors on `device`:
       q        [batch*(gamma+1), Hq, D]   verification queries
-      k, v     [total_kv, Hkv, D]         (kv_cache_pair: V placed KV_OFFSET_BYTES from K mod 2 MB)
+      k, v     [total_kv, Hkv, D]         (kv_cache_pair: K and V in one allocation)
       cu_seqlens_k, cu_k  int32 [batch+1]
       draft_q  [n_drafts, batch, Hq, D]   fresh draft queries, one set per draft step
     If `out` holds preallocated k/v tensors of the right shape they are filled in place.
@@ -276,7 +289,7 @@ def page_cache(wl: Workload, inp: dict, page_size: int, seed: int = 0, spare_pag
     permuted page pool (with a few unused pages).  A data layout only: no values change.
 
     Returns {"k_pool", "v_pool": [num_pages, page_size, Hkv, D] (kv_cache_pair: on a GPU the V pool
-    starts KV_OFFSET_BYTES after the K pool modulo 2 MB), "block_table": int32 [batch, max_pages]
+    sits past the K pool in the same allocation), "block_table": int32 [batch, max_pages]
     (unused slots point at pool page 0), "num_pages"}.
     """
     k, v = inp["k"], inp["v"]
