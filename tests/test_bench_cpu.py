@@ -1,6 +1,6 @@
 """bench.py's contract on the CPU: the algorithmic bytes it divides by (written out here from the
-shapes), its refusal of more than one GPU, and the filter that keys the counter summaries to the
-product kernels' code."""
+shapes), its refusal of more than one GPU and of malformed cache placement flags, and the filter
+that keys the counter summaries to the product kernels' code."""
 import os
 import subprocess
 import sys
@@ -40,6 +40,17 @@ def test_bench_refuses_more_than_one_gpu():
     assert run.returncode == 2
     assert "one GPU only" in run.stderr and "--gpus 2" in run.stderr
     assert run.stdout == ""
+
+
+def test_bench_rejects_bad_kv_placement_arguments():
+    """--kv-offset takes a non-negative multiple of 16 bytes and --kv-gap a non-negative multiple of
+    2 MB; anything else exits with status 2 and says which, before touching a device."""
+    for flag, value, msg in (("--kv-offset", "8", "--kv-offset must be"), ("--kv-offset", "-16", "--kv-offset must be"),
+                             ("--kv-gap", "1000", "--kv-gap must be"), ("--kv-gap", str(3 << 20), "--kv-gap must be")):
+        run = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), flag, value], capture_output=True,
+                             text=True, timeout=300, cwd=ROOT)
+        assert run.returncode == 2, (flag, value, run.stderr)
+        assert msg in run.stderr and run.stdout == ""
 
 
 def test_counter_key_ignores_comments_and_the_trace_build():
