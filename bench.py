@@ -9,7 +9,7 @@ every layer.  The reported value is microseconds per layer-step
 (verify + select + gamma drafts of one layer) = step time / layers.
 
 With several layers, verification + selection runs as the one call in two
-halves: the selections (keys, candidates, write) of a group of four layers go
+halves: the selections (keys, candidates, write) of a group of nine layers go
 to a second stream after the group's last verification, beside the next
 layers' verifications (the selected positions are used only by the drafting
 passes, which wait for each group's selections).
@@ -639,9 +639,10 @@ def main():
     overlap = fused and host_plan and layers > 1 and not args.single_stream
     # The second halves go to the side stream in groups of SEL_GROUP layers, each group after its
     # last layer's first half: every cross-stream event costs the launch stream ~1 us, and the
-    # selections are needed only by the drafting passes (interleaved in one process, 128K step:
-    # 477.5 us per layer-step with a group per layer, 473.6 with groups of four).
-    SEL_GROUP = 4
+    # selections are needed only by the drafting passes (interleaved in one process, 128K step, µs
+    # per layer-step: 464.7 with a group per layer, 459.9 with groups of 4, 458.7 of 6, 458.2 of 9,
+    # 458.7 of 12; 449.6 with no selection work at all).
+    SEL_GROUP = 9
     side = torch.cuda.Stream() if overlap else None              # default priority, as the launch stream
     begin_calls = [st.bind_fused(stream, part="begin") for st in steps] if overlap else None
     end_calls = [st.bind_fused(side, part="end") for st in steps] if overlap else None
