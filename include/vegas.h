@@ -368,8 +368,10 @@ typedef struct {
 } vegas_paged_kv_t;
 
 /* Workspace of vegas_verify_attn_paged for a cache of `page_size` (0: the
- * contiguous cache, same as vegas_verify_workspace_size).  Small pages cap the
- * positions one split covers, so they can need more workspace. */
+ * contiguous cache, same as vegas_verify_workspace_size).  A split stages its
+ * page list in LDS beside its collected scores, so small pages cap the
+ * positions one split covers (1-token pages: 11200 at D = 128, bf16) and can
+ * need more splits, hence more workspace. */
 vegas_status_t vegas_verify_paged_workspace_size(const vegas_attn_shape_t* shape, int32_t gamma,
                                                  int32_t max_seqlen_k, int32_t page_size, size_t* bytes);
 vegas_status_t vegas_verify_attn_paged(const vegas_attn_shape_t* shape, int32_t gamma,

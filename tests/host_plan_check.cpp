@@ -84,6 +84,7 @@ namespace {
 
 long long g_cases = 0;
 long long g_balanced = 0;   // balanced host plans checked
+long long g_multiround = 0; // verification plans over more than one round of workgroups
 
 [[noreturn]] void violation(const char* what, const std::string& detail) {
     std::printf("VIOLATION after %lld cases: %s\n%s\n", g_cases, what, detail.c_str());
@@ -214,6 +215,16 @@ void check_attn(const Case& c, bool gather, size_t ws_bytes, const char* entry, 
     REQUIRE((size_t)(wsp - wml) >= slots * rows * 2 * 4, "part_ml region short");
     REQUIRE((size_t)(wsp - w0) + (size_t)B * 4 <= ws_bytes, "split counts past the workspace");
 
+    // the split target: one round of 256 workgroups per KV head (pairs of heads for a paired
+    // drafting pass), or, for verification of at most kHostPlanMax sequences, whole rounds up to four
+    {
+        const int groups = (gather && a.pair) ? c.hkv / 2 : c.hkv;
+        const int base = std::max(1, 256 / groups);
+        REQUIRE(a.target % base == 0 && a.target >= base && a.target <= 4 * base, "target %d (round %d)", a.target,
+                base);
+        REQUIRE(a.target == base || (!gather && B <= vegas::kHostPlanMax), "target %d over one round", a.target);
+        if (a.target > base) ++g_multiround;
+    }
     std::vector<int> len, lo;
     spans(c, gather, len, lo);
     // the device plan: the grid (max_units per KV head) and the slots (nsplit)
@@ -229,8 +240,8 @@ void check_attn(const Case& c, bool gather, size_t ws_bytes, const char* entry, 
         if (page > 0 && !gather)
             for (int s = 0; s < dp.ns_raw[b]; ++s) {
                 const int st = lo[b] + s * dp.chunk[b], en = std::min(st + dp.chunk[b], lo[b] + len[b]);
-                REQUIRE(pages_spanned(st, en, page) <= vegas::kMaxPagesPerSplit, "device plan: %d pages",
-                        pages_spanned(st, en, page));
+                REQUIRE(pages_spanned(st, en, page) <= a.page_cap, "device plan: %d pages > page list %d",
+                        pages_spanned(st, en, page), a.page_cap);
             }
     }
     REQUIRE(dp.units <= a.max_units, "device plan: %lld units > max_units %d", dp.units, a.max_units);
@@ -246,7 +257,7 @@ void check_attn(const Case& c, bool gather, size_t ws_bytes, const char* entry, 
         const int main_lds = std::max(ring, (vegas::kAttnWaves / 2) * mslot);
         const long long stat = main_lds + (gather ? vegas::kMaxGatherChunk * 4 : 4) + 64;
         const long long dyn = (!gather && g_cap.collect ? vegas::attn_score_lds_bytes(a.score_cap) : 0) +
-                              (!gather && page > 0 ? vegas::kMaxPagesPerSplit * 4 : 0);
+                              (!gather && page > 0 ? (long long)a.page_cap * 4 : 0);
         REQUIRE(stat + dyn <= 160 * 1024, "LDS %lld static + %lld dynamic", stat, dyn);
     }
 
@@ -526,6 +537,7 @@ int main(int argc, char** argv) {
     const unsigned long long seed = argc > 2 ? std::strtoull(argv[2], nullptr, 10) : 1;
     rng.seed(seed);
     for (g_cases = 0; g_cases < n; ++g_cases) run_case(make_case());
-    std::printf("ok %lld cases, %lld balanced plans (seed %llu)\n", g_cases, g_balanced, seed);
+    std::printf("ok %lld cases, %lld balanced plans, %lld multi-round plans (seed %llu)\n", g_cases, g_balanced,
+                g_multiround, seed);
     return 0;
 }

@@ -419,6 +419,8 @@ PAGED_CASES = [
     ("bf16", 2, 32, 8, 64, 5, [3000, 40], 256),
     ("f32", 2, 8, 2, 64, 2, [300, 77], 4),
     ("bf16", 1, 64, 8, 128, 6, [2000], 32),
+    # 1-token pages with splits of ~3K positions, longer than a 2048-word page list alone would allow
+    ("bf16", 1, 32, 8, 128, 3, [100000], 1),
 ]
 
 

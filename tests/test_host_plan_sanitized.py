@@ -32,11 +32,14 @@ def test_host_plan_bounds_under_asan_and_ubsan(tmp_path):
         pytest.skip("this g++ has no sanitizer runtime")
     assert build.returncode == 0, build.stderr
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1")
-    seen_balanced = 0
+    seen_balanced = seen_multiround = 0
     for seed, n in ((1, 60000), (2, 60000)):
         run = subprocess.run([str(exe), str(n), str(seed)], capture_output=True, text=True, env=env, timeout=600)
         assert run.returncode == 0, run.stdout + run.stderr
         assert run.stdout.startswith(f"ok {n} cases"), run.stdout
         seen_balanced += int(run.stdout.split(",")[1].split()[0])
-    # the ragged batches exercise the balanced plan's tables too
+        seen_multiround += int(run.stdout.split(",")[2].split()[0])
+    # the ragged batches exercise the balanced plan's tables too, and long sequences (or small
+    # pages) the plans over several rounds of workgroups
     assert seen_balanced >= 1000, seen_balanced
+    assert seen_multiround >= 1000, seen_multiround

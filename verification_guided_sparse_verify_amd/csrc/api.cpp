@@ -44,6 +44,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // kernel holds one workgroup per CU).  Each further round costs a workgroup's
 // start-up and drain on the critical path, about 10 us at 128K positions.
 constexpr int kRoundWorkgroups = 256;
+// Most rounds of verification workgroups a plan aims for (see plan_attn).
+constexpr int kMaxRounds = 4;
 
 struct AttnPlan {
     bool pair = false;   // gather: workgroups take two KV heads (the split kernel's PAIR layout)
@@ -62,7 +64,7 @@ struct AttnPlan {
 // each sequence's splits from the device-side lengths (seq_plan in attn.hip);
 // this sizes the grid and the partial slots for any lengths up to max_n.
 AttnPlan plan_attn(bool bf16, int batch, int hkv, int M, int head_dim, int max_n, bool gather,
-                   int page_size = 0) {
+                   int page_size = 0, int64_t total = -1) {
     AttnPlan p;
     p.mb = (M + 15) / 16;
     const int unit = vegas::kAttnWaves * vegas::kAttnBlock;
@@ -71,9 +73,9 @@ AttnPlan plan_attn(bool bf16, int batch, int hkv, int M, int head_dim, int max_n
     // and without collection, so the two give bit-identical outputs.
     int cap = gather ? vegas::kMaxGatherChunk : vegas::collect_chunk_cap(bf16, head_dim);
     if (!gather && page_size > 0) {
-        // a paged split stages its page list in LDS: at most kMaxPagesPerSplit pages
-        const int64_t page_cap = (int64_t)(vegas::kMaxPagesPerSplit - 2) * page_size / unit * unit;
-        if (page_cap < cap) cap = (int)page_cap;
+        // a paged split stages its page list in LDS beside the score buffer
+        const int page_cap = vegas::paged_split_cap(bf16, head_dim, page_size);
+        if (page_cap < cap) cap = page_cap;
     }
     p.cap = cap;
     // A drafting pass with one query tile and an even KV head count runs its
@@ -86,7 +88,23 @@ AttnPlan plan_attn(bool bf16, int batch, int hkv, int M, int head_dim, int max_n
     // Bounds of the device plan (seq_plan / batch_plan in attn.hip): a sequence
     // gets at most max(target + 1, ceil(len / cap)) splits (the float share can
     // round one up), the batch at most max(target, ceil(total / cap)) + 2 * batch.
-    p.target = std::max(1, kRoundWorkgroups / groups);
+    // Splits per KV head: one round of workgroups, or whole rounds when the
+    // cap forces more splits than one round holds (long sequences over small
+    // pages): a round and a half of equal splits takes as long as two rounds
+    // of half-length ones.  Only for batches the host can plan (the partial
+    // slots grow with the target per sequence), up to four rounds.  `total`
+    // (rows of the call's cache) counts at most batch * max_n positions, the
+    // bound a workspace query takes, so a call never needs more workspace
+    // than the query gave.
+    const int base = std::max(1, kRoundWorkgroups / groups);
+    int rounds = 1;
+    if (!gather && batch <= vegas::kHostPlanMax) {
+        const int64_t bound = (int64_t)batch * n;
+        const int64_t tot = total >= 0 ? std::min<int64_t>(total, bound) : bound;
+        const int64_t need = (tot + cap - 1) / cap;
+        rounds = (int)std::min<int64_t>(kMaxRounds, std::max<int64_t>(1, (need + base - 1) / base));
+    }
+    p.target = base * rounds;
     p.nsplit = (int)std::max<int64_t>(p.target + 1, (n + cap - 1) / cap);
     p.max_units = (int)std::max<int64_t>(p.target, (batch * n + cap - 1) / cap) + 2 * batch;
     // a single 16-row tile keeps only its M valid rows in a partial (part_rows in attn.hip)
@@ -418,7 +436,7 @@ vegas_status_t verify_impl(const vegas_attn_shape_t* shape, int32_t gamma, const
         return fail(VEGAS_ERR_INVALID_ARGUMENT, "collection is not defined under a local mask");
     const AttnPlan plan = plan_attn(shape->dtype == VEGAS_DTYPE_BF16, shape->batch, shape->num_kv_heads, W * G,
                                     shape->head_dim, verify_span(max_seqlen_k, gamma, window), false,
-                                    pages ? pages->page_size : 0);
+                                    pages ? pages->page_size : 0, total_kv);
     if (workspace_bytes < plan.total())
         return fail(VEGAS_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.total(),
                     workspace_bytes);
@@ -473,6 +491,7 @@ vegas_status_t verify_impl(const vegas_attn_shape_t* shape, int32_t gamma, const
     }
     a.score_cap = plan.cap;
     if (a.hp.n > 0) a.score_cap = longest_unit(a.hp);
+    a.page_cap = pages ? vegas::paged_list_words(plan.cap, 1 << shift) : 0;
     if (!launch) return VEGAS_OK;                  // arguments checked only
     // (fused without the keys step: the split kernel still clears the selection's histograms)
     return hip_status(vegas::launch_attn(a, shape->dtype == VEGAS_DTYPE_BF16, shape->head_dim, plan.mb,
@@ -821,7 +840,7 @@ vegas_status_t vegas_verify_hostplan_info(const vegas_attn_shape_t* shape, int32
     }
     const int G = shape->num_q_heads / shape->num_kv_heads;
     const AttnPlan plan = plan_attn(shape->dtype == VEGAS_DTYPE_BF16, shape->batch, shape->num_kv_heads, W * G,
-                                    shape->head_dim, max_seqlen_k, false);
+                                    shape->head_dim, max_seqlen_k, false, 0, total_kv);
     *balanced = 0;
     *workgroups = plan.max_units;
     if (shape->batch <= vegas::kHostPlanMax) {

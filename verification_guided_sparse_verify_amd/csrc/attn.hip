@@ -651,7 +651,7 @@ __device__ __forceinline__ void split_unit(const AttnArgs& a, int g0, int b, int
     } else {
         if (paged) {                      // the pool pages of positions start .. end-1
             page0 = start >> a.page_shift;
-            const int npg = min(((end - 1) >> a.page_shift) - page0 + 1, kMaxPagesPerSplit);
+            const int npg = min(((end - 1) >> a.page_shift) - page0 + 1, a.page_cap);
             for (int i = threadIdx.x; i < npg; i += blockDim.x) {
                 const int pg = a.block_table[(size_t)b * a.max_pages + min(page0 + i, a.max_pages - 1)];
                 page_s[i] = min(max(pg, 0), a.num_pages - 1);
@@ -1057,7 +1057,7 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream, const SelectArgs* sel
     const unsigned split_grid = (unsigned)((PAIR ? a.hkv / 2 : a.hkv) * per_head);
     const unsigned comb_grid = (unsigned)(a.batch * a.hkv * MB * (D / 16));
     const size_t dyn = (COLLECT ? attn_score_lds_bytes(a.score_cap) : 0) +
-                       (!GATHER && a.page_shift >= 0 ? kMaxPagesPerSplit * sizeof(int) : 0);
+                       (!GATHER && a.page_shift >= 0 ? (size_t)a.page_cap * sizeof(int) : 0);
     if (split_grid > 0)
         hipLaunchKernelGGL((attn_split_kernel<BF16, D, MB, GATHER, COLLECT, PAIR>), dim3(split_grid),
                            dim3(kAttnWaves * 64), dyn, stream, a);

@@ -28,7 +28,9 @@ __host__ __device__ constexpr int attn_stages(bool bf16, int head_dim, bool gath
 // Longest position range one workgroup takes in gather mode: its index list
 // is staged in LDS.
 constexpr int kMaxGatherChunk = 2048;
-// Paged KV cache: pool pages of one verification split, staged in LDS.
+// Paged KV cache: LDS words set aside for a verification split's page list on
+// top of its collected-score buffer.  Splits over small pages trade score
+// buffer for page list (paged_split_cap below).
 constexpr int kMaxPagesPerSplit = 2048;
 constexpr int kMaxPageSize = 256;
 // Largest batch the attention passes take (their split plan keeps a few
@@ -50,6 +52,25 @@ __host__ __device__ constexpr int collect_chunk_cap(bool bf16, int head_dim) {
 // `positions` positions (the buffer is sized at launch).
 __host__ __device__ constexpr int attn_score_lds_bytes(int positions) {
     return (positions * 4 + 15) / 16 * 16;
+}
+// Pool pages a paged verification split of at most `positions` positions
+// stages in LDS: a range of n positions starting anywhere touches at most
+// (n - 1) / page + 2 pages.
+__host__ __device__ constexpr int paged_list_words(int positions, int page_size) {
+    return (positions - 1) / page_size + 2;
+}
+// Longest paged verification split: the collected-score buffer and the page
+// list share the LDS that a contiguous split's score buffer and
+// kMaxPagesPerSplit words would take, so splits over small pages stay long
+// (1-token pages at D = 128, bf16: 11200 positions instead of ~2K); a
+// multiple of kAttnWaves*kAttnBlock, at most collect_chunk_cap.
+__host__ __device__ constexpr int paged_split_cap(bool bf16, int head_dim, int page_size) {
+    const int cap = collect_chunk_cap(bf16, head_dim);
+    const int budget = attn_score_lds_bytes(cap) + kMaxPagesPerSplit * 4;
+    int n = cap;
+    while (n > kAttnWaves * kAttnBlock && attn_score_lds_bytes(n) + paged_list_words(n, page_size) * 4 > budget)
+        n -= kAttnWaves * kAttnBlock;
+    return n;
 }
 
 // Split plan computed on the host from host copies of the sequence offsets,
@@ -112,6 +133,7 @@ struct AttnArgs {
     int32_t max_pages;
     int32_t num_pages;
     int32_t page_shift;            // log2(page size); -1: contiguous varlen cache
+    int32_t page_cap;              // LDS words of a verification split's page list (paged only)
     int32_t window;                // verification local mask: row r sees keys (L+r-window, L+r]; 0: none
     int32_t pair;                  // gather: each workgroup takes KV heads g and g+1 (two waves each)
     // Fused selection (verification with collection only): the split kernel
