@@ -298,7 +298,8 @@ def launch_floor(chain: int = 200, reps: int = 5):
     """Cost of one kernel boundary in a chain of dependent launches on one stream
     (libvegas_probe.so's empty chained kernel), for one workgroup and for one round of 256
     workgroups holding 64 KB of LDS each (one per CU, as the attention kernels run): the floor
-    under each small dependent kernel of a pass."""
+    under each small dependent kernel of a pass.  The chain is queued behind a 5 ms wait on the
+    GPU, so it is timed at the GPU's rate rather than the host's launch rate."""
     import ctypes
     import torch
     from verification_guided_sparse_verify_amd import build as B
@@ -308,6 +309,9 @@ def launch_floor(chain: int = 200, reps: int = 5):
     fn = probe.vegas_probe_launch_chain
     fn.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     fn.restype = ctypes.c_int
+    delay = probe.vegas_probe_delay
+    delay.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    delay.restype = ctypes.c_int
     sink = torch.zeros(64, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
     out = {}
@@ -316,6 +320,10 @@ def launch_floor(chain: int = 200, reps: int = 5):
         for r in range(reps + 1):
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
+            # hold the GPU for 5 ms while the host queues the chain: the chain is then timed on
+            # the GPU alone, not at the host's launch rate
+            if delay(500000, sink.data_ptr(), stream.cuda_stream) != 0:
+                raise RuntimeError("vegas_probe_delay failed")
             a.record(stream)
             rc = fn(chain, wgs, lds, sink.data_ptr(), stream.cuda_stream)
             b.record(stream)
@@ -325,7 +333,8 @@ def launch_floor(chain: int = 200, reps: int = 5):
         torch.cuda.synchronize()
         out[name] = round(statistics.median(x.elapsed_time(y) for x, y in times[1:]) * 1e3 / chain, 2)
     out["unit"] = "us per dependent launch"
-    out["kernel"] = f"vegas_probe_launch_chain ({chain} chained launches of an empty kernel, median of {reps})"
+    out["kernel"] = (f"vegas_probe_launch_chain ({chain} chained launches of an empty kernel queued behind "
+                     f"vegas_probe_delay, median of {reps})")
     return out
 
 

@@ -64,6 +64,16 @@ int vegas_probe_gather_read(const void* k, const void* v, const int32_t* rows, i
  */
 int vegas_probe_launch_chain(int32_t launches, int32_t workgroups, int32_t lds_bytes, uint32_t* sink, void* stream);
 
+/*
+ * One wave on `stream` that spins for `ticks` (0..1e8, i.e. up to 1 s) of the
+ * 100 MHz constant clock and then adds 0 or 1 to sink[0] (device uint32 [1]).
+ * Launched before a timed chain, it holds the GPU while the host queues the
+ * chain, so the chain's time is the GPU's own and not the host's launch rate.
+ * Asynchronous.  Returns 0, -1 for invalid arguments (nothing launched), or the
+ * HIP error code of the launch.
+ */
+int vegas_probe_delay(int64_t ticks, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

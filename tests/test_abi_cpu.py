@@ -280,7 +280,8 @@ def test_probe_library_exports_and_rejects_bad_arguments(V):
     from verification_guided_sparse_verify_amd import build as B
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "vegas_probe.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(vegas_[a-z_0-9]+)\s*\(", text)))
-    assert names == ["vegas_probe_gather_read", "vegas_probe_launch_chain", "vegas_probe_stream_read"]
+    assert names == ["vegas_probe_delay", "vegas_probe_gather_read", "vegas_probe_launch_chain",
+                     "vegas_probe_stream_read"]
     nm = subprocess.run(["nm", "-D", "--defined-only", B.PROBE_LIB], capture_output=True, text=True).stdout
     assert all(n in nm for n in names)
     fn = ctypes.CDLL(B.PROBE_LIB).vegas_probe_stream_read
@@ -351,6 +352,11 @@ def test_launch_chain_probe_rejects_bad_arguments(V):
     assert fn(10, 4097, 0, FAKE, None) == -1
     assert fn(10, 256, -1, FAKE, None) == -1        # LDS outside 0..65536
     assert fn(10, 256, 65537, FAKE, None) == -1
+    delay = ctypes.CDLL(B.PROBE_LIB).vegas_probe_delay
+    delay.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    assert delay(1000, None, None) == -1              # no sink
+    assert delay(-1, FAKE, None) == -1                # negative
+    assert delay(100000001, FAKE, None) == -1         # over a second
 
 
 def test_trace_build_is_separate_from_the_product_library(V):

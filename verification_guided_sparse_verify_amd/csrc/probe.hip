@@ -118,7 +118,24 @@ __global__ void __launch_bounds__(kThreads) launch_chain_kernel(uint32_t* __rest
     (void)chain_lds;
 }
 
+// Spins one wave for `ticks` of the 100 MHz constant clock (bounded: the clock
+// only moves forward), so that launches queued behind it are timed on the GPU
+// alone.
+__global__ void __launch_bounds__(64) delay_kernel(unsigned long long ticks, uint32_t* __restrict__ sink) {
+    const unsigned long long t0 = wall_clock64();
+    unsigned long long t = t0;
+    while (t - t0 < ticks) t = wall_clock64();
+    if (threadIdx.x == 0) sink[0] = sink[0] + (uint32_t)(t - t0 > ticks);
+}
+
 }  // namespace
+
+extern "C" int vegas_probe_delay(int64_t ticks, uint32_t* sink, void* stream) {
+    if (!sink || ticks < 0 || ticks > 100000000) return -1;
+    hipLaunchKernelGGL(delay_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                       (unsigned long long)ticks, sink);
+    return (int)hipGetLastError();
+}
 
 extern "C" int vegas_probe_launch_chain(int32_t launches, int32_t workgroups, int32_t lds_bytes, uint32_t* sink,
                                         void* stream) {
