@@ -458,6 +458,33 @@ def test_paged_cache_matches_contiguous(case):
     check_layer(wl, inp, st)   # and the contiguous path against the oracle
 
 
+MULTI_ROUND_CASES = [
+    # dtype, batch, Hq, Hkv, D, gamma, prefix lengths, page size (0: contiguous)
+    # 16 KV heads: one round is 16 splits per head; 400K positions need 17 of at most 24576
+    ("bf16", 1, 16, 16, 64, 1, [400000], 0),
+    # 1-token pages: the page list shares the split's LDS (13248 positions), 250K need 19 splits
+    ("bf16", 1, 32, 16, 64, 3, [250000], 1),
+]
+
+
+@pytest.mark.parametrize("case", MULTI_ROUND_CASES, ids=lambda c: f"{c[0]}-{c[2]}x{c[3]}-D{c[4]}-g{c[5]}-L{c[6]}-P{c[7]}")
+def test_multi_round_plans_match_oracle(case):
+    """When the LDS cap forces more splits than one round of workgroups holds, the plan takes
+    whole rounds (here two, twice the one-round split count); verification, scores, selection and
+    drafts still match the oracle."""
+    dtype, B, hq, hkv, d, gamma, prefixes, P = case
+    wl = W.custom_workload(dtype, B, hq, hkv, d, gamma, prefixes, draft_steps=2)
+    log(f"case: multi-round {wl.name} L={prefixes} page={P}")
+    inp = W.make_inputs(wl, seed=12, device="cuda")
+    paged = W.page_cache(wl, inp, P, seed=12) if P else None
+    st = LayerStep(inp, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.gamma, wl.seqlens,
+                   wl.k_per_seq, wl.scale, n_drafts=wl.n_drafts, paged=paged)
+    st.run()
+    torch.cuda.synchronize()
+    worst = check_layer(wl, inp, st)
+    log(f"  worst {worst}")
+
+
 LOCAL_CASES = [
     # dtype, batch, Hq, Hkv, D, gamma, prefix lengths, window
     ("bf16", 3, 16, 4, 128, 3, [1000, 4097, 129], 128),
