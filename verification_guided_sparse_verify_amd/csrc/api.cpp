@@ -85,9 +85,6 @@ AttnPlan plan_attn(bool bf16, int batch, int hkv, int M, int head_dim, int max_n
     // one round of workgroups.
     p.pair = gather && p.mb == 1 && hkv % 2 == 0;
     const int groups = p.pair ? hkv / 2 : hkv;
-    // Bounds of the device plan (seq_plan / batch_plan in attn.hip): a sequence
-    // gets at most max(target + 1, ceil(len / cap)) splits (the float share can
-    // round one up), the batch at most max(target, ceil(total / cap)) + 2 * batch.
     // Splits per KV head: one round of workgroups, or whole rounds when the
     // cap forces more splits than one round holds (long sequences over small
     // pages): a round and a half of equal splits takes as long as two rounds
@@ -105,6 +102,9 @@ AttnPlan plan_attn(bool bf16, int batch, int hkv, int M, int head_dim, int max_n
         rounds = (int)std::min<int64_t>(kMaxRounds, std::max<int64_t>(1, (need + base - 1) / base));
     }
     p.target = base * rounds;
+    // Bounds of the device plan (seq_plan / batch_plan in attn.hip): a sequence
+    // gets at most max(target + 1, ceil(len / cap)) splits (the float share can
+    // round one up), the batch at most max(target, ceil(total / cap)) + 2 * batch.
     p.nsplit = (int)std::max<int64_t>(p.target + 1, (n + cap - 1) / cap);
     p.max_units = (int)std::max<int64_t>(p.target, (batch * n + cap - 1) / cap) + 2 * batch;
     // a single 16-row tile keeps only its M valid rows in a partial (part_rows in attn.hip)
